@@ -1,0 +1,433 @@
+"""Pins of the CPU oracle to what the Positional-LSH pages and the mathematics
+fix ("Positional LSH: Binary Block Matrix Approximation for Attention with
+Linear Biases", technical summaries).  No GPU.  Statistical checks use fixed
+seeds and 5-standard-error bands."""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.integrate
+import scipy.special
+import scipy.stats
+import torch
+
+import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_qkv(rng, B, H, Hkv, n, d, scale=1.0):
+    q = rng.standard_normal((B, H, n, d)) * scale
+    k = rng.standard_normal((B, Hkv, n, d)) * scale
+    v = rng.standard_normal((B, Hkv, n, d))
+    return q, k, v
+
+
+def _tables(seed, sigma, s, n):
+    params = orc.sample_params(seed, sigma, s)
+    offsets, starts = orc.tables_from_params(n, params)
+    return params, orc.starts_per_head(offsets, starts, len(sigma), s)
+
+
+# ---------------------------------------------------------------- golden ---
+def test_golden_worked_example():
+    """Hand-worked example (Methodology §1 bins/masks, §3 ratio of sums)."""
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    n = g["n"]
+    tables = []
+    for hs in g["hashes"]:
+        assert orc.bins(n, hs["delta"], hs["u"]).astype(int).tolist() == hs["bins"]
+        st = orc.block_starts(n, hs["delta"], hs["u"])
+        assert st.tolist() == hs["starts"]
+        tables.append(st)
+    q = np.zeros((1, 1, n, 2))
+    k = np.zeros((1, 1, n, 2))
+    v = np.zeros((1, 1, n, 2))
+    v[0, 0, :, 0] = np.arange(n)
+    v[0, 0, :, 1] = np.arange(n) ** 2
+    for mode in ("noncausal", "causal"):
+        causal = mode == "causal"
+        want = np.array([[float(Fraction(x)) for x in row] for row in g[mode]["T"]])
+        got = orc.lsh_estimate(q, k, v, [tables], causal)[0, 0]
+        np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
+        got2 = orc.lsh_estimate_multiplicity(q, k, v, [tables], causal)[0, 0]
+        np.testing.assert_allclose(got2, want, rtol=1e-14, atol=1e-14)
+        c = orc.multiplicity_dense(n, tables, causal)
+        assert c.sum(axis=1).tolist() == g[mode]["multiplicity_rowsums"]
+        alg, distinct = orc.work_counts(n, [tables], causal)
+        assert (alg, distinct) == (g[mode]["pairs_alg"], g[mode]["pairs_distinct"])
+
+
+# ------------------------------------------------------------------- P1 ---
+@pytest.mark.parametrize("sigma", [1.0, 16.0, 64.0])
+def test_p1_pitch_law_reproduces_laplacian_kernel(sigma):
+    """Methodology §1: L* = E_h[M(h)].  For a pitch density p(delta), two
+    points Delta apart share a bin with probability E[max(0, 1-Delta/delta)].
+    With p = Gamma(2, sigma) this integral is exactly exp(-Delta/sigma)."""
+    for Delta in (0.0, 1.0, 5.0, 40.0, 200.0):
+        f = lambda dl: (1.0 - Delta / dl) * dl / sigma ** 2 * math.exp(-dl / sigma)
+        val, err = scipy.integrate.quad(f, Delta, np.inf, epsabs=1e-14, epsrel=1e-13,
+                                        limit=400) if Delta > 0 else (1.0, 0.0)
+        assert abs(val - math.exp(-Delta / sigma)) <= 1e-10
+
+
+def test_p1_sampled_laws_ks():
+    """The oracle's draws follow delta ~ Gamma(2, sigma), u/delta ~ U[0,1)."""
+    sigma = [3.0, 50.0]
+    s = 3000
+    p = orc.sample_params(7, sigma, s)
+    for h, sg in enumerate(sigma):
+        dl = p[h * s:(h + 1) * s, 0]
+        uu = p[h * s:(h + 1) * s, 1]
+        assert np.all(dl > 0) and np.all(uu >= 0) and np.all(uu < dl)
+        assert scipy.stats.kstest(dl, scipy.stats.gamma(a=2, scale=sg).cdf).pvalue > 1e-4
+        assert scipy.stats.kstest(uu / dl, "uniform").pvalue > 1e-4
+    # a wrong law (exponential pitch) is rejected by the same test
+    assert scipy.stats.kstest(p[:s, 0], scipy.stats.expon(scale=6.0).cdf).pvalue < 1e-6
+
+
+# ------------------------------------------------------------------- P2 ---
+def test_p2_unbiased_mean_and_variance_identity():
+    """Methodology §1-§2: each M(h)_ij is Bernoulli(L*_ij) and the s hashes are
+    i.i.d., so E||M~ - L*||_F^2 = (1/s) sum_ij L*_ij (1 - L*_ij) exactly and
+    the pooled mean of the masks tends to L*."""
+    n, sigma, s, R = 24, 4.0, 8, 300
+    Ls = orc.alibi_matrix(n, sigma)
+    fro2 = np.empty(R)
+    pooled = np.zeros((n, n))
+    for r in range(R):
+        _, tabs = _tables(1000 + r, [sigma], s, n)
+        Mt = orc.mask_mean(n, tabs[0])
+        fro2[r] = ((Mt - Ls) ** 2).sum()
+        pooled += Mt
+    pooled /= R
+    expect = (Ls * (1 - Ls)).sum() / s
+    se = fro2.std(ddof=1) / math.sqrt(R)
+    assert abs(fro2.mean() - expect) <= 5 * se
+    # pointwise unbiasedness
+    sd = np.sqrt(Ls * (1 - Ls) / (R * s))
+    z = np.abs(pooled - Ls) / np.where(sd > 0, sd, 1.0)
+    assert np.all(np.where(sd > 0, z, 0.0) <= 5.5)
+    assert np.all(np.diag(pooled) == 1.0)
+
+
+# ------------------------------------------------------------------- P3 ---
+@pytest.mark.parametrize("sigma", [4.0, 16.0])
+def test_p3_max_norm_error_decays_like_inverse_sqrt_s(sigma):
+    """Key results: spectral- and max-norm errors decay as O(1/sqrt(s))."""
+    n, R = 48, 5
+    ss = [2 ** e for e in range(2, 13)]
+    Ls = orc.alibi_matrix(n, sigma)
+    err = np.zeros((R, len(ss)))
+    spec = np.zeros((R, len(ss)))
+    for r in range(R):
+        params = orc.sample_params(500 + r, [sigma], ss[-1])
+        acc = np.zeros((n, n))
+        done = 0
+        for si, s in enumerate(ss):
+            for kk in range(done, s):
+                acc += orc.mask_dense(n, orc.block_starts(n, params[kk, 0], params[kk, 1]))
+            done = s
+            e = orc.matrix_errors(Ls, acc / s)
+            err[r, si], spec[r, si] = e["max"], e["spectral"]
+    slope = np.polyfit(np.log(ss), np.log(err.mean(axis=0)), 1)[0]
+    assert -0.6 <= slope <= -0.4, slope
+    sslope = np.polyfit(np.log(ss), np.log(spec.mean(axis=0)), 1)[0]
+    assert -0.65 <= sslope <= -0.35, sslope
+
+
+# ------------------------------------------------------------------- P4 ---
+@pytest.mark.parametrize("delta", [0.7, 3.3, 17.9, 130.2])
+def test_p4_collision_probability_per_pitch(delta):
+    """Random binning with fixed pitch: over u ~ U[0, delta), positions Delta
+    apart share a bin with probability max(0, 1 - Delta/delta)."""
+    M = 100000
+    us = (np.arange(M) + 0.5) / M * delta
+    for i, j in [(0, 0), (3, 4), (10, 13), (0, 17), (5, 100), (200, 330)]:
+        bi = np.floor((i + us) / delta)
+        bj = np.floor((j + us) / delta)
+        frac = np.mean(bi == bj)
+        assert abs(frac - max(0.0, 1 - abs(i - j) / delta)) <= 2.0 / M
+        # and the oracle's own bin routine agrees with this evaluation
+    for t in range(0, M, 9973):
+        b = orc.bins(40, delta, us[t])
+        assert np.array_equal(b, np.floor((np.arange(40) + us[t]) / delta))
+
+
+# ------------------------------------------------------------------- P5 ---
+def test_p5_block_structure():
+    """Methodology §1: bins on integer positions give contiguous,
+    non-overlapping blocks.  Derived: interior block lengths are floor(delta)
+    or ceil(delta)."""
+    n = 3000
+    params = orc.sample_params(11, [2.5, 9.0, 40.0, 300.0], 5000 // 4)
+    for r in range(params.shape[0]):
+        dl, u = params[r]
+        st = orc.block_starts(n, dl, u)
+        assert st[0] == 0 and st[-1] == n
+        assert np.all(np.diff(st) > 0)
+        L = np.diff(st)
+        if len(L) > 2:
+            inner = L[1:-1]
+            ok = (inner == math.floor(dl)) | (inner == math.ceil(dl))
+            assert ok.all(), (dl, u, np.unique(inner))
+        assert L[0] <= math.ceil(dl) and L[-1] <= math.ceil(dl)
+    # interval closure: M_il = 1 implies M_ij = M_jl = 1 for i < j < l
+    st = orc.block_starts(40, 4.7, 1.3)
+    M = orc.mask_dense(40, st)
+    for i in range(40):
+        for l in range(i + 1, 40):
+            if M[i, l]:
+                assert M[i, i:l + 1].all() and M[i:l + 1, l].all()
+
+
+# ------------------------------------------------------------------- P6 ---
+def test_p6_largest_block_tracks_sigma_loglog_n():
+    """Methodology §2: b_max ~ sigma log log n with s ~ log n hashes.  The
+    longest block is floor or ceil of the largest pitch (edge blocks aside);
+    its law is that of the max of s Gamma(2, sigma) draws, whose mean over
+    sigma grows like log s, i.e. like log log n when s = ceil(4 ln n)."""
+    sigma = 64.0
+    n = 65536
+    s = int(math.ceil(4 * math.log(n)))
+    bmax = []
+    dmax = []
+    for r in range(6):
+        params = orc.sample_params(90 + r, [sigma], s)
+        longest = max(int(np.diff(orc.block_starts(n, p[0], p[1])).max()) for p in params)
+        md = params[:, 0].max()
+        assert longest in (math.floor(md), math.ceil(md))
+        bmax.append(longest)
+    # law of max_k delta_k: KS against F(t)^s, F the Gamma(2, sigma) cdf
+    ratios = {}
+    for n_ in (65536, 131072, 524288):
+        s_ = int(math.ceil(4 * math.log(n_)))
+        R = 400
+        p = orc.sample_params(3, [sigma] * R, s_)[:, 0].reshape(R, s_)
+        mx = p.max(axis=1)
+        cdf = lambda t: scipy.stats.gamma(a=2, scale=sigma).cdf(t) ** s_
+        assert scipy.stats.kstest(mx, cdf).pvalue > 1e-4
+        emax = scipy.integrate.quad(lambda t: 1 - scipy.stats.gamma(a=2).cdf(t) ** s_, 0, 200)[0]
+        assert abs(mx.mean() / sigma - emax) <= 5 * mx.std(ddof=1) / sigma / math.sqrt(R)
+        ratios[n_] = emax / math.log(math.log(n_))
+    vals = list(ratios.values())
+    assert max(vals) / min(vals) < 1.1 and 2.0 < min(vals) < 3.2, ratios
+
+
+# ------------------------------------------------------------------- P7 ---
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,s,sigma", [(7, 3, 2.0), (33, 5, 6.0), (64, 9, 11.0)])
+def test_p7_brute_force_small_n(causal, n, s, sigma):
+    """Brute force from the definitions: dense masks built pair by pair from
+    the floor formula (no table), (A o sum_k M_k o C) V / row sums."""
+    rng = np.random.default_rng(n * 100 + s)
+    q, k, v = _rand_qkv(rng, 1, 2, 1, n, 5, scale=0.7)
+    params = orc.sample_params(5, [sigma, sigma * 0.5], s)
+    tables = []
+    for h in range(2):
+        tables.append([orc.block_starts(n, *params[h * s + kk]) for kk in range(s)])
+    got = orc.lsh_estimate(q, k, v, tables, causal)
+    for h in range(2):
+        c = np.zeros((n, n))
+        for kk in range(s):
+            dl, u = params[h * s + kk]
+            for i in range(n):
+                for j in range(n):
+                    same = math.floor((i + u) / dl) == math.floor((j + u) / dl)
+                    if same and (j <= i or not causal):
+                        c[i, j] += 1
+        w = c * np.exp(q[0, h] @ k[0, 0].T)
+        ref = (w @ v[0, 0]) / w.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(got[0, h], ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------- P8 ---
+@pytest.mark.parametrize("causal", [False, True])
+def test_p8_large_sigma_is_plain_softmax_attention(causal):
+    """Key results / no-bias baseline: as sigma -> inf every hash is one
+    block, so the estimate is textbook softmax attention; exact ALiBi agrees
+    up to its e^{-n/sigma} expansion."""
+    n, d = 50, 8
+    rng = np.random.default_rng(3)
+    q, k, v = _rand_qkv(rng, 1, 1, 1, n, d)
+    _, tabs = _tables(0, [1e12], 4, n)
+    for st in tabs[0]:
+        assert st.tolist() == [0, n]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        is_causal=causal, scale=1.0).numpy()
+    np.testing.assert_allclose(orc.lsh_estimate(q, k, v, tabs, causal), ref,
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(orc.exact_alibi(q, k, v, [1e12], causal), ref,
+                               rtol=1e-9, atol=1e-9)
+
+
+# ------------------------------------------------------------------- P9 ---
+def test_p9_small_sigma_returns_values():
+    """sigma -> 0: every block is a single position, so T~ = V exactly, and
+    the exact ALiBi output collapses to V as well."""
+    n, d = 40, 6
+    rng = np.random.default_rng(4)
+    q, k, v = _rand_qkv(rng, 1, 2, 2, n, d)
+    v = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+    _, tabs = _tables(2, [1e-3, 1e-3], 7, n)
+    for per in tabs:
+        for st in per:
+            assert st.tolist() == list(range(n + 1))
+    for causal in (False, True):
+        assert np.array_equal(orc.lsh_estimate(q, k, v, tabs, causal), v)
+        np.testing.assert_array_equal(orc.exact_alibi(q, k, v, [1e-3, 1e-3], causal), v)
+
+
+# ------------------------------------------------------------------ P10 ---
+def test_p10_single_hash_duplicates_and_order():
+    """Methodology §3: with s = 1 the estimate is plain attention inside each
+    block; s identical hashes give the s = 1 result; hash order is irrelevant."""
+    n, d = 60, 4
+    rng = np.random.default_rng(5)
+    q, k, v = _rand_qkv(rng, 1, 1, 1, n, d)
+    params = orc.sample_params(9, [8.0], 6)
+    sts = [orc.block_starts(n, *params[kk]) for kk in range(6)]
+    for causal in (False, True):
+        blk = np.searchsorted(sts[0], np.arange(n), side="right") - 1
+        allowed = blk[:, None] == blk[None, :]
+        if causal:
+            allowed &= np.tril(np.ones((n, n), dtype=bool))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            attn_mask=torch.from_numpy(allowed), scale=1.0).numpy()
+        one = orc.lsh_estimate(q, k, v, [[sts[0]]], causal)
+        np.testing.assert_allclose(one, ref, rtol=1e-12, atol=1e-12)
+        dup = orc.lsh_estimate(q, k, v, [[sts[0]] * 5], causal)
+        np.testing.assert_allclose(dup, one, rtol=1e-13, atol=1e-13)
+        a = orc.lsh_estimate(q, k, v, [sts], causal)
+        b = orc.lsh_estimate(q, k, v, [sts[::-1]], causal)
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ P11 ---
+@pytest.mark.parametrize("causal", [False, True])
+def test_p11_output_error_bounded_by_bias_error(causal):
+    """Methodology §3 (error bound): per row,
+    |T*_i - T~_i|_inf <= 2 max|V| sum_j |w*_ij - w~_ij| / sum_j w*_ij with
+    w* = e^{q.k} L*_ij, w~ = e^{q.k} M~_ij (both times the causal mask)."""
+    n, d, s = 80, 6, 6
+    rng = np.random.default_rng(6)
+    q, k, v = _rand_qkv(rng, 1, 2, 1, n, d, scale=0.8)
+    sig = [5.0, 20.0]
+    _, tabs = _tables(21, sig, s, n)
+    Tst = orc.exact_alibi(q, k, v, sig, causal)
+    Tt = orc.lsh_estimate(q, k, v, tabs, causal)
+    C = np.tril(np.ones((n, n))) if causal else np.ones((n, n))
+    for h in range(2):
+        A = np.exp(q[0, h] @ k[0, 0].T)
+        ws = A * orc.alibi_matrix(n, sig[h]) * C
+        wt = A * orc.mask_mean(n, tabs[h]) * C
+        bound = 2 * np.abs(v).max() * np.abs(ws - wt).sum(1) / ws.sum(1)
+        lhs = np.abs(Tst[0, h] - Tt[0, h]).max(axis=1)
+        assert np.all(lhs <= bound * (1 + 1e-12) + 1e-14)
+
+
+# ------------------------------------------------------------------ P12 ---
+def test_p12_convex_hull():
+    """T~_i is a convex combination of the values in the union of i's blocks."""
+    n, d, s = 90, 5, 5
+    rng = np.random.default_rng(8)
+    q, k, v = _rand_qkv(rng, 1, 1, 1, n, d)
+    _, tabs = _tables(4, [7.0], s, n)
+    for causal in (False, True):
+        T = orc.lsh_estimate(q, k, v, tabs, causal)[0, 0]
+        c = orc.multiplicity_dense(n, tabs[0], causal)
+        for i in range(n):
+            sup = v[0, 0][c[i] > 0]
+            assert np.all(T[i] >= sup.min(0) - 1e-12) and np.all(T[i] <= sup.max(0) + 1e-12)
+
+
+# ------------------------------------------------------------------ P13 ---
+@pytest.mark.parametrize("causal", [False, True])
+def test_p13_two_formulations_agree(causal):
+    """Per-hash log-sum-exp combination == explicit multiplicity sum."""
+    n, d, s = 150, 8, 10
+    rng = np.random.default_rng(10)
+    q, k, v = _rand_qkv(rng, 2, 4, 2, n, d)
+    _, tabs = _tables(12, [1.5, 6.0, 30.0, 400.0], s, n)
+    a = orc.lsh_estimate(q, k, v, tabs, causal)
+    b = orc.lsh_estimate_multiplicity(q, k, v, tabs, causal)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+def test_row_subset_mode_matches_full_mode():
+    n, d, s = 300, 8, 6
+    rng = np.random.default_rng(13)
+    q, k, v = _rand_qkv(rng, 1, 2, 1, n, d)
+    _, tabs = _tables(14, [3.0, 60.0], s, n)
+    rows = np.array([0, 1, 17, 150, 298, 299])
+    for causal in (False, True):
+        full = orc.lsh_estimate(q, k, v, tabs, causal)
+        sub = orc.lsh_estimate(q, k, v, tabs, causal, rows=rows)
+        np.testing.assert_allclose(sub, full[:, :, rows], rtol=1e-13, atol=1e-13)
+        ef = orc.exact_alibi(q, k, v, [3.0, 60.0], causal)
+        es = orc.exact_alibi(q, k, v, [3.0, 60.0], causal, rows=rows)
+        np.testing.assert_allclose(es, ef[:, :, rows], rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- O1 pins ---
+@pytest.mark.parametrize("causal", [False, True])
+def test_o1_exact_alibi_matches_library_attention_with_bias(causal):
+    """Methodology §1: ALiBi attention = softmax(q.k - |i-j|/sigma); checked
+    against the library attention routine with an additive bias."""
+    n, d = 70, 8
+    rng = np.random.default_rng(15)
+    q, k, v = _rand_qkv(rng, 2, 4, 2, n, d)
+    sig = [1.5, 4.0, 16.0, 256.0]
+    got = orc.exact_alibi(q, k, v, sig, causal)
+    x = np.arange(n)
+    for h in range(4):
+        bias = -np.abs(x[:, None] - x[None, :]) / sig[h]
+        if causal:
+            bias = np.where(x[None, :] <= x[:, None], bias, -np.inf)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[:, h]), torch.from_numpy(k[:, h // 2]),
+            torch.from_numpy(v[:, h // 2]), attn_mask=torch.from_numpy(bias),
+            scale=1.0).numpy()
+        np.testing.assert_allclose(got[:, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_o1_closed_form_geometric_sums():
+    """With q = 0 the exact output is a ratio of geometric sums:
+    sum_j r^{|i-j|} = (1 - r^{i+1} + r - r^{n-i}) / (1 - r), r = e^{-1/sigma}."""
+    n, sigma = 37, 3.0
+    q = np.zeros((1, 1, n, 1))
+    k = np.zeros((1, 1, n, 1))
+    v = np.ones((1, 1, n, 1))
+    v2 = np.zeros((1, 1, n, 1))
+    v2[0, 0, 0, 0] = 1.0
+    r = math.exp(-1 / sigma)
+    T = orc.exact_alibi(q, k, v2, [sigma], False)[0, 0, :, 0]
+    for i in range(n):
+        den = (1 - r ** (i + 1) + r - r ** (n - i)) / (1 - r)
+        assert abs(T[i] - r ** i / den) <= 1e-14
+    assert np.allclose(orc.exact_alibi(q, k, v, [sigma], True), 1.0, atol=1e-15)
+
+
+# ---------------------------------------------------------------- O5 pins ---
+@pytest.mark.parametrize("causal", [False, True])
+def test_o5_work_counts_brute_force(causal):
+    n, s = 45, 4
+    _, tabs = _tables(16, [2.0, 9.0], s, n)
+    alg, distinct = orc.work_counts(n, tabs, causal)
+    C = np.tril(np.ones((n, n), dtype=np.int64)) if causal else np.ones((n, n), dtype=np.int64)
+    want_alg = sum(int((orc.mask_dense(n, st) * C).sum()) for per in tabs for st in per)
+    want_distinct = sum(int((orc.multiplicity_dense(n, per, causal) > 0).sum()) for per in tabs)
+    assert (alg, distinct) == (want_alg, want_distinct)
+
+
+def test_sampler_stream_is_splitmix64():
+    """The published SplitMix64 reference vector: seed 1234567 gives
+    6457827717110365317, 3203168211198807973, 9817491932198370423 first."""
+    want = [6457827717110365317, 3203168211198807973, 9817491932198370423]
+    assert [orc.splitmix64(1234567, i) for i in range(3)] == want
