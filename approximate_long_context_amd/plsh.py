@@ -1,0 +1,198 @@
+"""ctypes binding of libplsh (include/plsh.h): argument marshalling only.
+
+Every step of the estimator runs inside the library; torch supplies device
+memory and the current HIP stream.  Loading fails loudly when the library has
+not been built: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libplsh.so")
+
+PLSH_OK, PLSH_ERR_ARG, PLSH_ERR_TABLE, PLSH_ERR_UNSUPPORTED, PLSH_ERR_CAPACITY, PLSH_ERR_HIP = range(6)
+PLSH_BF16, PLSH_F32 = 0, 1
+STATUS_NAMES = {0: "PLSH_OK", 1: "PLSH_ERR_ARG", 2: "PLSH_ERR_TABLE", 3: "PLSH_ERR_UNSUPPORTED",
+                4: "PLSH_ERR_CAPACITY", 5: "PLSH_ERR_HIP"}
+
+EXPORTED = ["plsh_sample_tables", "plsh_validate_tables", "plsh_count_work",
+            "plsh_alibi_attention", "plsh_debug_block_intervals",
+            "plsh_debug_attention_reference", "plsh_last_error"]
+
+
+class PlshError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Tables(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("heads", ctypes.c_int32), ("s", ctypes.c_int32),
+                ("params", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("starts", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libplsh.so (built by approximate_long_context_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m approximate_long_context_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, u64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+        TP = ctypes.POINTER(_Tables)
+        L.plsh_sample_tables.argtypes = [u64, i32, i32, vp, i32, vp, vp, vp, i64, ctypes.POINTER(i64)]
+        L.plsh_validate_tables.argtypes = [TP]
+        L.plsh_count_work.argtypes = [TP, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        attn = [vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp, i32, TP, i32, vp]
+        L.plsh_alibi_attention.argtypes = attn
+        L.plsh_debug_attention_reference.argtypes = attn
+        L.plsh_debug_block_intervals.argtypes = [TP, vp, vp]
+        for f in EXPORTED[:-1]:
+            getattr(L, f).restype = ctypes.c_int
+        L.plsh_last_error.restype = ctypes.c_char_p
+        L.plsh_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != PLSH_OK:
+        raise PlshError(status, lib().plsh_last_error().decode())
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+@dataclass
+class Tables:
+    """Boundary table of s hashes per head (host arrays; see include/plsh.h)."""
+    n: int
+    heads: int
+    s: int
+    params: np.ndarray   # float64 [heads*s, 2]
+    offsets: np.ndarray  # int32 [heads*s + 1]
+    starts: np.ndarray   # int32 [offsets[-1]]
+
+    def c_struct(self) -> _Tables:
+        return _Tables(self.n, self.heads, self.s, _ptr(self.params), _ptr(self.offsets),
+                       _ptr(self.starts))
+
+    def to(self, device) -> "DeviceTables":
+        return DeviceTables(self.n, self.heads, self.s,
+                            torch.from_numpy(self.params).to(device),
+                            torch.from_numpy(self.offsets).to(device),
+                            torch.from_numpy(self.starts).to(device))
+
+    def starts_of(self, h: int, k: int) -> np.ndarray:
+        r = h * self.s + k
+        return self.starts[self.offsets[r]:self.offsets[r + 1]]
+
+
+@dataclass
+class DeviceTables:
+    """The same table resident on the GPU (torch tensors own the memory)."""
+    n: int
+    heads: int
+    s: int
+    params: torch.Tensor
+    offsets: torch.Tensor
+    starts: torch.Tensor
+
+    def c_struct(self) -> _Tables:
+        return _Tables(self.n, self.heads, self.s, self.params.data_ptr(), self.offsets.data_ptr(),
+                       self.starts.data_ptr())
+
+
+def sample_tables(seed: int, n: int, sigma: Sequence[float], s: int) -> Tables:
+    """plsh_sample_tables (two-call protocol)."""
+    L = lib()
+    sig = np.ascontiguousarray(sigma, dtype=np.float64)
+    heads = len(sig)
+    params = np.empty((heads * s, 2), dtype=np.float64)
+    offsets = np.empty(heads * s + 1, dtype=np.int32)
+    need = ctypes.c_int64(0)
+    _check(L.plsh_sample_tables(seed, n, heads, _ptr(sig), s, _ptr(params), _ptr(offsets), None, 0,
+                                ctypes.byref(need)))
+    starts = np.empty(max(need.value, 1), dtype=np.int32)
+    _check(L.plsh_sample_tables(seed, n, heads, _ptr(sig), s, _ptr(params), _ptr(offsets),
+                                _ptr(starts), starts.size, ctypes.byref(need)))
+    return Tables(n, heads, s, params, offsets, starts[:need.value])
+
+
+def validate_tables(t: Tables) -> None:
+    st = t.c_struct()
+    _check(lib().plsh_validate_tables(ctypes.byref(st)))
+
+
+def count_work(t: Tables, causal: bool):
+    """(pairs_alg, pairs_distinct) per batch element."""
+    st = t.c_struct()
+    a, d = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().plsh_count_work(ctypes.byref(st), int(bool(causal)), ctypes.byref(a), ctypes.byref(d)))
+    return a.value, d.value
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PLSH_BF16
+    if t.dtype == torch.float32:
+        return PLSH_F32
+    raise PlshError(PLSH_ERR_UNSUPPORTED, f"dtype {t.dtype} not supported")
+
+
+def _attention(fn, q, k, v, sigma, s, tables: DeviceTables, causal, out, stream):
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if not x.is_contiguous():
+            raise PlshError(PLSH_ERR_ARG, f"{name} must be contiguous")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise PlshError(PLSH_ERR_ARG, "q [B,H,n,d], k/v [B,Hkv,n,d] with one dtype expected")
+    B, H, n, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    sig = np.ascontiguousarray(sigma, dtype=np.float64)
+    if sig.size != H:
+        raise PlshError(PLSH_ERR_ARG, "sigma must have one entry per query head")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = tables.c_struct()
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, n, H, k.shape[1], d,
+              _dtype_code(q), _ptr(sig), s, ctypes.byref(st), int(bool(causal)), stream))
+    return out
+
+
+def attention(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
+              out: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
+    """plsh_alibi_attention on the current stream: q [B,H,n,d], k/v [B,Hkv,n,d]."""
+    return _attention(lib().plsh_alibi_attention, q, k, v, sigma, s, tables, causal, out, stream)
+
+
+def attention_reference(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
+                        out: Optional[torch.Tensor] = None, stream: Optional[int] = None):
+    """plsh_debug_attention_reference: the one-row-per-wave VALU formulation."""
+    return _attention(lib().plsh_debug_attention_reference, q, k, v, sigma, s, tables, causal, out,
+                      stream)
+
+
+def debug_block_intervals(tables: DeviceTables, stream: Optional[int] = None) -> torch.Tensor:
+    """int32 [heads*s, n, 2] (lo, hi) recomputed on the GPU."""
+    lohi = torch.empty((tables.heads * tables.s, tables.n, 2), dtype=torch.int32,
+                       device=tables.params.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(lohi.device).cuda_stream
+    st = tables.c_struct()
+    _check(lib().plsh_debug_block_intervals(ctypes.byref(st), lohi.data_ptr(), stream))
+    return lohi

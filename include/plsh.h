@@ -1,0 +1,173 @@
+/*
+ * plsh.h -- C ABI of the Positional-LSH ALiBi attention library (libplsh.so).
+ *
+ * Method: "Positional LSH: Binary Block Matrix Approximation for Attention
+ * with Linear Biases" (Wolfson & Wagner), technical-summary pages.
+ *   Methodology §1: the ALiBi bias L*_ij = exp(-|i-j|/sigma) is a Laplacian
+ *     kernel on positions; random binning of integer positions gives hashes h
+ *     whose 0/1 same-bin masks M(h) are contiguous block-diagonal and satisfy
+ *     L* = E_h[M(h)].
+ *   Methodology §2 (Theorem 2.1): M~ = (1/s) sum_k M(h_k) approximates L*;
+ *     blocks stay short (b_max ~ sigma log log n); the bins follow a Gamma law.
+ *   Methodology §3 (Theorem 2.2): ALiBi attention reduces to s randomized
+ *     short-context attentions without positional bias, in near-linear time.
+ *
+ * The estimator computed here is the ratio of sums
+ *   T~ = D~^-1 (A o M~ o C) V,  D~ = diag((A o M~ o C) 1),  A = exp(Q K^T),
+ * with C the optional causal mask and logits q.k taken with scale 1.
+ *
+ * Conventions shared by every entry point:
+ *   - Every call returns a plsh_status; nothing throws across the ABI.  On a
+ *     non-OK status no device work has been enqueued and plsh_last_error()
+ *     describes the failure.
+ *   - Host pointers are read during the call only; the library keeps no
+ *     reference to any caller buffer after it returns (device work enqueued on
+ *     `stream` reads device buffers until it completes: they must stay alive
+ *     until then).  The library allocates no device memory.
+ *   - The library keeps no state besides a thread-local error string.
+ */
+#ifndef PLSH_H
+#define PLSH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PLSH_OK = 0,
+  PLSH_ERR_ARG = 1,          /* null pointer, bad size, bad sigma, aliasing       */
+  PLSH_ERR_TABLE = 2,        /* malformed table or table/call mismatch            */
+  PLSH_ERR_UNSUPPORTED = 3,  /* head dim / dtype / size not supported             */
+  PLSH_ERR_CAPACITY = 4,     /* caller buffer too small (sampler two-call protocol)*/
+  PLSH_ERR_HIP = 5           /* no HIP device, or a HIP launch/runtime error      */
+} plsh_status;
+
+typedef enum { PLSH_BF16 = 0, PLSH_F32 = 1 } plsh_dtype;
+
+/* A HIP stream handle (hipStream_t); NULL selects the null stream. */
+typedef void *plsh_stream_t;
+
+/*
+ * Boundary table of s random-binning hashes per head (a view: the caller owns
+ * every array).  For head h and sample k, row r = h*s + k:
+ *   params[2r] = delta (pitch, > 0), params[2r+1] = u (offset, 0 <= u < delta);
+ *   bin_r(x) = floor((x + u) / delta) in IEEE binary64 (add, divide, floor);
+ *   starts[offsets[r] .. offsets[r+1]) lists 0, every x in 1..n-1 with
+ *   bin_r(x) != bin_r(x-1), and finally n (strictly increasing).
+ * (Methodology §1: a hash partitions positions into contiguous bins.)
+ * Depending on the call the arrays are host or device pointers (see below).
+ */
+typedef struct {
+  int32_t n;
+  int32_t heads;
+  int32_t s;
+  const double *params;    /* [heads*s][2]                                      */
+  const int32_t *offsets;  /* [heads*s + 1], offsets[0] == 0                    */
+  const int32_t *starts;   /* [offsets[heads*s]]                                */
+} plsh_tables;
+
+/*
+ * plsh_sample_tables -- draw the hashes and build their boundary table (host).
+ * Methodology §1 (random binning on positions) and §2 (Gamma law): for every
+ * (head h, sample k) draws delta ~ Gamma(shape 2, scale sigma[h]) as
+ * -sigma (ln U1 + ln U2) and u = delta * U3, U1, U2 in (0,1), U3 in [0,1),
+ * from a SplitMix64 stream used as a counter-based generator keyed by
+ * (seed, h, k): draw i = ((h << 32) | k) * 4 + j, j = 0, 1, 2.  Deterministic
+ * in (seed, n, sigma[], s); sample k of head h does not depend on s.
+ *   seed            generator key
+ *   n               sequence length, >= 1
+ *   heads, sigma    sigma[heads] (host), each finite and > 0
+ *   s               samples per head, >= 1
+ *   params          out, host [heads*s][2]
+ *   offsets         out, host [heads*s + 1]
+ *   starts          out, host [starts_capacity], may be NULL
+ *   starts_needed   out, host: total entries the table needs
+ * Two-call protocol: with starts == NULL (or too small a capacity) params,
+ * offsets and *starts_needed are written and the call returns PLSH_OK
+ * (starts == NULL) or PLSH_ERR_CAPACITY (capacity too small); a second call
+ * with a large enough buffer fills starts.  Needs no GPU.
+ */
+plsh_status plsh_sample_tables(uint64_t seed, int32_t n, int32_t heads, const double *sigma,
+                               int32_t s, double *params, int32_t *offsets, int32_t *starts,
+                               int64_t starts_capacity, int64_t *starts_needed);
+
+/*
+ * plsh_validate_tables -- check a table (all arrays HOST pointers): sizes > 0,
+ * every delta finite and > 0, 0 <= u < delta, offsets[0] == 0 and
+ * non-decreasing, each row strictly increasing from 0 to n, and every row's
+ * starts equal to the bin changes of its (delta, u) (Methodology §1: bins are
+ * contiguous and non-overlapping).  Returns PLSH_ERR_TABLE on the first
+ * violation.  Needs no GPU.
+ */
+plsh_status plsh_validate_tables(const plsh_tables *host_tables);
+
+/*
+ * plsh_count_work -- work counts of one batch element, summed over heads
+ * (HOST table).  Methodology §3 (Theorem 2.2 cost):
+ *   pairs_alg      = sum over (h, k, block of length L) of L^2 (causal:
+ *                    L(L+1)/2): the literal s-short-attention pair count;
+ *   pairs_distinct = sum over (h, i) of |U_h(i) & J(i)|, U_h(i) the union of
+ *                    the s blocks containing i (one interval), J(i) = [0, n)
+ *                    or [0, i] when causal: the nonzeros of M~ o C.
+ * Needs no GPU.
+ */
+plsh_status plsh_count_work(const plsh_tables *host_tables, int32_t causal,
+                            int64_t *pairs_alg, int64_t *pairs_distinct);
+
+/*
+ * plsh_alibi_attention -- the estimator T~ on the GPU (asynchronous).
+ * Methodology §3 (Theorem 2.2): s randomized short-context attentions without
+ * positional bias, fused over the samples: each query row i attends to the
+ * union of its s blocks with integer weights c_ij = #{k : j in B_k(i)}
+ * (times the causal mask), T~_i = sum_j c_ij e^{q_i.k_j} v_j /
+ * sum_j c_ij e^{q_i.k_j}.
+ *   q, out      DEVICE [batch][heads][n][d], contiguous
+ *   k, v        DEVICE [batch][kv_heads][n][d], contiguous; query head h reads
+ *               kv head h / (heads / kv_heads)
+ *   dtype       element type of q, k, v and out (bf16 or fp32); accumulation
+ *               is fp32; bf16 results are rounded to nearest even
+ *   d           head dim: 64 or 128
+ *   sigma       HOST [heads], finite and > 0: checked, and orders the heads
+ *               heavy-first for scheduling; the blocks come from `boundaries`
+ *   s           samples per head (== boundaries->s)
+ *   boundaries  HOST struct; params is a DEVICE pointer read by the kernel
+ *               (block intervals are recomputed from (delta, u) with the same
+ *               binary64 predicate); offsets/starts are not read and may be
+ *               NULL.  n/heads/s must match the call.
+ *   causal      0 or 1
+ *   stream      HIP stream for the launch
+ * Buffers must be 16-byte aligned; out must not overlap q, k or v.
+ * Errors: PLSH_ERR_ARG (null pointer, n < 1, batch < 1, heads or kv_heads < 1,
+ * heads % kv_heads != 0, s < 1, sigma not finite or <= 0, aliasing),
+ * PLSH_ERR_TABLE (boundaries mismatch), PLSH_ERR_UNSUPPORTED (d not 64/128,
+ * batch*heads*n*d >= 2^31, s > 255), PLSH_ERR_HIP (launch error).  Execution
+ * faults surface at the caller's next synchronisation.
+ */
+plsh_status plsh_alibi_attention(const void *q, const void *k, const void *v, void *out,
+                                 int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                 int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                 const plsh_tables *boundaries, int32_t causal,
+                                 plsh_stream_t stream);
+
+/*
+ * plsh_debug_block_intervals -- writes, for every (head h, sample k, position
+ * i), the block [lo, hi) containing i as recomputed on the GPU by the same
+ * per-tile interval code the attention kernel runs (Methodology §1 blocks):
+ *   lohi  DEVICE int32 [heads*s][n][2], (lo, hi) pairs
+ * boundaries as for plsh_alibi_attention (params on the device).  Test aid:
+ * the result must equal the host table bit for bit.
+ */
+plsh_status plsh_debug_block_intervals(const plsh_tables *boundaries, int32_t *lohi,
+                                       plsh_stream_t stream);
+
+/* Thread-local, NUL-terminated description of the last non-OK status of this
+ * thread ("" if none).  Valid until the thread's next plsh_* call. */
+const char *plsh_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLSH_H */

@@ -1,0 +1,270 @@
+"""GPU parity of libplsh against the fp64 CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (ctypes binding).  Inputs are the seeded
+synthetic workloads; the oracle reads exactly the values the GPU sees
+(bf16/fp32 upcast to fp64) and the same hash parameters, deriving its blocks
+by its own scan.
+
+Tolerances: fp32 path max|O - T~| <= 1e-5 max|T~| per (batch, head) slab;
+bf16 path |O - T~| <= 1e-2 beyond the half-ulp of rounding T~ itself to bf16
+(the output is specified as T~ rounded to nearest-even bf16); block
+intervals bit-exact.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from approximate_long_context_amd import plsh, workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    plsh.lib()
+    return torch.device("cuda:0")
+
+
+def bf16_excess(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max(|gpu - ref| - half ulp of bf16 at |ref|)."""
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    half = np.where(a > 0, 2.0 ** (e - 8), 0.0)
+    return float((np.abs(gpu - ref) - half).max())
+
+
+def check_bf16(gpu, ref, tol=1e-2, what=""):
+    ex = bf16_excess(gpu, ref)
+    mx = float(np.abs(gpu - ref).max())
+    say(what, f"bf16 max|diff|={mx:.3e} excess-over-rounding={ex:.3e}")
+    assert ex <= tol, (what, mx, ex)
+
+
+def check_f32(gpu, ref, what=""):
+    B, H = ref.shape[:2]
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            d = np.abs(gpu[b, h] - ref[b, h]).max() / np.abs(ref[b, h]).max()
+            worst = max(worst, d)
+    say(what, f"fp32 normwise rel err={worst:.3e}")
+    assert worst <= 1e-5, (what, worst)
+
+
+def run_case(dev, w: W.Workload, rows=None, reference=False, seed=None, tables=None):
+    """GPU output (fp64 numpy) and oracle output for workload w."""
+    q, k, v = W.make_qkv(w, seed=seed)
+    t = tables or plsh.sample_tables(w.hash_seed, w.n, w.sigma, w.s)
+    dt = t.to(dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    fn = plsh.attention_reference if reference else plsh.attention
+    say(w.name, "B", w.batch, "H", w.heads, "Hkv", w.kv_heads, "n", w.n, "d", w.d, "s", w.s,
+        "causal", w.causal, "rows", None if rows is None else len(rows), "ref" if reference else "")
+    out = fn(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal)
+    torch.cuda.synchronize()
+    o = W.to_f64(out)
+    off, st = orc.tables_from_params(w.n, t.params)
+    tabs = orc.starts_per_head(off, st, w.heads, w.s)
+    qf, kf, vf = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    if rows is None:
+        ref = orc.lsh_estimate(qf, kf, vf, tabs, w.causal)
+        return o, ref, (qf, kf, vf, tabs)
+    ref = orc.lsh_estimate(qf, kf, vf, tabs, w.causal, rows=rows)
+    return o[:, :, rows], ref, (qf, kf, vf, tabs)
+
+
+def small(name, B, H, Hkv, n, d, dtype, causal, sigma, s, heavy=False):
+    return W.Workload(name, B, H, Hkv, n, d, dtype, causal, list(sigma), s, heavy_tail=heavy)
+
+
+# ------------------------------------------------------------------- G1 ---
+@pytest.mark.parametrize("wname", ["tiny-f32-n512", "slopes-n4096", "qwen3-0.6b-n8192-s20",
+                                   "mistral-7b-n16384-s40", "long-n65536"])
+def test_g1_block_intervals_bit_exact(dev, wname):
+    """Methodology §1 blocks: the GPU's per-wave interval recomputation
+    equals the oracle's full scan for every (head, sample, position)."""
+    w = W.get(wname)
+    t = plsh.sample_tables(w.hash_seed, w.n, w.sigma, w.s)
+    say("G1", wname)
+    lohi = plsh.debug_block_intervals(t.to(dev)).cpu().numpy()
+    off, st = orc.tables_from_params(w.n, t.params)
+    for r in range(w.heads * w.s):
+        lo, hi = orc.block_intervals(w.n, st[off[r]:off[r + 1]])
+        assert np.array_equal(lohi[r, :, 0], lo), r
+        assert np.array_equal(lohi[r, :, 1], hi), r
+
+
+def test_g1_block_intervals_extreme_pitches(dev):
+    n = 5000
+    sig = [1e-3, 0.3, 1.0, 1.19, 3.7, 31.0, 500.0, 1e12]
+    t = plsh.sample_tables(77, n, sig, 9)
+    lohi = plsh.debug_block_intervals(t.to(dev)).cpu().numpy()
+    off, st = orc.tables_from_params(n, t.params)
+    for r in range(len(sig) * 9):
+        lo, hi = orc.block_intervals(n, st[off[r]:off[r + 1]])
+        assert np.array_equal(lohi[r, :, 0], lo) and np.array_equal(lohi[r, :, 1], hi), r
+
+
+def test_g1_block_intervals_512k_two_heads(dev):
+    n = 524288
+    s = W.long_context_s(n)
+    t = plsh.sample_tables(0, n, [64.0, 64.0], s)
+    lohi = plsh.debug_block_intervals(t.to(dev)).cpu().numpy()
+    off, st = orc.tables_from_params(n, t.params)
+    for r in range(2 * s):
+        lo, hi = orc.block_intervals(n, st[off[r]:off[r + 1]])
+        assert np.array_equal(lohi[r, :, 0], lo) and np.array_equal(lohi[r, :, 1], hi), r
+
+
+# ------------------------------------------------------------ G2 / G3 ---
+def test_g2_fp32_tiny_config(dev):
+    w = W.get("tiny-f32-n512")
+    o, ref, _ = run_case(dev, w)
+    check_f32(o, ref, w.name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_ragged_gqa(dev, d, causal):
+    w = small("f32-ragged", 2, 4, 2, 1000, d, "f32", causal, [1.3, 9.0, 60.0, 700.0], 7)
+    o, ref, _ = run_case(dev, w)
+    check_f32(o, ref, w.name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_ragged_gqa_full(dev, d, causal):
+    """Several tiles, a ragged tail, GQA, heads of very different sigma."""
+    w = small("bf16-ragged", 2, 4, 2, 1000, d, "bf16", causal, [1.3, 9.0, 60.0, 700.0], 7)
+    o, ref, _ = run_case(dev, w)
+    check_bf16(o, ref, what=f"{w.name} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 33, 127, 129, 255, 257])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_small_n_edges(dev, n, causal):
+    w = small(f"edge-n{n}", 1, 2, 1, n, 128, "bf16", causal, [3.0, 40.0], 5)
+    o, ref, _ = run_case(dev, w)
+    check_bf16(o, ref, what=w.name)
+
+
+@pytest.mark.parametrize("s", [1, 2, 255])
+def test_bf16_sample_count_edges(dev, s):
+    w = small(f"edge-s{s}", 1, 3, 3, 700, 64, "bf16", True, [1.5, 12.0, 90.0], s)
+    o, ref, _ = run_case(dev, w)
+    check_bf16(o, ref, what=w.name)
+
+
+def test_g3_slopes_config_full(dev):
+    w = W.get("slopes-n4096")
+    o, ref, _ = run_case(dev, w)
+    check_bf16(o, ref, what=w.name)
+
+
+@pytest.mark.parametrize("wname,nrows", [
+    ("qwen3-0.6b-n8192-s10", 96), ("qwen3-0.6b-n8192-s20", 96),
+    ("mistral-7b-n16384-s10", 64), ("mistral-7b-n16384-s20", 64), ("mistral-7b-n16384-s40", 64),
+    ("long-n65536", 128), ("long-n131072", 64)])
+def test_g3_full_size_sampled_rows(dev, wname, nrows):
+    """Full-size workloads in the benchmark's launch configuration; the
+    oracle evaluates seeded sampled rows one by one."""
+    w = W.get(wname)
+    rows = W.sample_rows(w.n, nrows, seed=17)
+    o, ref, _ = run_case(dev, w, rows=rows)
+    check_bf16(o, ref, what=w.name)
+
+
+def test_g3_long_512k_sampled_rows(dev):
+    w = W.get("long-n524288")
+    rows = W.sample_rows(w.n, 32, seed=19)
+    o, ref, _ = run_case(dev, w, rows=rows)
+    check_bf16(o, ref, what=w.name)
+
+
+def test_mfma_matches_valu_reference(dev):
+    """Two independent GPU formulations of the same estimator agree."""
+    w = W.get("mistral-7b-n16384-s20")
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(0, w.n, w.sigma, w.s).to(dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    a = plsh.attention(qd, kd, vd, w.sigma, w.s, t, causal=True).float()
+    b = plsh.attention_reference(qd, kd, vd, w.sigma, w.s, t, causal=True).float()
+    torch.cuda.synchronize()
+    diff = (a - b).abs().max().item()
+    say("mfma vs valu", diff)
+    assert diff <= 2e-2
+
+
+# ------------------------------------------------------------------- G4 ---
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_g4_tiny_sigma_returns_v_bitwise(dev, dtype, causal):
+    """sigma -> 0: every block is one position, so T~ = V exactly."""
+    w = small("tiny-sigma", 1, 4, 2, 300, 64, dtype, causal, [1e-3] * 4, 8)
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(1, w.n, w.sigma, w.s).to(dev)
+    out = plsh.attention(q.to(dev), k.to(dev), v.to(dev), w.sigma, w.s, t, causal=causal).cpu()
+    vr = v.repeat_interleave(2, dim=1)
+    assert torch.equal(out, vr)
+
+
+# ------------------------------------------------------------------- G5 ---
+def test_g5_gqa_equals_repeated_kv(dev):
+    w = small("gqa", 1, 8, 2, 900, 128, "bf16", True, [2.0, 4.0, 8.0, 16.0, 32.0, 64.0, 128.0, 256.0], 9)
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(4, w.n, w.sigma, w.s).to(dev)
+    a = plsh.attention(q.to(dev), k.to(dev), v.to(dev), w.sigma, w.s, t, causal=True)
+    kr = k.repeat_interleave(4, dim=1).contiguous()
+    vr = v.repeat_interleave(4, dim=1).contiguous()
+    b = plsh.attention(q.to(dev), kr.to(dev), vr.to(dev), w.sigma, w.s, t, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------- G6 ---
+def test_g6_batch_slice_and_determinism(dev):
+    w = small("batch", 3, 4, 4, 700, 64, "bf16", False, [1.5, 6.0, 30.0, 300.0], 6)
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(8, w.n, w.sigma, w.s).to(dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    full = plsh.attention(qd, kd, vd, w.sigma, w.s, t)
+    again = plsh.attention(qd, kd, vd, w.sigma, w.s, t)
+    one = plsh.attention(qd[1:2].contiguous(), kd[1:2].contiguous(), vd[1:2].contiguous(), w.sigma,
+                         w.s, t)
+    torch.cuda.synchronize()
+    assert torch.equal(full, again)
+    assert torch.equal(full[1:2], one)
+
+
+# ------------------------------------------------------------------- G7 ---
+@pytest.mark.parametrize("causal", [False, True])
+def test_g7_huge_sigma_is_softmax_attention(dev, causal):
+    """Key results (model without bias): sigma -> inf gives plain softmax
+    attention; compared with library attention in fp32 on the CPU."""
+    w = small("huge-sigma", 1, 2, 1, 600, 128, "bf16", causal, [1e12, 1e12], 4)
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(2, w.n, w.sigma, w.s).to(dev)
+    out = plsh.attention(q.to(dev), k.to(dev), v.to(dev), w.sigma, w.s, t, causal=causal)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.float(), k.float().repeat_interleave(2, 1), v.float().repeat_interleave(2, 1),
+        is_causal=causal, scale=1.0)
+    check_bf16(out.cpu().double().numpy(), ref.double().numpy(), what="G7")
+
+
+def test_error_after_bad_call_leaves_no_work(dev):
+    w = small("err", 1, 2, 1, 64, 64, "bf16", True, [2.0, 3.0], 3)
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(0, w.n, w.sigma, w.s).to(dev)
+    with pytest.raises(plsh.PlshError) as e:
+        plsh.attention(q.to(dev), k.to(dev), v.to(dev), w.sigma, w.s + 1, t, causal=True)
+    assert e.value.status == plsh.PLSH_ERR_TABLE
