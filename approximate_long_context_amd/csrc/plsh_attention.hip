@@ -44,6 +44,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxHeadsArg = 128;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -110,25 +112,82 @@ __device__ __forceinline__ uint32_t bits_1_to(int t) {
   return t == 0 ? 0u : ((0xFFFFFFFFu >> (31 - t)) & ~1u);
 }
 
-// Per-wave block setup for rows [r0, r0 + 32) of one head (see file header).
-// Lanes take samples k = lane, lane + 64, ...
-__device__ void wave_setup(const double *prm, int s, int n, int r0, int lane, int32_t *lead,
-                           int32_t *trail, uint32_t *mask) {
+// Per-wave block setup for rows [r0, r0 + 32) of one head (see file header),
+// in LDS scratch of the wave.
+struct WaveTab {
+  double *prm;     // [2s] (delta, u) of the head, staged once
+  int32_t *lead;   // [s]
+  int32_t *trail;  // [s]
+  uint32_t *mask;  // [s]
+  int32_t *act;    // [s] samples with a block start inside the wave's rows
+};
+
+// bytes of LDS a WaveTab needs (16-byte multiple)
+__host__ __device__ constexpr size_t wavetab_bytes(int s) { return ((size_t)16 * s + 16 * s + 15) & ~(size_t)15; }
+
+__device__ __forceinline__ WaveTab carve_wavetab(uint8_t *base, int s) {
+  WaveTab w;
+  w.prm = (double *)base;
+  w.lead = (int32_t *)(base + 16 * (size_t)s);
+  w.trail = w.lead + s;
+  w.mask = (uint32_t *)(w.trail + s);
+  w.act = (int32_t *)(w.mask + s);
+  return w;
+}
+
+// Step 1: lanes take samples k = lane, lane + 64, ...: stage (delta, u) in
+// LDS, find the block of row r0 (lead) and of the wave's last row (trail),
+// and list the samples whose bins differ between those rows.  Returns the
+// number of listed samples (the same in every lane).
+__device__ int wave_ends(const double *prm, int s, int n, int r0, int lane, const WaveTab &w) {
   const int last = min(r0 + 31, n - 1);
-  for (int k = lane; k < s; k += 64) {
-    const double dl = prm[2 * k], u = prm[2 * k + 1];
-    const double b = bin_of(r0, dl, u);
-    const int32_t lo = block_lo(r0, dl, u, b);
-    int32_t y = block_hi(r0, n, dl, u, b);
-    uint32_t m = 0;
-    while (y <= last) {  // y starts a block inside (r0, last]
-      m |= 1u << (y - r0);
-      y = block_hi(y, n, dl, u, bin_of(y, dl, u));
+  int nact = 0;
+  for (int k0 = 0; k0 < s; k0 += 64) {
+    const int k = k0 + lane;
+    bool cross = false;
+    if (k < s) {
+      const double dl = prm[2 * k], u = prm[2 * k + 1];
+      w.prm[2 * k] = dl;
+      w.prm[2 * k + 1] = u;
+      const double b0 = bin_of(r0, dl, u), b1 = bin_of(last, dl, u);
+      w.lead[k] = block_lo(r0, dl, u, b0);
+      w.trail[k] = block_hi(last, n, dl, u, b1);
+      w.mask[k] = 0u;
+      cross = b0 != b1;
     }
-    lead[k] = lo;
-    trail[k] = y;
-    mask[k] = m;
+    const uint64_t bal = __ballot(cross);
+    if (cross) w.act[nact + __popcll(bal & ((1ull << lane) - 1ull))] = k;
+    nact += __popcll(bal);
   }
+  return nact;
+}
+
+// Step 2: start masks of the listed samples.  The two half-waves take one
+// sample each and lane t evaluates the bin of position r0 + t, so a start is
+// a bin change between neighbouring lanes.
+__device__ void wave_masks(int n, int r0, int lane, int nact, const WaveTab &w) {
+  const int last = min(r0 + 31, n - 1);
+  const int t = lane & 31, hh = lane >> 5;
+  const int x = r0 + t;
+#pragma unroll 2
+  for (int a0 = 0; a0 < nact; a0 += 2) {
+    const int ai = a0 + hh;
+    const bool have = ai < nact;
+    const int k = have ? w.act[ai] : 0;
+    const bool valid = have && x <= last;
+    double b = 0.0;
+    if (valid) b = bin_of(x, w.prm[2 * k], w.prm[2 * k + 1]);
+    const double bp = __shfl_up(b, 1, 32);
+    const uint64_t bal = __ballot(valid && t > 0 && b != bp);
+    if (t == 0 && have) w.mask[k] = (uint32_t)(bal >> (32 * hh));
+  }
+}
+
+__device__ void wave_setup(const double *prm, int s, int n, int r0, int lane, const WaveTab &w) {
+  const int nact = wave_ends(prm, s, n, r0, lane, w);
+  wave_sync();
+  wave_masks(n, r0, lane, nact, w);
+  wave_sync();
 }
 
 __device__ __forceinline__ int32_t row_lo(int32_t lead, uint32_t mask, int r0, int t) {
@@ -146,16 +205,15 @@ __device__ __forceinline__ int32_t row_hi(int32_t trail, uint32_t mask, int r0, 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void debug_intervals_kernel(const double *params, int n, int heads,
                                                              int s, int groups, int32_t *lohi) {
-  extern __shared__ uint8_t smem[];
-  int32_t *lead = (int32_t *)smem;
-  int32_t *trail = lead + s;
-  uint32_t *mask = (uint32_t *)(trail + s);
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const WaveTab w = carve_wavetab(smem, s);
+  const int32_t *lead = w.lead, *trail = w.trail;
+  const uint32_t *mask = w.mask;
   const int lane = threadIdx.x;
   const int h = blockIdx.x / groups;
   const int r0 = (blockIdx.x % groups) * 32;
   if (h >= heads) return;
-  wave_setup(params + 2 * (int64_t)h * s, s, n, r0, lane, lead, trail, mask);
-  wave_sync();
+  wave_setup(params + 2 * (int64_t)h * s, s, n, r0, lane, w);
   const int t = lane & 31;
   const int i = r0 + t;
   if (i >= n) return;
@@ -188,18 +246,21 @@ __device__ __forceinline__ void store_elem<uint16_t>(uint16_t *p, int64_t i, flo
   p[i] = (uint16_t)f32_to_bf16_bits(v);
 }
 
+__host__ __device__ constexpr size_t valu_wave_bytes(int s, int D) {
+  return (wavetab_bytes(s) + (size_t)8 * s + 4 * D + 256 + 15) & ~(size_t)15;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) {
-  extern __shared__ uint8_t smem[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int s = a.s, n = a.n;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // per-wave scratch: lead, trail, mask, rlo, rhi [s]; qrow [D]; p [64]
-  const size_t per_wave = (size_t)5 * s * 4 + D * 4 + 64 * 4;
-  uint8_t *base = smem + wave * per_wave;
-  int32_t *lead = (int32_t *)base;
-  int32_t *trail = lead + s;
-  uint32_t *mask = (uint32_t *)(trail + s);
-  int32_t *rlo = (int32_t *)(mask + s);
+  // per-wave scratch: WaveTab; rlo, rhi [s]; qrow [D]; p [64]
+  uint8_t *base = smem + wave * valu_wave_bytes(s, D);
+  const WaveTab w = carve_wavetab(base, s);
+  const int32_t *lead = w.lead, *trail = w.trail;
+  const uint32_t *mask = w.mask;
+  int32_t *rlo = (int32_t *)(base + wavetab_bytes(s));
   int32_t *rhi = rlo + s;
   float *qrow = (float *)(rhi + s);
   float *pj = qrow + D;
@@ -217,8 +278,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
   const T *V = (const T *)a.v + ((int64_t)b * a.kv_heads + kvh) * n * D;
   T *O = (T *)a.out + ((int64_t)b * a.heads + h) * n * D;
 
-  wave_setup(a.params + 2 * (int64_t)h * s, s, n, r0, lane, lead, trail, mask);
-  wave_sync();
+  wave_setup(a.params + 2 * (int64_t)h * s, s, n, r0, lane, w);
 
   constexpr int E = D / 64;
   for (int t = 0; t < 32 && r0 + t < n; ++t) {
@@ -297,18 +357,44 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
 //     the accumulators (no cross-lane shuffle).
 // Output O = acc / l is written once, rounded to bf16.
 // ---------------------------------------------------------------------------
-constexpr int kStageKeys = 64;
+// K and V stream through a ring of kRing stages of 32 keys each, filled by
+// direct global->LDS loads issued kRing - 1 stages ahead.  Rows are stored
+// whole (D bf16) with their 16-byte chunks XOR-swizzled by the key's low bits
+// so that both the K-operand reads (one key per lane) and the transposing
+// V-operand reads spread over the LDS banks.
+constexpr int kTileKeys = 32;
+constexpr int kRing = 4;
 
 template <int D>
 struct MfmaLds {
-  static constexpr int kKStride = D + 8;            // bf16 per K row
-  static constexpr int kVStride = kStageKeys + 8;   // bf16 per V^T row
-  static constexpr int kHistStride = 20;            // dwords per histogram row
-  alignas(16) uint16_t K[kStageKeys * kKStride];
-  alignas(16) uint16_t Vt[D * kVStride];
-  alignas(16) uint32_t hist[4][32 * kHistStride];
-  int32_t range[4][2];
+  alignas(16) uint16_t kv[kRing][2][kTileKeys * D];
 };
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+// byte offset of 16-byte chunk c of row `key` inside a swizzled tile
+template <int D>
+__device__ __forceinline__ uint32_t swz(int key, int c) {
+  return (uint32_t)(key * D * 2 + ((c ^ (key & (D / 8 - 1))) << 4));
+}
+
+// Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 l (lds_base wave-uniform).  Issued as inline assembly so that
+// the ring's only ordering is the explicit vmcnt wait + barrier of each stage
+// (the compiler would otherwise wait for every outstanding copy before any
+// LDS read, since it cannot tell which ring stage a copy targets).
+__device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(m0)
+               : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt <= v and lgkmcnt == 0 (gfx9 encoding)
+#define PLSH_WAIT_VM_LGKM0(v) __builtin_amdgcn_s_waitcnt(((v) & 15) | (((v) >> 4) << 14) | (7 << 4))
 
 // key held by row a of the S^T accumulator block (see kernel comment)
 __device__ __forceinline__ int key_of_row(int a) {
@@ -330,20 +416,133 @@ __device__ __forceinline__ uint32_t prefix16(u32x4 &x) {
   return carry;  // total
 }
 
+// ---------------------------------------------------------------------------
+// Block-edge pre-pass: one record per (head, 32-row group), in a workspace.
+//   [0, 16)              int32 nnz, U0w, U1w, 0: number of samples with a block
+//                        start inside the group's rows; the group's key range
+//                        [U0w, U1w) (32-aligned)
+//   [16, +8 E)           (lead, mask) of every sample sorted by (lead, k), then
+//                        16 sentinels (0x7FFFFFFF, 0); E = s + 16 rounded up
+//                        to even, so that each list is whole 16-byte chunks
+//   [.., +8 E)           (trail, mask) sorted by (trail, k), 16 sentinels
+//                        (written by the non-causal pass only)
+//   [.., +1024)          multiplicity of the diagonal tile: byte [t][u] is
+//                        c(r0 + t, r0 + u), zero where j > i (causal) or j >= n
+// The fp64 block searches are latency-bound; as a kernel of their own they
+// run at high occupancy instead of stalling the MFMA kernel.
+// ---------------------------------------------------------------------------
+constexpr int kSentinels = 16;
+__host__ __device__ constexpr int ev_count(int s) { return (s + kSentinels + 1) & ~1; }
+__host__ __device__ constexpr size_t rec_evl_off() { return 16; }
+__host__ __device__ constexpr size_t rec_evt_off(int s) { return 16 + (size_t)8 * ev_count(s); }
+__host__ __device__ constexpr size_t rec_diag_off(int s) { return 16 + (size_t)16 * ev_count(s); }
+__host__ __device__ constexpr size_t rec_bytes(int s) { return rec_diag_off(s) + 1024; }
+constexpr int kMaxMfmaSamples = 124;
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) void edges_kernel(const double *params, int n, int heads, int s, int g32,
+                                                    uint8_t *ws) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = lane & 31, hh = lane >> 5;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= heads * g32) return;
+  const int h = item / g32, q = item % g32;
+  const int r0 = 32 * q;
+  uint8_t *wb = smem + wave * (wavetab_bytes(s) + 32 * 16 * 4);
+  const WaveTab w = carve_wavetab(wb, s);
+  uint32_t *hist = (uint32_t *)(wb + wavetab_bytes(s));  // [32 rows][16 dwords]: up 0..7, down 8..15
+  for (int i = lane; i < 32 * 16; i += 64) hist[i] = 0u;
+  const int nact = wave_ends(params + 2 * (int64_t)h * s, s, n, r0, lane, w);
+  wave_sync();
+  wave_masks(n, r0, lane, nact, w);
+  wave_sync();
+  uint8_t *rec = ws + (size_t)item * rec_bytes(s);
+  u32x2 *evl = (u32x2 *)(rec + rec_evl_off());
+  u32x2 *evt = (u32x2 *)(rec + rec_evt_off(s));
+  int mn = INT32_MAX, mx = INT32_MIN;
+  for (int k = lane; k < s; k += 64) {
+    const int32_t lk = w.lead[k], tk = w.trail[k];
+    const uint32_t mk = w.mask[k];
+    mn = min(mn, lk);
+    mx = max(mx, tk);
+    int rl = 0, rt = 0;
+#pragma unroll 4
+    for (int k2 = 0; k2 < s; ++k2) {
+      const int32_t l2 = w.lead[k2], t2 = w.trail[k2];
+      rl += (l2 < lk) | ((l2 == lk) & (k2 < k));
+      rt += (t2 < tk) | ((t2 == tk) & (k2 < k));
+    }
+    evl[rl] = u32x2{(uint32_t)lk, mk};
+    if (!CAUSAL) evt[rt] = u32x2{(uint32_t)tk, mk};
+  }
+  if (lane < kSentinels) {
+    evl[s + lane] = u32x2{0x7FFFFFFFu, 0u};
+    if (!CAUSAL) evt[s + lane] = u32x2{0x7FFFFFFFu, 0u};
+  }
+  const int U0w = wave_min_i(mn) & ~31;
+  const int U1w = CAUSAL ? r0 + 32 : ((wave_max_i(mx) + 31) & ~31);
+  if (lane == 0) *(int4 *)rec = make_int4(nact, U0w, U1w, 0);
+
+  // diagonal tile: row t's block starts inside the rows (highest mask bit <= t)
+  // and, non-causal, its block ends inside them (lowest bit > t), as per-row
+  // byte histograms; prefix sums give the counts
+  const uint32_t low_t = bits_1_to(t), high_t = ~((2u << t) - 1u);
+  uint32_t *hup = hist + 16 * t, *hdn = hup + 8;
+  for (int z = 0; z < nact; ++z) {
+    const uint32_t mk = w.mask[w.act[z]];
+    const uint32_t ml = mk & low_t;
+    if (ml) {
+      const int rel = 31 - __builtin_clz(ml);
+      if ((rel >> 4) == hh) atomicAdd(&hup[rel >> 2], 1u << (8 * (rel & 3)));
+    }
+    if (!CAUSAL) {
+      const uint32_t mh = mk & high_t;
+      if (mh) {
+        const int rel = __builtin_ctz(mh);
+        if ((rel >> 4) == hh) atomicAdd(&hdn[rel >> 2], 1u << (8 * (rel & 3)));
+      }
+    }
+  }
+  wave_sync();
+  u32x4 hu = *(const u32x4 *)(hup + 4 * hh);
+  const uint32_t tu = prefix16(hu);
+  const uint32_t ou = other_half(tu, lane);
+  // samples whose block of row t starts at or before r0 count for every key
+  const uint32_t before = (uint32_t)s - tu - ou;
+  u32x4 c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = hu[i] + (before + (hh ? ou : 0u)) * 0x01010101u;
+  if (!CAUSAL) {
+    u32x4 hd = *(const u32x4 *)(hdn + 4 * hh);
+    const uint32_t td = prefix16(hd);
+    const uint32_t od = other_half(td, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] -= hd[i] + (hh ? od : 0u) * 0x01010101u;
+  }
+  const int last = min(r0 + 31, n - 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int u = 16 * hh + 4 * i + r;
+      if ((CAUSAL && u > t) || r0 + u > last) c[i] &= ~(0xFFu << (8 * r));
+    }
+  *(u32x4 *)(rec + rec_diag_off(s) + 32 * t + 16 * hh) = c;
+}
+
+__host__ __device__ constexpr size_t ev_wave_bytes(int s, bool causal) {
+  return (size_t)(causal ? 8 : 16) * ev_count(s);
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   using L = MfmaLds<D>;
   __shared__ __attribute__((aligned(16))) L lds;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int s = a.s, n = a.n;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t = lane & 31, hh = lane >> 5;
-  int32_t *lead = (int32_t *)dyn + wave * 6 * s;
-  int32_t *trail = lead + s;
-  uint32_t *mask = (uint32_t *)(trail + s);
-  int32_t *lord = (int32_t *)(mask + s);   // samples sorted by lead
-  int32_t *tord = lord + s;                // samples sorted by trail
-  int32_t *nzl = tord + s;                 // samples with a block edge inside the wave
 
   // ---- workgroup -> (head, batch, row tile): heavy heads first; on each of
   // the 8 XCDs (workgroups are dealt round-robin) a contiguous run of row
@@ -367,61 +566,18 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   const int kvh = h / (a.heads / a.kv_heads);
   const int r0 = g * 128 + wave * 32;
   const bool active = r0 < n;
+  const int g32 = (n + 31) / 32;
+  const size_t rb = rec_bytes(s);
+  const uint8_t *rec_wg = ws + ((size_t)h * g32 + 4 * g) * rb;
 
   const uint16_t *Q = (const uint16_t *)a.q + ((int64_t)b * a.heads + h) * n * D;
   const uint16_t *K = (const uint16_t *)a.k + ((int64_t)b * a.kv_heads + kvh) * n * D;
   const uint16_t *V = (const uint16_t *)a.v + ((int64_t)b * a.kv_heads + kvh) * n * D;
   uint16_t *O = (uint16_t *)a.out + ((int64_t)b * a.heads + h) * n * D;
 
-  // ---- a3: per-wave block intervals
-  int U0w = INT32_MAX, U1w = INT32_MIN, nnz = 0;
-  if (active) {
-    wave_setup(a.params + 2 * (int64_t)h * s, s, n, r0, lane, lead, trail, mask);
-    wave_sync();
-    int mn = INT32_MAX, mx = INT32_MIN;
-    for (int k = lane; k < s; k += 64) {
-      mn = min(mn, lead[k]);
-      mx = max(mx, trail[k]);
-      // rank by (lead, k) and (trail, k)
-      const int32_t lk = lead[k], tk = trail[k];
-      int rl = 0, rt = 0;
-      for (int k2 = 0; k2 < s; ++k2) {
-        const int32_t l2 = lead[k2], t2 = trail[k2];
-        rl += (l2 < lk) | ((l2 == lk) & (k2 < k));
-        rt += (t2 < tk) | ((t2 == tk) & (k2 < k));
-      }
-      lord[rl] = k;
-      tord[rt] = k;
-    }
-    // compact list of samples with a block edge inside the wave's rows
-    for (int k0 = 0; k0 < s; k0 += 64) {
-      const int k = k0 + lane;
-      const bool nz = k < s && mask[k] != 0u;
-      const uint64_t bal = __ballot(nz);
-      if (nz) nzl[nnz + __popcll(bal & ((1ull << lane) - 1ull))] = k;
-      nnz += __popcll(bal);
-    }
-    U0w = wave_min_i(mn) & ~31;
-    U1w = CAUSAL ? r0 + 32 : ((wave_max_i(mx) + 31) & ~31);
-    wave_sync();
-  }
-  if (lane == 0) {
-    lds.range[wave][0] = U0w;
-    lds.range[wave][1] = U1w;
-  }
-  // zero this wave's histogram rows
-  for (int w = lane; w < 32 * L::kHistStride; w += 64) lds.hist[wave][w] = 0u;
-  __syncthreads();
-  int U0 = INT32_MAX, U1 = INT32_MIN;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    U0 = min(U0, lds.range[w][0]);
-    U1 = max(U1, lds.range[w][1]);
-  }
-  U0 &= ~(kStageKeys - 1);
-  const int nst = (U1 > U0) ? (U1 - U0 + kStageKeys - 1) / kStageKeys : 0;
-
-  // ---- Q fragment (B operand of S^T = K Q^T): query r0 + t, dims 16c + 8hh + e
+  // ---- loads that need nothing: Q fragment (B operand of S^T = K Q^T:
+  // query r0 + t, dims 16c + 8hh + e), the wave's edge record into
+  // lane-indexed registers, and the four groups' key ranges.
   constexpr int NC = D / 16;
   bf16x8 qf[NC];
   {
@@ -433,7 +589,61 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
       qf[c] = __builtin_bit_cast(bf16x8, raw);
     }
   }
+  // this row's 16 bytes of the diagonal-tile multiplicity table
+  u32x4 dg = {0u, 0u, 0u, 0u};
+  if (active) dg = *(const u32x4 *)(rec_wg + (size_t)wave * rb + rec_diag_off(s) + 32 * t + 16 * hh);
+  int U0 = INT32_MAX, U1 = INT32_MIN, U0w = INT32_MAX, U1w = INT32_MIN;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (g * 128 + 32 * w < n) {
+      const int4 hdr = *(const int4 *)(rec_wg + (size_t)w * rb);
+      U0 = min(U0, hdr.y);
+      U1 = max(U1, hdr.z);
+      if (w == wave) { U0w = hdr.y; U1w = hdr.z; }
+    }
+  }
+  // stage st covers keys [U0 + 32 st, U0 + 32 st + 32)
+  const int nst = (U1 > U0) ? (U1 - U0) / kTileKeys : 0;
+  // everything loaded so far is needed before the first tile; later waits
+  // count only the asynchronous LDS copies issued below
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
 
+  // the wave's sorted edge lists, copied into its LDS slice (16 bytes = two
+  // edges per lane and instruction)
+  const int nch = ev_count(s) / 2;  // 16-byte chunks per list
+  u32x2 *evl = (u32x2 *)(dyn + (size_t)wave * ev_wave_bytes(s, CAUSAL));
+  u32x2 *evt = evl + ev_count(s);
+  if (active) {
+    const uint8_t *rec = rec_wg + (size_t)wave * rb;
+    for (int c0 = 0; c0 < nch; c0 += 64)
+      if (c0 + lane < nch) dma16(rec + rec_evl_off() + 16 * (c0 + lane), evl + 2 * c0);
+    if (!CAUSAL)
+      for (int c0 = 0; c0 < nch; c0 += 64)
+        if (c0 + lane < nch) dma16(rec + rec_evt_off(s) + 16 * (c0 + lane), evt + 2 * c0);
+  }
+
+  // ---- K/V staging: wave w copies chunks [w D, (w + 1) D) of each tile
+  // (a tile is 32 rows of D / 8 chunks); keys past the end read row n - 1,
+  // whose products are multiplied by c = 0.
+  constexpr int CPR = D / 8;           // chunks per row
+  constexpr int LPS = 2 * (D / 64);    // loads per thread per stage (K and V)
+  const char *Kb = (const char *)K, *Vb = (const char *)V;
+  auto issue_stage = [&](int st) {
+    const int q = st % kRing;
+    const int jt = U0 + kTileKeys * st;
+#pragma unroll
+    for (int ins = 0; ins < D / 64; ++ins) {
+      const int slot = wave * D + 64 * ins + lane;
+      const int key = slot / CPR, pos = slot % CPR;
+      const int c = pos ^ (key & (CPR - 1));
+      const int64_t off = ((int64_t)min(jt + key, n - 1) * D + 8 * c) * 2;
+      dma16(Kb + off, lds.kv[q][0] + (wave * D + 64 * ins) * 8);
+      dma16(Vb + off, lds.kv[q][1] + (wave * D + 64 * ins) * 8);
+    }
+  };
+#pragma unroll
+  for (int pst = 0; pst < kRing - 1; ++pst)
+    if (pst < nst) issue_stage(pst);
   // ---- running state
   constexpr int NDB = D / 32;
   floatx16 oacc[NDB];
@@ -443,169 +653,131 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m2 = -INFINITY;  // running max, log2 units
   float lsum = 0.f;      // this lane's share of the row sum
-  int base_up = 0, base_dn = 0, lp = 0, tp = 0;
+  int base = 0, lp = 0, tp = 0;  // running multiplicity of the row before the tile; edge pointers
   const uint32_t low_t = bits_1_to(t);
   const uint32_t high_t = ~((2u << t) - 1u);
   const int arow_key = key_of_row(lane & 31);
-
-  // ---- K/V staging (register prefetch of the next stage)
-  constexpr int KCH = kStageKeys * D / 8 / 256;   // 16-byte K chunks per thread
-  constexpr int VIT = kStageKeys / 2 * D / 8 / 256;  // key-pair items per thread
-  u32x4 kreg[KCH], vreg[VIT][2];
-  auto load_stage = [&](int st) {
-    const int kb = U0 + st * kStageKeys;
-#pragma unroll
-    for (int it = 0; it < KCH; ++it) {
-      const int id = tid + 256 * it;
-      const int key = id / (D / 8), part = id % (D / 8);
-      const int j = kb + key;
-      kreg[it] = (j >= 0 && j < n) ? *(const u32x4 *)(K + (int64_t)j * D + 8 * part)
-                                   : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int id = tid + 256 * it;
-      const int kp = id % (kStageKeys / 2), part = id / (kStageKeys / 2);
-      const int j = kb + 2 * kp;
-      vreg[it][0] = (j >= 0 && j < n) ? *(const u32x4 *)(V + (int64_t)j * D + 8 * part)
-                                      : u32x4{0u, 0u, 0u, 0u};
-      vreg[it][1] = (j + 1 >= 0 && j + 1 < n) ? *(const u32x4 *)(V + (int64_t)(j + 1) * D + 8 * part)
-                                              : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_stage = [&]() {
-#pragma unroll
-    for (int it = 0; it < KCH; ++it) {
-      const int id = tid + 256 * it;
-      const int key = id / (D / 8), part = id % (D / 8);
-      *(u32x4 *)(lds.K + key * L::kKStride + 8 * part) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int id = tid + 256 * it;
-      const int kp = id % (kStageKeys / 2), part = id / (kStageKeys / 2);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x = vreg[it][0][w], y = vreg[it][1][w];
-        const int dim = 8 * part + 2 * w;
-        *(uint32_t *)(lds.Vt + dim * L::kVStride + 2 * kp) = (x & 0xFFFFu) | (y << 16);
-        *(uint32_t *)(lds.Vt + (dim + 1) * L::kVStride + 2 * kp) = (x >> 16) | (y & 0xFFFF0000u);
-      }
-    }
-  };
-
-  if (nst > 0) load_stage(0);
-  uint32_t *hrow = &lds.hist[wave][t * L::kHistStride];
+  // V-operand rows for v_ds_read_b64_tr_b16: in each group of 16 lanes, lane
+  // r names row (key kb + r / 4, dims dbase + 4 (r % 4) .. + 3); lane i then
+  // receives V^T[dbase + i][kb .. kb + 3].
+  const int vg = lane >> 4, vr = lane & 15;
 
   for (int st = 0; st < nst; ++st) {
-    __syncthreads();
-    store_stage();
-    if (st + 1 < nst) load_stage(st + 1);
-    __syncthreads();
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int j0 = U0 + st * kStageKeys + 32 * tt;
+    // this thread's loads of stage st are done once at most those of the
+    // (up to two) later stages already issued are outstanding
+    const int ahead = min(kRing - 2, nst - 1 - st);
+    if (ahead >= 2) PLSH_WAIT_VM_LGKM0(2 * LPS);
+    else if (ahead == 1) PLSH_WAIT_VM_LGKM0(LPS);
+    else PLSH_WAIT_VM_LGKM0(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // every wave's loads of stage st landed; stage st - 1 is consumed
+    asm volatile("" ::: "memory");
+    if (st + kRing - 1 < nst) issue_stage(st + kRing - 1);
+    {
+      const int j0 = U0 + kTileKeys * st;
       if (!active || j0 < U0w || j0 >= U1w) continue;
+      const char *kt = (const char *)lds.kv[st % kRing][0];
+      const char *vt = (const char *)lds.kv[st % kRing][1];
 
       // a5: S^T = K Q^T
       floatx16 sacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-      const uint16_t *krow = lds.K + (32 * tt + arow_key) * L::kKStride + 8 * hh;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4 *)(krow + 16 * c));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kt + swz<D>(arow_key, 2 * c + hh)));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], sacc, 0, 0, 0);
       }
 
-      // a4: multiplicity c for keys j0 + 16 hh + r
+      // a4: multiplicity c for keys j0 + 16 hh + r.
+      //  * diagonal tile: the row's bytes of the precomputed table;
+      //  * a tile holding sample edges at wave-uniform positions (lower ends
+      //    = leads, upper ends = trails): c = base + sum_e w_e(row) [pos_e <=
+      //    key] evaluated as one 32x32x16 bf16 MFMA per 15 edges, the A operand
+      //    being the key indicators and the B operand the row weights; the
+      //    16th slot carries the row's running count;
+      //  * otherwise c = base for all 16 keys.
       const bool diag = (j0 == r0);
-      const int jend = j0 + 32;
-      const bool up_in = (lp < s) && (lead[lord[lp]] < jend);
-      const bool dn_in = !CAUSAL && (tp < s) && (trail[tord[tp]] < jend);
+      const int jend = j0 + kTileKeys;
+      const bool up_in = (int32_t)evl[lp][0] < jend;
+      const bool dn_in = !CAUSAL && (int32_t)evt[tp][0] < jend;
       float cf[16];
-      if (!diag && !up_in && !dn_in) {
-        const float cu = (float)(base_up - base_dn);
+      bool uni = false;
+      if (diag) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cf[r] = cu;
-      } else {
-        uint32_t *hup = hrow;
-        uint32_t *hdn = hrow + 8;
-        while (lp < s) {
-          const int k = lord[lp];
-          const int32_t pos = lead[k];
-          if (pos >= jend) break;
-          const int rel = pos - j0;
-          if ((mask[k] & low_t) == 0u && (rel >> 4) == hh)
-            atomicAdd(&hup[rel >> 2], 1u << (8 * (rel & 3)));
-          ++lp;
+        for (int r = 0; r < 16; ++r) cf[r] = (float)((dg[r >> 2] >> (8 * (r & 3))) & 0xFFu);
+        // the table already counts every edge at or before the tile's end
+        while ((int32_t)evl[lp][0] < jend) ++lp;
+        if (!CAUSAL) {
+          while ((int32_t)evt[tp][0] < jend) ++tp;
+          base = (int)(other_half((dg[3] >> 24) & 0xFFu, lane) * (uint32_t)(hh == 0) +
+                       ((dg[3] >> 24) & 0xFFu) * (uint32_t)(hh == 1));
         }
-        if (diag) {
-          for (int z = 0; z < nnz; ++z) {
-            const uint32_t mk = mask[nzl[z]];
-            const uint32_t ml = mk & low_t;
-            if (ml) {
-              const int rel = 31 - __builtin_clz(ml);
-              if ((rel >> 4) == hh) atomicAdd(&hup[rel >> 2], 1u << (8 * (rel & 3)));
-            }
-            if (!CAUSAL) {
-              const uint32_t mh = mk & high_t;
-              if (mh) {
-                const int rel = __builtin_ctz(mh);
-                if ((rel >> 4) == hh) atomicAdd(&hdn[rel >> 2], 1u << (8 * (rel & 3)));
+      } else if (up_in || dn_in) {
+        floatx16 cacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cacc[r] = 0.f;
+        const int akey = j0 + arow_key;
+        bool base_in = false;
+#pragma unroll
+        for (int list = 0; list < (CAUSAL ? 1 : 2); ++list) {
+          const u32x2 *ev = list ? evt : evl;
+          int &ptr = list ? tp : lp;
+          const uint32_t wmask = list ? high_t : low_t;
+          const uint32_t one = list ? 0xBF80u : 0x3F80u;  // bf16 -1 / +1
+          while ((int32_t)ev[ptr][0] < jend) {
+            u32x4 aw, bw;
+            int nin = 0, wsum = 0;
+#pragma unroll
+            for (int m2i = 0; m2i < 4; ++m2i) {
+              uint32_t av2 = 0u, bv2 = 0u;
+#pragma unroll
+              for (int half = 0; half < 2; ++half) {
+                const int slot = 8 * hh + 2 * m2i + half;
+                const u32x2 e = ev[ptr + slot];
+                const bool in = slot < 15 && (int32_t)e[0] < jend;
+                const bool on = in && (e[1] & wmask) == 0u;
+                uint32_t a16 = ((int32_t)e[0] <= akey && slot < 15) ? 0x3F80u : 0u;
+                uint32_t b16 = on ? one : 0u;
+                if (slot == 15) {
+                  a16 = 0x3F80u;
+                  b16 = base_in ? 0u : f32_to_bf16_bits((float)base);
+                }
+                av2 |= a16 << (16 * half);
+                bv2 |= b16 << (16 * half);
+                nin += in;
+                wsum += on;
               }
+              aw[m2i] = av2;
+              bw[m2i] = bv2;
             }
+            cacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw),
+                                                           __builtin_bit_cast(bf16x8, bw), cacc, 0, 0, 0);
+            base_in = true;
+            nin += (int)other_half((uint32_t)nin, lane);
+            wsum += (int)other_half((uint32_t)wsum, lane);
+            ptr += nin;
+            base += list ? -wsum : wsum;
+            if (nin < 15) break;
           }
         }
-        if (!CAUSAL) {
-          while (tp < s) {
-            const int k = tord[tp];
-            const int32_t pos = trail[k];
-            if (pos >= jend) break;
-            const int rel = pos - j0;
-            if ((mask[k] & high_t) == 0u && (rel >> 4) == hh)
-              atomicAdd(&hdn[rel >> 2], 1u << (8 * (rel & 3)));
-            ++tp;
-          }
-        }
-        wave_sync();
-        u32x4 up = *(const u32x4 *)(hup + 4 * hh);
-        const uint32_t tot_up = prefix16(up);
-        const uint32_t oth_up = other_half(tot_up, lane);
-        const uint32_t add_up = (uint32_t)base_up + (hh ? oth_up : 0u);
-        base_up += (int)(tot_up + oth_up);
-        u32x4 cnt;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) cnt[w] = up[w] + add_up * 0x01010101u;
-        if (!CAUSAL) {
-          u32x4 dn = *(const u32x4 *)(hdn + 4 * hh);
-          const uint32_t tot_dn = prefix16(dn);
-          const uint32_t oth_dn = other_half(tot_dn, lane);
-          const uint32_t add_dn = (uint32_t)base_dn + (hh ? oth_dn : 0u);
-          base_dn += (int)(tot_dn + oth_dn);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) cnt[w] -= dn[w] + add_dn * 0x01010101u;
-          *(u32x4 *)(hdn + 4 * hh) = u32x4{0u, 0u, 0u, 0u};
-        }
-        *(u32x4 *)(hup + 4 * hh) = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cf[r] = (float)((cnt[r >> 2] >> (8 * (r & 3))) & 0xFFu);
-        if (CAUSAL && diag) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (16 * hh + r > t) cf[r] = 0.f;
-        }
-        wave_sync();
+        for (int r = 0; r < 16; ++r) cf[r] = cacc[r];
+      } else {
+        uni = true;
+        cf[0] = (float)base;  // one count for the lane's 16 keys
       }
 
-      // a6: weighted online softmax (log2 domain, lazily raised max)
-      float mx = -INFINITY;
+      // a6: weighted online softmax in the log2 domain.  The running max is
+      // raised only when a logit exceeds it by more than 2^8 (the result does
+      // not depend on the max used, and a rescale of the accumulators is then
+      // rare).  A tile with one count per row folds log2(c) into the exponent
+      // bias; otherwise P = c * 2^(...).  P is rounded to bf16 in pairs and the
+      // row sum adds exactly the rounded weights that enter PV.
+      float mx = sacc[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[r] *= kLog2e;
-        mx = fmaxf(mx, sacc[r]);
-      }
-      mx = fmaxf(mx, other_half_f(mx, lane));
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      mx = fmaxf(mx, other_half_f(mx, lane)) * kLog2e;
       const bool need = mx > m2 + 8.0f;
       if (__any(need)) {
         const float mnew = need ? mx : m2;
@@ -617,22 +789,47 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         m2 = mnew;
       }
-      bf16x8 pk[2];
+      u32x4 pw[2];
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      if (uni) {
+        const float bias = m2 - __builtin_amdgcn_logf(cf[0]);  // c = 0 gives bias = +inf, P = 0
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const __bf16 pb = (__bf16)(cf[r] * __builtin_amdgcn_exp2f(sacc[r] - m2));
-        pk[r >> 3][r & 7] = pb;
-        lsum += (float)pb;  // the row sum uses the same rounded weights as PV
+        for (int r = 0; r < 16; r += 2) {
+          const floatx2 pf = {__builtin_amdgcn_exp2f(fmaf(sacc[r], kLog2e, -bias)),
+                              __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], kLog2e, -bias))};
+          const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+          pw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const floatx2 pf = {cf[r] * __builtin_amdgcn_exp2f(fmaf(sacc[r], kLog2e, -m2)),
+                              cf[r + 1] * __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], kLog2e, -m2))};
+          const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+          pw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
+        }
       }
+      const bf16x8 pk[2] = {__builtin_bit_cast(bf16x8, pw[0]), __builtin_bit_cast(bf16x8, pw[1])};
 
-      // a7: O^T += V^T P^T
+      // a7: O^T += V^T P^T; A operand rows: dims 32 db + 16 (vg % 2) + i, keys
+      // 16 (vg / 2) + 8 cc + (0..7), read transposed from row-major V
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const uint16_t *vp = lds.Vt + (32 * db + (lane & 31)) * L::kVStride + 32 * tt + 16 * hh + 8 * cc;
-          const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4 *)vp);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[cc], oacc[db], 0, 0, 0);
+          const int key = 16 * (vg >> 1) + 8 * cc + (vr >> 2);
+          const int dim = 32 * db + 16 * (vg & 1) + 4 * (vr & 3);
+          const uint32_t o1 = swz<D>(key, dim >> 3) + ((dim & 4) << 1);
+          const uint32_t o2 = swz<D>(key + 4, dim >> 3) + ((dim & 4) << 1);
+          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(vt + o1));
+          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(vt + o2));
+          const u32x4 w4 = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4), pk[cc], oacc[db], 0, 0, 0);
         }
       }
     }
@@ -743,8 +940,7 @@ plsh_status have_device(const char *who) {
 
 plsh_status launch_valu(const dev::AttnArgs &a, int d, plsh_dtype dtype, int causal, hipStream_t st,
                         const char *who) {
-  const size_t per_wave = (size_t)5 * a.s * 4 + d * 4 + 64 * 4;
-  const size_t shm = 4 * per_wave;
+  const size_t shm = 4 * dev::valu_wave_bytes(a.s, d);
   const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(256);
   if (dtype == PLSH_F32) {
     if (d == 64) hipLaunchKernelGGL((dev::attn_valu_kernel<float, 64>), grid, block, shm, st, a, causal);
@@ -757,16 +953,40 @@ plsh_status launch_valu(const dev::AttnArgs &a, int d, plsh_dtype dtype, int cau
 }
 
 plsh_status launch_mfma(const dev::AttnArgs &a, int d, int causal, hipStream_t st, const char *who) {
-  const size_t shm = (size_t)4 * 6 * a.s * 4;
-  const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(256);
-  if (d == 64) {
-    if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<64, true>), grid, block, shm, st, a);
-    else hipLaunchKernelGGL((dev::attn_mfma_kernel<64, false>), grid, block, shm, st, a);
-  } else {
-    if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<128, true>), grid, block, shm, st, a);
-    else hipLaunchKernelGGL((dev::attn_mfma_kernel<128, false>), grid, block, shm, st, a);
+  const int g32 = (a.n + 31) / 32;
+  const size_t ws_bytes = (size_t)a.heads * g32 * dev::rec_bytes(a.s);
+  void *ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, ws_bytes, st);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PLSH_ERR_HIP, "%s: workspace allocation of %zu bytes failed: %s", who, ws_bytes,
+                hipGetErrorString(e));
   }
-  return launch_check(who);
+  const int items = a.heads * g32;
+  const dim3 egrid((unsigned)((items + 3) / 4)), eblock(256);
+  const size_t eshm = 4 * (dev::wavetab_bytes(a.s) + 32 * 16 * 4);
+  if (causal) hipLaunchKernelGGL(dev::edges_kernel<true>, egrid, eblock, eshm, st, a.params, a.n, a.heads, a.s, g32, (uint8_t *)ws);
+  else hipLaunchKernelGGL(dev::edges_kernel<false>, egrid, eblock, eshm, st, a.params, a.n, a.heads, a.s, g32, (uint8_t *)ws);
+  plsh_status rc = launch_check(who);
+  if (rc == PLSH_OK) {
+    const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(256);
+    const uint8_t *w8 = (const uint8_t *)ws;
+    const size_t shm = 4 * dev::ev_wave_bytes(a.s, causal != 0);
+    if (d == 64) {
+      if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<64, true>), grid, block, shm, st, a, w8);
+      else hipLaunchKernelGGL((dev::attn_mfma_kernel<64, false>), grid, block, shm, st, a, w8);
+    } else {
+      if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<128, true>), grid, block, shm, st, a, w8);
+      else hipLaunchKernelGGL((dev::attn_mfma_kernel<128, false>), grid, block, shm, st, a, w8);
+    }
+    rc = launch_check(who);
+  }
+  e = hipFreeAsync(ws, st);
+  if (e != hipSuccess && rc == PLSH_OK) {
+    (void)hipGetLastError();
+    return fail(PLSH_ERR_HIP, "%s: workspace release failed: %s", who, hipGetErrorString(e));
+  }
+  return rc;
 }
 
 }  // namespace
@@ -786,7 +1006,7 @@ extern "C" plsh_status plsh_alibi_attention(const void *q, const void *k, const 
   if ((st = have_device(who)) != PLSH_OK) return st;
   dev::AttnArgs a;
   fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
-  if (dtype == PLSH_BF16) return launch_mfma(a, d, causal != 0, (hipStream_t)stream, who);
+  if (dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples) return launch_mfma(a, d, causal != 0, (hipStream_t)stream, who);
   return launch_valu(a, d, dtype, causal != 0, (hipStream_t)stream, who);
 }
 
@@ -816,7 +1036,7 @@ extern "C" plsh_status plsh_debug_block_intervals(const plsh_tables *bt, int32_t
   plsh_status st = have_device(who);
   if (st != PLSH_OK) return st;
   const int groups = (bt->n + 31) / 32;
-  const size_t shm = (size_t)3 * bt->s * 4;
+  const size_t shm = dev::wavetab_bytes(bt->s);
   hipLaunchKernelGGL(dev::debug_intervals_kernel, dim3((unsigned)((int64_t)groups * bt->heads)), dim3(64), shm,
                      (hipStream_t)stream, bt->params, bt->n, bt->heads, bt->s, groups, lohi);
   return launch_check(who);

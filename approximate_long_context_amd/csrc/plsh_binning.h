@@ -32,12 +32,15 @@ PLSH_HD double bin_of(int32_t x, double delta, double u) {
 // bin(y) == bin(x) == b.  The arithmetic guess is settled with the exact
 // predicate, so the answer never depends on how the guess was rounded; a
 // bisection (bin is non-decreasing) finishes any case the local steps do not.
+// Both probes of a step are independent, so their divisions overlap.
 PLSH_HD int32_t block_lo(int32_t x, double delta, double u, double b) {
   double c = ceil(b * delta - u);
   int32_t y = (c <= 0.0) ? 0 : (c >= (double)x ? x : (int32_t)c);
   for (int it = 0; it < 4; ++it) {
-    if (y > 0 && bin_of(y - 1, delta, u) >= b) { --y; continue; }
-    if (bin_of(y, delta, u) < b) { ++y; continue; }
+    const double bl = bin_of(y > 0 ? y - 1 : 0, delta, u);
+    const double by = bin_of(y, delta, u);
+    if (y > 0 && bl >= b) { --y; continue; }
+    if (by < b) { ++y; continue; }
     return y;
   }
   int32_t lo = 0, hi = x;  // bin(x) == b, so the answer lies in [0, x]
@@ -54,8 +57,10 @@ PLSH_HD int32_t block_hi(int32_t x, int32_t n, double delta, double u, double b)
   double c = ceil((b + 1.0) * delta - u);
   int32_t y = (c <= (double)(x + 1)) ? x + 1 : (c >= (double)n ? n : (int32_t)c);
   for (int it = 0; it < 4; ++it) {
-    if (y > x + 1 && bin_of(y - 1, delta, u) > b) { --y; continue; }
-    if (y < n && bin_of(y, delta, u) <= b) { ++y; continue; }
+    const double bl = bin_of(y - 1, delta, u);
+    const double by = bin_of(y, delta, u);
+    if (y > x + 1 && bl > b) { --y; continue; }
+    if (y < n && by <= b) { ++y; continue; }
     return y;
   }
   int32_t lo = x + 1, hi = n;

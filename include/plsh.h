@@ -23,7 +23,12 @@
  *   - Host pointers are read during the call only; the library keeps no
  *     reference to any caller buffer after it returns (device work enqueued on
  *     `stream` reads device buffers until it completes: they must stay alive
- *     until then).  The library allocates no device memory.
+ *     until then).
+ *   - Device memory: plsh_alibi_attention on the bf16 path takes a workspace
+ *     of heads * ceil(n/32) * (1040 + 16 * E) bytes, E = s + 16 rounded up to
+ *     even, from the stream-ordered allocator (hipMallocAsync on `stream`) and
+ *     releases it on the same stream (hipFreeAsync) within the call; no other
+ *     entry point allocates device memory.
  *   - The library keeps no state besides a thread-local error string.
  */
 #ifndef PLSH_H
@@ -137,12 +142,17 @@ plsh_status plsh_count_work(const plsh_tables *host_tables, int32_t causal,
  *               binary64 predicate); offsets/starts are not read and may be
  *               NULL.  n/heads/s must match the call.
  *   causal      0 or 1
- *   stream      HIP stream for the launch
+ *   stream      HIP stream for the launches
+ * Kernels: bf16 with s <= 124 runs a block-edge pre-pass (per head and
+ * 32-row group: sorted block ends and the diagonal tile's multiplicities,
+ * into the workspace) and then the MFMA attention kernel; fp32, or s > 124,
+ * runs the one-row-per-wave VALU kernel (no workspace).
  * Buffers must be 16-byte aligned; out must not overlap q, k or v.
  * Errors: PLSH_ERR_ARG (null pointer, n < 1, batch < 1, heads or kv_heads < 1,
  * heads % kv_heads != 0, s < 1, sigma not finite or <= 0, aliasing),
  * PLSH_ERR_TABLE (boundaries mismatch), PLSH_ERR_UNSUPPORTED (d not 64/128,
- * batch*heads*n*d >= 2^31, s > 255), PLSH_ERR_HIP (launch error).  Execution
+ * batch*heads*n*d >= 2^31, s > 255), PLSH_ERR_HIP (launch error, workspace
+ * allocation failure).  Execution
  * faults surface at the caller's next synchronisation.
  */
 plsh_status plsh_alibi_attention(const void *q, const void *k, const void *v, void *out,

@@ -158,7 +158,7 @@ def test_bf16_small_n_edges(dev, n, causal):
     check_bf16(o, ref, what=w.name)
 
 
-@pytest.mark.parametrize("s", [1, 2, 255])
+@pytest.mark.parametrize("s", [1, 2, 60, 61, 124, 125, 255])
 def test_bf16_sample_count_edges(dev, s):
     w = small(f"edge-s{s}", 1, 3, 3, 700, 64, "bf16", True, [1.5, 12.0, 90.0], s)
     o, ref, _ = run_case(dev, w)
