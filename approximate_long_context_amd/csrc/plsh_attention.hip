@@ -359,9 +359,16 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
 // ---------------------------------------------------------------------------
 // K and V stream through a ring of kRing stages of 32 keys each, filled by
 // direct global->LDS loads issued kRing - 1 stages ahead.  Rows are stored
-// whole (D bf16) with their 16-byte chunks XOR-swizzled by the key's low bits
-// so that both the K-operand reads (one key per lane) and the transposing
-// V-operand reads spread over the LDS banks.
+// whole (D bf16) with their 16-byte chunks XOR-swizzled by swz_key<D>(key) so
+// that both operand reads are free of bank conflicts.  The LDS has 64 banks
+// of 4 bytes, so 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read,
+// must cover 256 distinct bytes modulo 256:
+//   K operand (16-byte reads): lanes 16m .. 16m + 15 read keys
+//     {0..7, 16..23} + 8m at one chunk: swz_key separates key bits 0, 1, 2, 4;
+//   V operand (8-byte transposing reads): 32 lanes read chunks 4j .. 4j + 3
+//     of 4 consecutive keys: swz_key moves those keys to distinct aligned
+//     groups of 4 chunks (D = 128: bits 2, 3 from key bits 0, 1; D = 64: the
+//     row parity is the 128-byte half, bit 2 from key bit 1).
 constexpr int kTileKeys = 32;
 constexpr int kRing = 4;
 
@@ -374,10 +381,16 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
+template <int D>
+__device__ __forceinline__ int swz_key(int key) {
+  const int g = ((key >> 2) & 1) | (((key >> 4) & 1) << 1);
+  return D == 128 ? (((key & 3) << 2) | g) : ((((key >> 1) & 1) << 2) | g);
+}
+
 // byte offset of 16-byte chunk c of row `key` inside a swizzled tile
 template <int D>
 __device__ __forceinline__ uint32_t swz(int key, int c) {
-  return (uint32_t)(key * D * 2 + ((c ^ (key & (D / 8 - 1))) << 4));
+  return (uint32_t)(key * D * 2 + ((c ^ swz_key<D>(key)) << 4));
 }
 
 // Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at
@@ -541,7 +554,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
   __shared__ __attribute__((aligned(16))) L lds;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int s = a.s, n = a.n;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is wave-uniform; saying so keeps all per-wave control flow
+  // on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int t = lane & 31, hh = lane >> 5;
 
   // ---- workgroup -> (head, batch, row tile): heavy heads first; on each of
@@ -635,12 +650,14 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
     for (int ins = 0; ins < D / 64; ++ins) {
       const int slot = wave * D + 64 * ins + lane;
       const int key = slot / CPR, pos = slot % CPR;
-      const int c = pos ^ (key & (CPR - 1));
+      const int c = pos ^ swz_key<D>(key);
       const int64_t off = ((int64_t)min(jt + key, n - 1) * D + 8 * c) * 2;
       dma16(Kb + off, lds.kv[q][0] + (wave * D + 64 * ins) * 8);
       dma16(Vb + off, lds.kv[q][1] + (wave * D + 64 * ins) * 8);
     }
   };
+  // stages 0 .. kRing - 2 now; iteration st of the tile loop issues stage
+  // st + kRing - 1
 #pragma unroll
   for (int pst = 0; pst < kRing - 1; ++pst)
     if (pst < nst) issue_stage(pst);
@@ -653,7 +670,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m2 = -INFINITY;  // running max, log2 units
   float lsum = 0.f;      // this lane's share of the row sum
-  int base = 0, lp = 0, tp = 0;  // running multiplicity of the row before the tile; edge pointers
+  int base = 0;          // the row's multiplicity just before the current tile
+  int lp = 0, tp = 0;     // next unconsumed lead / trail edge
+  int pl = 0, pt = 0;     // their positions (wave-uniform)
+  // edge positions read at a wave-uniform index are wave-uniform
+  auto pos_at = [&](const u32x2 *ev, int i) { return (int32_t)__builtin_amdgcn_readfirstlane(ev[i][0]); };
   const uint32_t low_t = bits_1_to(t);
   const uint32_t high_t = ~((2u << t) - 1u);
   const int arow_key = key_of_row(lane & 31);
@@ -661,6 +682,24 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
   // r names row (key kb + r / 4, dims dbase + 4 (r % 4) .. + 3); lane i then
   // receives V^T[dbase + i][kb .. kb + 3].
   const int vg = lane >> 4, vr = lane & 15;
+  // Per-lane operand offsets inside a ring stage.  Keys k and k + 8 (k % 16
+  // < 8) share swz_key, so the V rows of cc = 1 lie a fixed 8 rows further:
+  // an immediate offset of the LDS read.
+  uint32_t kofs[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) kofs[c] = swz<D>(arow_key, 2 * c + hh);
+  const int vkey = 16 * (vg >> 1) + (vr >> 2);
+  uint32_t vofs[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int dim = 32 * db + 16 * (vg & 1) + 4 * (vr & 3);
+#pragma unroll
+    for (int k4 = 0; k4 < 2; ++k4) vofs[db][k4] = swz<D>(vkey + 4 * k4, dim >> 3) + ((dim & 4) << 1);
+  }
+
+  // this wave's tiles are the stages [sa, sb)
+  const int sa = active ? (U0w - U0) / kTileKeys : 0;
+  const int sb = active ? (U1w - U0) / kTileKeys : 0;
 
   for (int st = 0; st < nst; ++st) {
     // this thread's loads of stage st are done once at most those of the
@@ -672,22 +711,28 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();  // every wave's loads of stage st landed; stage st - 1 is consumed
     asm volatile("" ::: "memory");
-    if (st + kRing - 1 < nst) issue_stage(st + kRing - 1);
-    {
-      const int j0 = U0 + kTileKeys * st;
-      if (!active || j0 < U0w || j0 >= U1w) continue;
-      const char *kt = (const char *)lds.kv[st % kRing][0];
-      const char *vt = (const char *)lds.kv[st % kRing][1];
+    if (st + kRing - 1 < nst) issue_stage(st + kRing - 1);  // into the ring slot of stage st - 1
+    if (st == 0 && active) {  // the edge lists landed with stage 0
+      pl = pos_at(evl, 0);
+      if (!CAUSAL) pt = pos_at(evt, 0);
+    }
+    if (st < sa || st >= sb) continue;
 
-      // a5: S^T = K Q^T
-      floatx16 sacc;
+    // a5: S^T = K Q^T; all K-operand reads are issued before the first product
+    floatx16 sacc;
+    {
+      const char *kt = (const char *)lds.kv[st % kRing][0];
+      u32x4 kr[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kr[c] = *(const u32x4 *)(kt + kofs[c]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, *(const u32x4 *)(kt + swz<D>(arow_key, 2 * c + hh)));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], sacc, 0, 0, 0);
-      }
+      for (int c = 0; c < NC; ++c)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc, 0, 0, 0);
+    }
+    {
+      const int j0 = U0 + kTileKeys * st;
 
       // a4: multiplicity c for keys j0 + 16 hh + r.
       //  * diagonal tile: the row's bytes of the precomputed table;
@@ -699,17 +744,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
       //  * otherwise c = base for all 16 keys.
       const bool diag = (j0 == r0);
       const int jend = j0 + kTileKeys;
-      const bool up_in = (int32_t)evl[lp][0] < jend;
-      const bool dn_in = !CAUSAL && (int32_t)evt[tp][0] < jend;
+      const bool up_in = pl < jend;
+      const bool dn_in = !CAUSAL && pt < jend;
       float cf[16];
       bool uni = false;
       if (diag) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) cf[r] = (float)((dg[r >> 2] >> (8 * (r & 3))) & 0xFFu);
         // the table already counts every edge at or before the tile's end
-        while ((int32_t)evl[lp][0] < jend) ++lp;
+        while (pl < jend) pl = pos_at(evl, ++lp);
         if (!CAUSAL) {
-          while ((int32_t)evt[tp][0] < jend) ++tp;
+          while (pt < jend) pt = pos_at(evt, ++tp);
           base = (int)(other_half((dg[3] >> 24) & 0xFFu, lane) * (uint32_t)(hh == 0) +
                        ((dg[3] >> 24) & 0xFFu) * (uint32_t)(hh == 1));
         }
@@ -723,9 +768,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
         for (int list = 0; list < (CAUSAL ? 1 : 2); ++list) {
           const u32x2 *ev = list ? evt : evl;
           int &ptr = list ? tp : lp;
+          int &pp = list ? pt : pl;
           const uint32_t wmask = list ? high_t : low_t;
           const uint32_t one = list ? 0xBF80u : 0x3F80u;  // bf16 -1 / +1
-          while ((int32_t)ev[ptr][0] < jend) {
+          while (pp < jend) {
             u32x4 aw, bw;
             int nin = 0, wsum = 0;
 #pragma unroll
@@ -754,9 +800,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
             cacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw),
                                                            __builtin_bit_cast(bf16x8, bw), cacc, 0, 0, 0);
             base_in = true;
-            nin += (int)other_half((uint32_t)nin, lane);
+            nin = __builtin_amdgcn_readfirstlane(nin + (int)other_half((uint32_t)nin, lane));
             wsum += (int)other_half((uint32_t)wsum, lane);
             ptr += nin;
+            pp = pos_at(ev, ptr);
             base += list ? -wsum : wsum;
             if (nin < 15) break;
           }
@@ -766,6 +813,29 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
       } else {
         uni = true;
         cf[0] = (float)base;  // one count for the lane's 16 keys
+      }
+
+      // V-operand reads of tile st for a7, landing during a6: A operand
+      // rows are dims 32 db + 16 (vg % 2) + i, keys 16 (vg / 2) + 8 cc + (0..7),
+      // read transposed from row-major V
+      u32x4 vop[NDB][2];
+      {
+        const char *vt = (const char *)lds.kv[st % kRing][1];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            // keys vkey + 8 cc (+ 4)
+            const uint32_t o1 = vofs[db][0] + 2 * D * 8 * cc;
+            const uint32_t o2 = vofs[db][1] + 2 * D * 8 * cc;
+            const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(vt + o1));
+            const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(vt + o2));
+            vop[db][cc] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                                __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                                __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                                __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+          }
+        }
       }
 
       // a6: weighted online softmax in the log2 domain.  The running max is
@@ -813,25 +883,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
       }
       const bf16x8 pk[2] = {__builtin_bit_cast(bf16x8, pw[0]), __builtin_bit_cast(bf16x8, pw[1])};
 
-      // a7: O^T += V^T P^T; A operand rows: dims 32 db + 16 (vg % 2) + i, keys
-      // 16 (vg / 2) + 8 cc + (0..7), read transposed from row-major V
+      // a7: O^T += V^T P^T
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const int key = 16 * (vg >> 1) + 8 * cc + (vr >> 2);
-          const int dim = 32 * db + 16 * (vg & 1) + 4 * (vr & 3);
-          const uint32_t o1 = swz<D>(key, dim >> 3) + ((dim & 4) << 1);
-          const uint32_t o2 = swz<D>(key + 4, dim >> 3) + ((dim & 4) << 1);
-          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(vt + o1));
-          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(vt + o2));
-          const u32x4 w4 = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
-                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
-                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
-                            __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w4), pk[cc], oacc[db], 0, 0, 0);
-        }
-      }
+        for (int cc = 0; cc < 2; ++cc)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[db][cc]), pk[cc],
+                                                             oacc[db], 0, 0, 0);
     }
   }
 
