@@ -42,6 +42,7 @@ namespace dev {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -340,22 +341,26 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
 // ---------------------------------------------------------------------------
 // Sample-fused MFMA kernel (bf16 in, fp32 accumulate).
 //
-// Workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
-// 32 rows.  Keys stream through LDS in stages of 64 (K row-major, V
-// transposed); each wave consumes the 32-key tiles of its own union range.
-// Per tile and wave:
-//   S^T (32 keys x 32 queries) = K Q^T on v_mfma_f32_32x32x16_bf16, with the
-//     key rows of the A operand permuted so that lane l holds query row
-//     r0 + l % 32 and the 16 consecutive keys j0 + 16 (l / 32) + r in its
-//     16 accumulators;
-//   multiplicity c_ij from a per-row byte histogram of block edges in LDS
-//     (prefix-summed four bytes at a time), or the row's running count when
-//     no edge falls in the tile;
+// Workgroup = 8 waves = 128 query rows of one (batch, head).  Wave w owns the
+// 16 rows r0 = 128 g + 16 w: half w % 2 of the 32-row group w / 2 whose
+// block-edge record the pre-pass wrote.  Keys stream through LDS in tiles of
+// 32; each wave consumes the tiles of its group's union range.  Per tile:
+//   S^T (32 keys x 16 queries) = K Q^T as two v_mfma_f32_16x16x32_bf16
+//     accumulators: lane l holds query r0 + l % 16 and the keys
+//     16 b + 4 (l / 16) + r of the tile (b = 0, 1; r = 0..3);
+//   multiplicities c: on the diagonal tile the pre-pass table; on a tile
+//     holding block edges, each edge adds its step to four byte counters per
+//     accumulator (keys at or after the edge); otherwise the row's running
+//     count, folded into the exponent;
 //   weighted online softmax in the log2 domain with a lazily raised running
 //     max (only when a logit exceeds it by more than 2^8);
-//   O^T (D x 32 queries) += V^T P^T on the same MFMA, P taken straight from
-//     the accumulators (no cross-lane shuffle).
-// Output O = acc / l is written once, rounded to bf16.
+//   O^T (D x 16 queries) += V^T P^T with P taken straight from the
+//     accumulators: k-slot 8 (l / 16) + e of the contraction stands for key
+//     16 (e / 4) + 4 (l / 16) + e % 4, and the transposing LDS reads deliver
+//     V^T in that order.
+// Output O = acc / l is written once, rounded to bf16.  16-row waves keep a
+// wave near 128 VGPRs, so four waves share each SIMD and cover each other's
+// LDS and matrix-core latency.
 // ---------------------------------------------------------------------------
 // K and V stream through a ring of kRing stages of 32 keys each, filled by
 // direct global->LDS loads issued kRing - 1 stages ahead.  Rows are stored
@@ -363,14 +368,14 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
 // that both operand reads are free of bank conflicts.  The LDS has 64 banks
 // of 4 bytes, so 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read,
 // must cover 256 distinct bytes modulo 256:
-//   K operand (16-byte reads): lanes 16m .. 16m + 15 read keys
-//     {0..7, 16..23} + 8m at one chunk: swz_key separates key bits 0, 1, 2, 4;
-//   V operand (8-byte transposing reads): 32 lanes read chunks 4j .. 4j + 3
-//     of 4 consecutive keys: swz_key moves those keys to distinct aligned
-//     groups of 4 chunks (D = 128: bits 2, 3 from key bits 0, 1; D = 64: the
-//     row parity is the 128-byte half, bit 2 from key bit 1).
+//   K operand (16-byte reads): 16 lanes read 16 consecutive keys at one
+//     chunk: swz_key is a bijection of the key's low four bits (D = 64: two
+//     rows share 256 bytes, so bit 0 picks the half and bits 1..3 the chunk);
+//   V operand (8-byte transposing reads): 32 lanes read chunks 2j, 2j + 1 of
+//     8 consecutive keys: swz_key sends those keys to distinct chunk pairs.
 constexpr int kTileKeys = 32;
 constexpr int kRing = 4;
+constexpr int kWaves = 8;  // waves per workgroup, 16 query rows each
 
 template <int D>
 struct MfmaLds {
@@ -383,8 +388,7 @@ typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 template <int D>
 __device__ __forceinline__ int swz_key(int key) {
-  const int g = ((key >> 2) & 1) | (((key >> 4) & 1) << 1);
-  return D == 128 ? (((key & 3) << 2) | g) : ((((key >> 1) & 1) << 2) | g);
+  return D == 128 ? (((key & 7) << 1) | ((key >> 3) & 1)) : ((((key >> 1) & 3) << 1) | ((key >> 3) & 1));
 }
 
 // byte offset of 16-byte chunk c of row `key` inside a swizzled tile
@@ -408,11 +412,6 @@ __device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base) {
 
 // s_waitcnt with vmcnt <= v and lgkmcnt == 0 (gfx9 encoding)
 #define PLSH_WAIT_VM_LGKM0(v) __builtin_amdgcn_s_waitcnt(((v) & 15) | (((v) >> 4) << 14) | (7 << 4))
-
-// key held by row a of the S^T accumulator block (see kernel comment)
-__device__ __forceinline__ int key_of_row(int a) {
-  return 16 * ((a >> 2) & 1) + 4 * (a >> 3) + (a & 3);
-}
 
 // prefix-sum 16 bytes held in 4 dwords (bytes never exceed 255)
 __device__ __forceinline__ uint32_t prefix16(u32x4 &x) {
@@ -544,12 +543,26 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int n,
   *(u32x4 *)(rec + rec_diag_off(s) + 32 * t + 16 * hh) = c;
 }
 
+// x from lane l ^ 16 (within each 32-lane half; ds_swizzle bit mode, no
+// memory access)
+__device__ __forceinline__ float xor16_f(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
+// four byte counters for keys k, k + 1, k + 2, k + 3: 1 in byte r when
+// r >= d, i.e. the keys at or after an edge d keys past k
+__device__ __forceinline__ uint32_t step4(int d) {
+  const int dc = min(max(d, 0), 4);
+  return dc < 4 ? (0x01010101u << (8 * dc)) : 0u;
+}
+
 __host__ __device__ constexpr size_t ev_wave_bytes(int s, bool causal) {
   return (size_t)(causal ? 8 : 16) * ev_count(s);
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves), amdgpu_waves_per_eu(4, 4)))
+void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   using L = MfmaLds<D>;
   __shared__ __attribute__((aligned(16))) L lds;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
@@ -557,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
   // the wave index is wave-uniform; saying so keeps all per-wave control flow
   // on the scalar unit
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int t = lane & 31, hh = lane >> 5;
+  const int qc = lane & 15, gq = lane >> 4;
 
   // ---- workgroup -> (head, batch, row tile): heavy heads first; on each of
   // the 8 XCDs (workgroups are dealt round-robin) a contiguous run of row
@@ -579,34 +592,44 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
   const int h = a.order[unit / a.batch];
   const int b = unit % a.batch;
   const int kvh = h / (a.heads / a.kv_heads);
-  const int r0 = g * 128 + wave * 32;
+  const int grp = wave >> 1, half = wave & 1;  // 32-row group of the workgroup, and which half
+  const int rg = g * 128 + 32 * grp;           // the group's first row
+  const int r0 = rg + 16 * half;               // this wave's first row
   const bool active = r0 < n;
+  const int t32 = 16 * half + qc;              // the lane's row within its group
   const int g32 = (n + 31) / 32;
   const size_t rb = rec_bytes(s);
   const uint8_t *rec_wg = ws + ((size_t)h * g32 + 4 * g) * rb;
+  const uint8_t *rec = rec_wg + (size_t)grp * rb;
 
   const uint16_t *Q = (const uint16_t *)a.q + ((int64_t)b * a.heads + h) * n * D;
   const uint16_t *K = (const uint16_t *)a.k + ((int64_t)b * a.kv_heads + kvh) * n * D;
   const uint16_t *V = (const uint16_t *)a.v + ((int64_t)b * a.kv_heads + kvh) * n * D;
   uint16_t *O = (uint16_t *)a.out + ((int64_t)b * a.heads + h) * n * D;
 
-  // ---- loads that need nothing: Q fragment (B operand of S^T = K Q^T:
-  // query r0 + t, dims 16c + 8hh + e), the wave's edge record into
-  // lane-indexed registers, and the four groups' key ranges.
-  constexpr int NC = D / 16;
+  // ---- loads that need nothing: the Q fragment (B operand of S^T = K Q^T:
+  // query r0 + qc, dims 32 c + 8 gq + e), the row's diagonal-tile
+  // multiplicities, and the four groups' key ranges
+  constexpr int NC = D / 32;
   bf16x8 qf[NC];
   {
-    const int i = r0 + t;
+    const int i = r0 + qc;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (active && i < n) raw = *(const u32x4 *)(Q + (int64_t)i * D + 16 * c + 8 * hh);
+      if (active && i < n) raw = *(const u32x4 *)(Q + (int64_t)i * D + 32 * c + 8 * gq);
       qf[c] = __builtin_bit_cast(bf16x8, raw);
     }
   }
-  // this row's 16 bytes of the diagonal-tile multiplicity table
-  u32x4 dg = {0u, 0u, 0u, 0u};
-  if (active) dg = *(const u32x4 *)(rec_wg + (size_t)wave * rb + rec_diag_off(s) + 32 * t + 16 * hh);
+  // bytes c(t32, 16 b + 4 gq + r), and (non-causal) c(t32, 31)
+  uint32_t dg[2] = {0u, 0u};
+  int dlast = 0;
+  if (active) {
+    const uint8_t *drow = rec + rec_diag_off(s) + 32 * t32;
+    dg[0] = *(const uint32_t *)(drow + 4 * gq);
+    dg[1] = *(const uint32_t *)(drow + 16 + 4 * gq);
+    if (!CAUSAL) dlast = (int)(*(const uint32_t *)(drow + 28) >> 24);
+  }
   int U0 = INT32_MAX, U1 = INT32_MIN, U0w = INT32_MAX, U1w = INT32_MIN;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -614,7 +637,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
       const int4 hdr = *(const int4 *)(rec_wg + (size_t)w * rb);
       U0 = min(U0, hdr.y);
       U1 = max(U1, hdr.z);
-      if (w == wave) { U0w = hdr.y; U1w = hdr.z; }
+      if (w == grp) { U0w = hdr.y; U1w = hdr.z; }
     }
   }
   // stage st covers keys [U0 + 32 st, U0 + 32 st + 32)
@@ -623,13 +646,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
   // count only the asynchronous LDS copies issued below
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
 
-  // the wave's sorted edge lists, copied into its LDS slice (16 bytes = two
-  // edges per lane and instruction)
-  const int nch = ev_count(s) / 2;  // 16-byte chunks per list
-  u32x2 *evl = (u32x2 *)(dyn + (size_t)wave * ev_wave_bytes(s, CAUSAL));
+  // the group's sorted edge lists, copied by its first wave into the group's
+  // LDS slice (16 bytes = two edges per lane and instruction); they are
+  // complete for both waves after the first stage's barrier
+  const int nch = ev_count(s) / 2;
+  u32x2 *evl = (u32x2 *)(dyn + (size_t)grp * ev_wave_bytes(s, CAUSAL));
   u32x2 *evt = evl + ev_count(s);
-  if (active) {
-    const uint8_t *rec = rec_wg + (size_t)wave * rb;
+  if (active && half == 0) {
     for (int c0 = 0; c0 < nch; c0 += 64)
       if (c0 + lane < nch) dma16(rec + rec_evl_off() + 16 * (c0 + lane), evl + 2 * c0);
     if (!CAUSAL)
@@ -637,278 +660,239 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a, const uin
         if (c0 + lane < nch) dma16(rec + rec_evt_off(s) + 16 * (c0 + lane), evt + 2 * c0);
   }
 
-  // ---- K/V staging: wave w copies chunks [w D, (w + 1) D) of each tile
-  // (a tile is 32 rows of D / 8 chunks); keys past the end read row n - 1,
-  // whose products are multiplied by c = 0.
-  constexpr int CPR = D / 8;           // chunks per row
-  constexpr int LPS = 2 * (D / 64);    // loads per thread per stage (K and V)
+  // ---- K/V staging: a tile is 32 rows of D / 8 chunks, 4 D chunks per
+  // matrix; wave w copies chunks [w CPW, (w + 1) CPW) with its first CPW
+  // lanes.  Keys past the end read row n - 1, whose products get c = 0.
+  constexpr int CPR = D / 8;            // chunks per row
+  constexpr int CPW = 4 * D / kWaves;   // chunks per wave, stage and matrix (<= 64)
+  constexpr int LPS = 2;                // loads per thread per stage (K and V)
   const char *Kb = (const char *)K, *Vb = (const char *)V;
   auto issue_stage = [&](int st) {
     const int q = st % kRing;
     const int jt = U0 + kTileKeys * st;
-#pragma unroll
-    for (int ins = 0; ins < D / 64; ++ins) {
-      const int slot = wave * D + 64 * ins + lane;
+    if (lane < CPW) {
+      const int slot = wave * CPW + lane;
       const int key = slot / CPR, pos = slot % CPR;
       const int c = pos ^ swz_key<D>(key);
       const int64_t off = ((int64_t)min(jt + key, n - 1) * D + 8 * c) * 2;
-      dma16(Kb + off, lds.kv[q][0] + (wave * D + 64 * ins) * 8);
-      dma16(Vb + off, lds.kv[q][1] + (wave * D + 64 * ins) * 8);
+      dma16(Kb + off, lds.kv[q][0] + wave * CPW * 8);
+      dma16(Vb + off, lds.kv[q][1] + wave * CPW * 8);
     }
   };
-  // stages 0 .. kRing - 2 now; iteration st of the tile loop issues stage
-  // st + kRing - 1
-#pragma unroll
-  for (int pst = 0; pst < kRing - 1; ++pst)
-    if (pst < nst) issue_stage(pst);
+  // stages 0 and 1 now; iteration st of the tile loop issues stage st + 2
+  if (nst > 0) issue_stage(0);
+  if (nst > 1) issue_stage(1);
+
   // ---- running state
-  constexpr int NDB = D / 32;
-  floatx16 oacc[NDB];
+  constexpr int NDB = D / 16;  // 16-dim blocks of O^T
+  floatx4 oacc[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  for (int db = 0; db < NDB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m2 = -INFINITY;  // running max, log2 units
   float lsum = 0.f;      // this lane's share of the row sum
   int base = 0;          // the row's multiplicity just before the current tile
-  int lp = 0, tp = 0;     // next unconsumed lead / trail edge
-  int pl = 0, pt = 0;     // their positions (wave-uniform)
+  int lp = 0, tp = 0;    // next unconsumed lead / trail edge
+  int pl = 0, pt = 0;    // their positions (wave-uniform)
   // edge positions read at a wave-uniform index are wave-uniform
   auto pos_at = [&](const u32x2 *ev, int i) { return (int32_t)__builtin_amdgcn_readfirstlane(ev[i][0]); };
-  const uint32_t low_t = bits_1_to(t);
-  const uint32_t high_t = ~((2u << t) - 1u);
-  const int arow_key = key_of_row(lane & 31);
-  // V-operand rows for v_ds_read_b64_tr_b16: in each group of 16 lanes, lane
-  // r names row (key kb + r / 4, dims dbase + 4 (r % 4) .. + 3); lane i then
-  // receives V^T[dbase + i][kb .. kb + 3].
-  const int vg = lane >> 4, vr = lane & 15;
-  // Per-lane operand offsets inside a ring stage.  Keys k and k + 8 (k % 16
-  // < 8) share swz_key, so the V rows of cc = 1 lie a fixed 8 rows further:
-  // an immediate offset of the LDS read.
+  const uint32_t low_t = bits_1_to(t32);
+  const uint32_t high_t = ~((2u << t32) - 1u);
+  // K operand: key 16 b + qc, chunk 4 c + gq; b = 1 lies 16 rows further
   uint32_t kofs[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) kofs[c] = swz<D>(arow_key, 2 * c + hh);
-  const int vkey = 16 * (vg >> 1) + (vr >> 2);
-  uint32_t vofs[NDB][2];
+  for (int c = 0; c < NC; ++c) kofs[c] = swz<D>(qc, 4 * c + gq);
+  // V operand (v_ds_read_b64_tr_b16): in each 16-lane group gq, lane r names
+  // the row (key 4 gq + r / 4, dims 16 db + 4 (r % 4) .. + 3), and lane i
+  // receives V[4 gq + e][16 db + i], e = 0..3; keys + 16 lie 16 rows further
+  uint32_t vofs[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    const int dim = 32 * db + 16 * (vg & 1) + 4 * (vr & 3);
-#pragma unroll
-    for (int k4 = 0; k4 < 2; ++k4) vofs[db][k4] = swz<D>(vkey + 4 * k4, dim >> 3) + ((dim & 4) << 1);
+    const int dim = 16 * db + 4 * (qc & 3);
+    vofs[db] = swz<D>(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1);
   }
 
   // this wave's tiles are the stages [sa, sb)
   const int sa = active ? (U0w - U0) / kTileKeys : 0;
   const int sb = active ? (U1w - U0) / kTileKeys : 0;
 
+  // a5: S^T = K Q^T for the tile of stage st, keys 16 b + 4 gq + r
+  floatx4 sacc[2];
+  auto qk_tile = [&](int st) {
+    const char *kt = (const char *)lds.kv[st % kRing][0];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      u32x4 kr[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kr[c] = *(const u32x4 *)(kt + kofs[c] + 32 * D * bb);
+      sacc[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc[bb], 0, 0, 0);
+    }
+  };
+
+  // a4, a6, a7 for the tile of stage st, whose logits are in sacc
+  auto finish_tile = [&](int st) {
+    const char *vt = (const char *)lds.kv[st % kRing][1];
+    const int j0 = U0 + kTileKeys * st;
+
+    // a4: multiplicity c for keys j0 + 16 b + 4 gq + r.
+    //  * diagonal tile: the row's bytes of the precomputed table;
+    //  * a tile holding sample edges (lower block ends = leads on the left of
+    //    the diagonal, upper ends = trails on the right; positions are
+    //    wave-uniform): c = base +- sum over edges of w_e(row) [key >= pos_e],
+    //    four keys per byte-counter word;
+    //  * otherwise c = base for all keys of the tile.
+    const int jend = j0 + kTileKeys;
+    float cf[8];
+    int kind;  // 0: one count for the tile, 1: per-key counts
+    if (j0 == rg) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) cf[r] = (float)((dg[r >> 2] >> (8 * (r & 3))) & 0xFFu);
+      // the table already counts every edge at or before the tile's end
+      while (pl < jend) pl = pos_at(evl, ++lp);
+      if (!CAUSAL) {
+        while (pt < jend) pt = pos_at(evt, ++tp);
+        base = dlast;
+      }
+      kind = 1;
+    } else if (pl < jend || (!CAUSAL && pt < jend)) {
+      const int kb = j0 + 4 * gq;  // the lane's first key of word 0 (word 1: + 16)
+      uint32_t cw[2] = {(uint32_t)base * 0x01010101u, (uint32_t)base * 0x01010101u};
+      while (pl < jend) {  // leads: the sample's block of the row starts at pl
+        const uint32_t w = (evl[lp][1] & low_t) == 0u ? 1u : 0u;
+        cw[0] += w * step4(pl - kb);
+        cw[1] += w * step4(pl - kb - 16);
+        base += (int)w;
+        pl = pos_at(evl, ++lp);
+      }
+      if (!CAUSAL) {
+        while (pt < jend) {  // trails: the sample's block of the row ends before pt
+          const uint32_t w = (evt[tp][1] & high_t) == 0u ? 1u : 0u;
+          cw[0] -= w * step4(pt - kb);
+          cw[1] -= w * step4(pt - kb - 16);
+          base -= (int)w;
+          pt = pos_at(evt, ++tp);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) cf[r] = (float)((cw[r >> 2] >> (8 * (r & 3))) & 0xFFu);
+      kind = 1;
+    } else {
+      cf[0] = (float)base;
+      kind = 0;
+    }
+
+    // a6: weighted online softmax in the log2 domain.  The running max is
+    // raised only when a logit exceeds it by more than 2^8 (the result does
+    // not depend on the max used, and a rescale of the accumulators is then
+    // rare).  A tile with one count per row folds log2(c) into the exponent
+    // bias; otherwise P = c * 2^(...).  P is rounded to bf16 in pairs and the
+    // row sum adds exactly the rounded weights that enter PV.
+    float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    mx = fmaxf(mx, xor16_f(mx));
+    mx = fmaxf(mx, other_half_f(mx, lane)) * kLog2e;
+    const bool need = mx > m2 + 8.0f;
+    if (__any(need)) {
+      const float mnew = need ? mx : m2;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m2 = mnew;
+    }
+    u32x4 pw;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    if (__builtin_amdgcn_readfirstlane(kind) == 0) {
+      const float bias = m2 - __builtin_amdgcn_logf(cf[0]);  // c = 0 gives bias = +inf, P = 0
+#pragma unroll
+      for (int r = 0; r < 8; r += 2) {
+        const floatx2 pf = {__builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][r & 3], kLog2e, -bias)),
+                            __builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][(r & 3) + 1], kLog2e, -bias))};
+        const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+        pw[r >> 1] = __builtin_bit_cast(uint32_t, pb);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; r += 2) {
+        const floatx2 pf = {cf[r] * __builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][r & 3], kLog2e, -m2)),
+                            cf[r + 1] * __builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][(r & 3) + 1], kLog2e, -m2))};
+        const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+        pw[r >> 1] = __builtin_bit_cast(uint32_t, pb);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
+      }
+    }
+    const bf16x8 pk = __builtin_bit_cast(bf16x8, pw);
+
+    // a7: O^T += V^T P^T, the V operand read in two batches of 16-dim blocks
+    constexpr int NB = NDB < 4 ? NDB : 4;
+#pragma unroll
+    for (int d0 = 0; d0 < NDB; d0 += NB) {
+      u32x4 vop[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const char *va = vt + vofs[d0 + j];
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)va);
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(va + 16 * 2 * D));
+        vop[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                       __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                       __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                       __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        oacc[d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[j]), pk, oacc[d0 + j], 0, 0, 0);
+    }
+  };
+
+  // Ping-pong schedule.  Waves w and w + 4 share a SIMD.  Waves 0..3 run a
+  // tile within one iteration (S^T on the matrix cores, then softmax on the
+  // vector unit, then PV); waves 4..7 lag half a tile: an iteration finishes
+  // the previous tile (softmax, PV) and then starts its own (S^T).  The two
+  // waves of a SIMD thus alternate between the matrix cores and the vector
+  // unit instead of contending for the same one.  The lagging waves read the
+  // V rows of stage st - 1 during iteration st, so iteration st refills the
+  // ring slot of stage st - 2 (loads issued two stages ahead).
+  const bool lag = wave >= 4;
   for (int st = 0; st < nst; ++st) {
-    // this thread's loads of stage st are done once at most those of the
-    // (up to two) later stages already issued are outstanding
-    const int ahead = min(kRing - 2, nst - 1 - st);
-    if (ahead >= 2) PLSH_WAIT_VM_LGKM0(2 * LPS);
-    else if (ahead == 1) PLSH_WAIT_VM_LGKM0(LPS);
+    // this thread's loads of stage st are done once at most those of stage
+    // st + 1 (issued one iteration ago) are outstanding
+    if (st + 1 < nst) PLSH_WAIT_VM_LGKM0(LPS);
     else PLSH_WAIT_VM_LGKM0(0);
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // every wave's loads of stage st landed; stage st - 1 is consumed
+    __builtin_amdgcn_s_barrier();  // every wave: stage st landed, stage st - 2 consumed
     asm volatile("" ::: "memory");
-    if (st + kRing - 1 < nst) issue_stage(st + kRing - 1);  // into the ring slot of stage st - 1
+    if (st + 2 < nst) issue_stage(st + 2);  // into the ring slot of stage st - 2
     if (st == 0 && active) {  // the edge lists landed with stage 0
       pl = pos_at(evl, 0);
       if (!CAUSAL) pt = pos_at(evt, 0);
     }
-    if (st < sa || st >= sb) continue;
-
-    // a5: S^T = K Q^T; all K-operand reads are issued before the first product
-    floatx16 sacc;
-    {
-      const char *kt = (const char *)lds.kv[st % kRing][0];
-      u32x4 kr[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kr[c] = *(const u32x4 *)(kt + kofs[c]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc, 0, 0, 0);
-    }
-    {
-      const int j0 = U0 + kTileKeys * st;
-
-      // a4: multiplicity c for keys j0 + 16 hh + r.
-      //  * diagonal tile: the row's bytes of the precomputed table;
-      //  * a tile holding sample edges at wave-uniform positions (lower ends
-      //    = leads, upper ends = trails): c = base + sum_e w_e(row) [pos_e <=
-      //    key] evaluated as one 32x32x16 bf16 MFMA per 15 edges, the A operand
-      //    being the key indicators and the B operand the row weights; the
-      //    16th slot carries the row's running count;
-      //  * otherwise c = base for all 16 keys.
-      const bool diag = (j0 == r0);
-      const int jend = j0 + kTileKeys;
-      const bool up_in = pl < jend;
-      const bool dn_in = !CAUSAL && pt < jend;
-      float cf[16];
-      bool uni = false;
-      if (diag) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cf[r] = (float)((dg[r >> 2] >> (8 * (r & 3))) & 0xFFu);
-        // the table already counts every edge at or before the tile's end
-        while (pl < jend) pl = pos_at(evl, ++lp);
-        if (!CAUSAL) {
-          while (pt < jend) pt = pos_at(evt, ++tp);
-          base = (int)(other_half((dg[3] >> 24) & 0xFFu, lane) * (uint32_t)(hh == 0) +
-                       ((dg[3] >> 24) & 0xFFu) * (uint32_t)(hh == 1));
-        }
-      } else if (up_in || dn_in) {
-        floatx16 cacc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cacc[r] = 0.f;
-        const int akey = j0 + arow_key;
-        bool base_in = false;
-#pragma unroll
-        for (int list = 0; list < (CAUSAL ? 1 : 2); ++list) {
-          const u32x2 *ev = list ? evt : evl;
-          int &ptr = list ? tp : lp;
-          int &pp = list ? pt : pl;
-          const uint32_t wmask = list ? high_t : low_t;
-          const uint32_t one = list ? 0xBF80u : 0x3F80u;  // bf16 -1 / +1
-          while (pp < jend) {
-            u32x4 aw, bw;
-            int nin = 0, wsum = 0;
-#pragma unroll
-            for (int m2i = 0; m2i < 4; ++m2i) {
-              uint32_t av2 = 0u, bv2 = 0u;
-#pragma unroll
-              for (int half = 0; half < 2; ++half) {
-                const int slot = 8 * hh + 2 * m2i + half;
-                const u32x2 e = ev[ptr + slot];
-                const bool in = slot < 15 && (int32_t)e[0] < jend;
-                const bool on = in && (e[1] & wmask) == 0u;
-                uint32_t a16 = ((int32_t)e[0] <= akey && slot < 15) ? 0x3F80u : 0u;
-                uint32_t b16 = on ? one : 0u;
-                if (slot == 15) {
-                  a16 = 0x3F80u;
-                  b16 = base_in ? 0u : f32_to_bf16_bits((float)base);
-                }
-                av2 |= a16 << (16 * half);
-                bv2 |= b16 << (16 * half);
-                nin += in;
-                wsum += on;
-              }
-              aw[m2i] = av2;
-              bw[m2i] = bv2;
-            }
-            cacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aw),
-                                                           __builtin_bit_cast(bf16x8, bw), cacc, 0, 0, 0);
-            base_in = true;
-            nin = __builtin_amdgcn_readfirstlane(nin + (int)other_half((uint32_t)nin, lane));
-            wsum += (int)other_half((uint32_t)wsum, lane);
-            ptr += nin;
-            pp = pos_at(ev, ptr);
-            base += list ? -wsum : wsum;
-            if (nin < 15) break;
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cf[r] = cacc[r];
-      } else {
-        uni = true;
-        cf[0] = (float)base;  // one count for the lane's 16 keys
-      }
-
-      // V-operand reads of tile st for a7, landing during a6: A operand
-      // rows are dims 32 db + 16 (vg % 2) + i, keys 16 (vg / 2) + 8 cc + (0..7),
-      // read transposed from row-major V
-      u32x4 vop[NDB][2];
-      {
-        const char *vt = (const char *)lds.kv[st % kRing][1];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            // keys vkey + 8 cc (+ 4)
-            const uint32_t o1 = vofs[db][0] + 2 * D * 8 * cc;
-            const uint32_t o2 = vofs[db][1] + 2 * D * 8 * cc;
-            const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(vt + o1));
-            const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(vt + o2));
-            vop[db][cc] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
-                                __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
-                                __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
-                                __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
-          }
-        }
-      }
-
-      // a6: weighted online softmax in the log2 domain.  The running max is
-      // raised only when a logit exceeds it by more than 2^8 (the result does
-      // not depend on the max used, and a rescale of the accumulators is then
-      // rare).  A tile with one count per row folds log2(c) into the exponent
-      // bias; otherwise P = c * 2^(...).  P is rounded to bf16 in pairs and the
-      // row sum adds exactly the rounded weights that enter PV.
-      float mx = sacc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-      mx = fmaxf(mx, other_half_f(mx, lane)) * kLog2e;
-      const bool need = mx > m2 + 8.0f;
-      if (__any(need)) {
-        const float mnew = need ? mx : m2;
-        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m2 = mnew;
-      }
-      u32x4 pw[2];
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-      if (uni) {
-        const float bias = m2 - __builtin_amdgcn_logf(cf[0]);  // c = 0 gives bias = +inf, P = 0
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const floatx2 pf = {__builtin_amdgcn_exp2f(fmaf(sacc[r], kLog2e, -bias)),
-                              __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], kLog2e, -bias))};
-          const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
-          pw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const floatx2 pf = {cf[r] * __builtin_amdgcn_exp2f(fmaf(sacc[r], kLog2e, -m2)),
-                              cf[r + 1] * __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], kLog2e, -m2))};
-          const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
-          pw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
-        }
-      }
-      const bf16x8 pk[2] = {__builtin_bit_cast(bf16x8, pw[0]), __builtin_bit_cast(bf16x8, pw[1])};
-
-      // a7: O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[db][cc]), pk[cc],
-                                                             oacc[db], 0, 0, 0);
-    }
+    const bool cur = st >= sa && st < sb;
+    if (!lag && cur) qk_tile(st);
+    const int fs = lag ? st - 1 : st;  // the tile this iteration finishes
+    if (fs >= sa && fs < sb) finish_tile(fs);
+    if (lag && cur) qk_tile(st);
   }
+  // the lagging waves' last tile (no ring slot is refilled any more)
+  if (lag && nst - 1 >= sa && nst - 1 < sb) finish_tile(nst - 1);
 
-  // a8: normalisation epilogue, one store per output element
+  // a8: normalisation epilogue, one store per output element; the row sum
+  // is spread over the four lanes qc + 16 gq
   if (!active) return;
-  const float ltot = lsum + other_half_f(lsum, lane);
+  float ltot = lsum + xor16_f(lsum);
+  ltot += other_half_f(ltot, lane);
   const float inv = 1.0f / ltot;
-  const int i = r0 + t;
+  const int i = r0 + qc;
   if (i >= n) return;
-  uint16_t *orow = O + (int64_t)i * D;
+  uint16_t *orow = O + (int64_t)i * D + 4 * gq;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      u32x2 w2;
-      w2[0] = f32_to_bf16_bits(oacc[db][4 * gq + 0] * inv) | (f32_to_bf16_bits(oacc[db][4 * gq + 1] * inv) << 16);
-      w2[1] = f32_to_bf16_bits(oacc[db][4 * gq + 2] * inv) | (f32_to_bf16_bits(oacc[db][4 * gq + 3] * inv) << 16);
-      *(u32x2 *)(orow + 32 * db + 8 * gq + 4 * hh) = w2;
-    }
+    u32x2 w2;
+    w2[0] = f32_to_bf16_bits(oacc[db][0] * inv) | (f32_to_bf16_bits(oacc[db][1] * inv) << 16);
+    w2[1] = f32_to_bf16_bits(oacc[db][2] * inv) | (f32_to_bf16_bits(oacc[db][3] * inv) << 16);
+    *(u32x2 *)(orow + 16 * db) = w2;
   }
 }
 
@@ -1027,7 +1011,7 @@ plsh_status launch_mfma(const dev::AttnArgs &a, int d, int causal, hipStream_t s
   else hipLaunchKernelGGL(dev::edges_kernel<false>, egrid, eblock, eshm, st, a.params, a.n, a.heads, a.s, g32, (uint8_t *)ws);
   plsh_status rc = launch_check(who);
   if (rc == PLSH_OK) {
-    const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(256);
+    const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(64 * dev::kWaves);
     const uint8_t *w8 = (const uint8_t *)ws;
     const size_t shm = 4 * dev::ev_wave_bytes(a.s, causal != 0);
     if (d == 64) {
