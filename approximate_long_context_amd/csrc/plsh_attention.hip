@@ -380,6 +380,9 @@ constexpr int kWaves = 8;  // waves per workgroup, 16 query rows each
 template <int D>
 struct MfmaLds {
   alignas(16) uint16_t kv[kRing][2][kTileKeys * D];
+  // step[u][k]: byte r of word k is 1 when key 4 k + r of a tile is at or
+  // after tile offset u (the keys an edge at offset u counts for)
+  uint32_t step[kTileKeys][kTileKeys / 4];
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -433,11 +436,16 @@ __device__ __forceinline__ uint32_t prefix16(u32x4 &x) {
 //   [0, 16)              int32 nnz, U0w, U1w, 0: number of samples with a block
 //                        start inside the group's rows; the group's key range
 //                        [U0w, U1w) (32-aligned)
-//   [16, +8 E)           (lead, mask) of every sample sorted by (lead, k), then
+//   [16, +8 E)           (lead, W) of every sample sorted by (lead, k), then
 //                        16 sentinels (0x7FFFFFFF, 0); E = s + 16 rounded up
-//                        to even, so that each list is whole 16-byte chunks
-//   [.., +8 E)           (trail, mask) sorted by (trail, k), 16 sentinels
-//                        (written by the non-causal pass only)
+//                        to even, so that each list is whole 16-byte chunks;
+//                        bit t of W is set when row r0 + t's block of that
+//                        sample starts at the lead (no block start in rows
+//                        r0 + 1 .. r0 + t)
+//   [.., +8 E)           (trail, W) sorted by (trail, k), 16 sentinels
+//                        (written by the non-causal pass only); bit t of W is
+//                        set when row r0 + t's block ends at the trail (no
+//                        block start in rows r0 + t + 1 .. r0 + 31)
 //   [.., +1024)          multiplicity of the diagonal tile: byte [t][u] is
 //                        c(r0 + t, r0 + u), zero where j > i (causal) or j >= n
 // The fp64 block searches are latency-bound; as a kernel of their own they
@@ -485,8 +493,11 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int n,
       rl += (l2 < lk) | ((l2 == lk) & (k2 < k));
       rt += (t2 < tk) | ((t2 == tk) & (k2 < k));
     }
-    evl[rl] = u32x2{(uint32_t)lk, mk};
-    if (!CAUSAL) evt[rt] = u32x2{(uint32_t)tk, mk};
+    const uint32_t ml = mk & ~1u;  // starts inside rows r0 + 1 .. r0 + 31
+    const uint32_t wl = ml ? ((1u << __builtin_ctz(ml)) - 1u) : 0xFFFFFFFFu;
+    const uint32_t wt = mk ? ~((1u << (31 - __builtin_clz(mk))) - 1u) : 0xFFFFFFFFu;
+    evl[rl] = u32x2{(uint32_t)lk, wl};
+    if (!CAUSAL) evt[rt] = u32x2{(uint32_t)tk, wt};
   }
   if (lane < kSentinels) {
     evl[s + lane] = u32x2{0x7FFFFFFFu, 0u};
@@ -571,6 +582,11 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   // on the scalar unit
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int qc = lane & 15, gq = lane >> 4;
+  // the step table, complete after the first stage's barrier
+  if (threadIdx.x < kTileKeys * kTileKeys / 4) {
+    const int u = threadIdx.x >> 3, k = threadIdx.x & 7;
+    lds.step[u][k] = step4(u - 4 * k);
+  }
 
   // ---- workgroup -> (head, batch, row tile): heavy heads first; on each of
   // the 8 XCDs (workgroups are dealt round-robin) a contiguous run of row
@@ -607,9 +623,25 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   const uint16_t *V = (const uint16_t *)a.v + ((int64_t)b * a.kv_heads + kvh) * n * D;
   uint16_t *O = (uint16_t *)a.out + ((int64_t)b * a.heads + h) * n * D;
 
-  // ---- loads that need nothing: the Q fragment (B operand of S^T = K Q^T:
-  // query r0 + qc, dims 32 c + 8 gq + e), the row's diagonal-tile
-  // multiplicities, and the four groups' key ranges
+  // ---- the four groups' key ranges first (the K/V copies need them), then
+  // the Q fragment (B operand of S^T = K Q^T: query r0 + qc, dims 32 c +
+  // 8 gq + e) and the row's diagonal-tile multiplicities, which are first
+  // needed after the first stage's wait and so overlap the first copies
+  int U0 = INT32_MAX, U1 = INT32_MIN, U0w = INT32_MAX, U1w = INT32_MIN;
+  {
+    // all four headers in one round trip: groups past the end re-read the
+    // last valid one (their ranges then add nothing)
+    const int wlast = min(3, (n - 1 - g * 128) / 32);
+    int4 hdr[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) hdr[w] = *(const int4 *)(rec_wg + (size_t)min(w, wlast) * rb);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      U0 = min(U0, hdr[w].y);
+      U1 = max(U1, hdr[w].z);
+      if (w == grp) { U0w = hdr[w].y; U1w = hdr[w].z; }
+    }
+  }
   constexpr int NC = D / 32;
   bf16x8 qf[NC];
   {
@@ -630,20 +662,11 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     dg[1] = *(const uint32_t *)(drow + 16 + 4 * gq);
     if (!CAUSAL) dlast = (int)(*(const uint32_t *)(drow + 28) >> 24);
   }
-  int U0 = INT32_MAX, U1 = INT32_MIN, U0w = INT32_MAX, U1w = INT32_MIN;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (g * 128 + 32 * w < n) {
-      const int4 hdr = *(const int4 *)(rec_wg + (size_t)w * rb);
-      U0 = min(U0, hdr.y);
-      U1 = max(U1, hdr.z);
-      if (w == grp) { U0w = hdr.y; U1w = hdr.z; }
-    }
-  }
   // stage st covers keys [U0 + 32 st, U0 + 32 st + 32)
   const int nst = (U1 > U0) ? (U1 - U0) / kTileKeys : 0;
-  // everything loaded so far is needed before the first tile; later waits
-  // count only the asynchronous LDS copies issued below
+  // Everything loaded so far is needed before the first tile.  Waiting here,
+  // before the first K/V copies are issued, measured faster than letting the
+  // first stage waits cover these loads.
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
 
   // the group's sorted edge lists, copied by its first wave into the group's
@@ -679,9 +702,11 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
       dma16(Vb + off, lds.kv[q][1] + wave * CPW * 8);
     }
   };
-  // stages 0 and 1 now; iteration st of the tile loop issues stage st + 2
-  if (nst > 0) issue_stage(0);
-  if (nst > 1) issue_stage(1);
+  // stages 0 .. kRing - 2 now; iteration st of the tile loop issues stage
+  // st + kRing - 1
+#pragma unroll
+  for (int pst = 0; pst < kRing - 1; ++pst)
+    if (pst < nst) issue_stage(pst);
 
   // ---- running state
   constexpr int NDB = D / 16;  // 16-dim blocks of O^T
@@ -695,8 +720,6 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   int pl = 0, pt = 0;    // their positions (wave-uniform)
   // edge positions read at a wave-uniform index are wave-uniform
   auto pos_at = [&](const u32x2 *ev, int i) { return (int32_t)__builtin_amdgcn_readfirstlane(ev[i][0]); };
-  const uint32_t low_t = bits_1_to(t32);
-  const uint32_t high_t = ~((2u << t32) - 1u);
   // K operand: key 16 b + qc, chunk 4 c + gq; b = 1 lies 16 rows further
   uint32_t kofs[NC];
 #pragma unroll
@@ -731,6 +754,22 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     }
   };
 
+  // Visits, in order, the edges of a sorted list at positions < jend starting
+  // at index ptr (position pp), and advances ptr / pp past them.  Lane l reads
+  // edge ptr + l, so up to 64 edges are found with one LDS read and a ballot
+  // (the list ends in 16 sentinels at INT32_MAX; reads stay inside it).
+  const int ev_last = s + kSentinels - 1;
+  auto edges_in_tile = [&](const u32x2 *ev, int &ptr, int &pp, int jend, auto &&visit) {
+    while (pp < jend) {
+      const u32x2 e = ev[min(ptr + lane, ev_last)];
+      const int k = __popcll(__ballot((int32_t)e[0] < jend));  // a prefix of the lanes
+      for (int i = 0; i < k; ++i)
+        visit((int32_t)__builtin_amdgcn_readlane(e[0], i), __builtin_amdgcn_readlane(e[1], i));
+      ptr += k;
+      pp = k < 64 ? (int32_t)__builtin_amdgcn_readlane(e[0], k) : pos_at(ev, ptr);
+    }
+  };
+
   // a4, a6, a7 for the tile of stage st, whose logits are in sacc
   auto finish_tile = [&](int st) {
     const char *vt = (const char *)lds.kv[st % kRing][1];
@@ -747,34 +786,40 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     float cf[8];
     int kind;  // 0: one count for the tile, 1: per-key counts
     if (j0 == rg) {
+      // (kept here: hoisted out of the loop, the conversion would wait for
+      // the table load, and with it for every K/V copy issued after it)
+      uint32_t d0 = dg[0], d1 = dg[1];
+      asm volatile("" : "+v"(d0), "+v"(d1));
 #pragma unroll
-      for (int r = 0; r < 8; ++r) cf[r] = (float)((dg[r >> 2] >> (8 * (r & 3))) & 0xFFu);
+      for (int r = 0; r < 8; ++r) cf[r] = (float)((((r >> 2) ? d1 : d0) >> (8 * (r & 3))) & 0xFFu);
       // the table already counts every edge at or before the tile's end
-      while (pl < jend) pl = pos_at(evl, ++lp);
+      edges_in_tile(evl, lp, pl, jend, [](int, uint32_t) {});
       if (!CAUSAL) {
-        while (pt < jend) pt = pos_at(evt, ++tp);
+        edges_in_tile(evt, tp, pt, jend, [](int, uint32_t) {});
         base = dlast;
       }
       kind = 1;
     } else if (pl < jend || (!CAUSAL && pt < jend)) {
-      const int kb = j0 + 4 * gq;  // the lane's first key of word 0 (word 1: + 16)
+      // the lane's keys are words gq and gq + 4 of the tile's step rows
+      const uint32_t *srow = &lds.step[0][gq];
       uint32_t cw[2] = {(uint32_t)base * 0x01010101u, (uint32_t)base * 0x01010101u};
-      while (pl < jend) {  // leads: the sample's block of the row starts at pl
-        const uint32_t w = (evl[lp][1] & low_t) == 0u ? 1u : 0u;
-        cw[0] += w * step4(pl - kb);
-        cw[1] += w * step4(pl - kb - 16);
+      // leads: the sample's block of the row starts at pos
+      edges_in_tile(evl, lp, pl, jend, [&](int pos, uint32_t W) {
+        const uint32_t w = (W >> t32) & 1u;
+        const uint32_t *sr = srow + 8 * (pos - j0);
+        cw[0] += w * sr[0];
+        cw[1] += w * sr[4];
         base += (int)w;
-        pl = pos_at(evl, ++lp);
-      }
-      if (!CAUSAL) {
-        while (pt < jend) {  // trails: the sample's block of the row ends before pt
-          const uint32_t w = (evt[tp][1] & high_t) == 0u ? 1u : 0u;
-          cw[0] -= w * step4(pt - kb);
-          cw[1] -= w * step4(pt - kb - 16);
+      });
+      // trails: the sample's block of the row ends before pos
+      if (!CAUSAL)
+        edges_in_tile(evt, tp, pt, jend, [&](int pos, uint32_t W) {
+          const uint32_t w = (W >> t32) & 1u;
+          const uint32_t *sr = srow + 8 * (pos - j0);
+          cw[0] -= w * sr[0];
+          cw[1] -= w * sr[4];
           base -= (int)w;
-          pt = pos_at(evt, ++tp);
-        }
-      }
+        });
 #pragma unroll
       for (int r = 0; r < 8; ++r) cf[r] = (float)((cw[r >> 2] >> (8 * (r & 3))) & 0xFFu);
       kind = 1;
@@ -847,36 +892,26 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     }
   };
 
-  // Ping-pong schedule.  Waves w and w + 4 share a SIMD.  Waves 0..3 run a
-  // tile within one iteration (S^T on the matrix cores, then softmax on the
-  // vector unit, then PV); waves 4..7 lag half a tile: an iteration finishes
-  // the previous tile (softmax, PV) and then starts its own (S^T).  The two
-  // waves of a SIMD thus alternate between the matrix cores and the vector
-  // unit instead of contending for the same one.  The lagging waves read the
-  // V rows of stage st - 1 during iteration st, so iteration st refills the
-  // ring slot of stage st - 2 (loads issued two stages ahead).
-  const bool lag = wave >= 4;
   for (int st = 0; st < nst; ++st) {
-    // this thread's loads of stage st are done once at most those of stage
-    // st + 1 (issued one iteration ago) are outstanding
-    if (st + 1 < nst) PLSH_WAIT_VM_LGKM0(LPS);
+    // this thread's loads of stage st are done once at most those of the
+    // (up to two) later stages already issued are outstanding
+    const int ahead = min(kRing - 2, nst - 1 - st);
+    if (ahead >= 2) PLSH_WAIT_VM_LGKM0(2 * LPS);
+    else if (ahead == 1) PLSH_WAIT_VM_LGKM0(LPS);
     else PLSH_WAIT_VM_LGKM0(0);
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // every wave: stage st landed, stage st - 2 consumed
+    __builtin_amdgcn_s_barrier();  // every wave's loads of stage st landed; stage st - 1 is consumed
     asm volatile("" ::: "memory");
-    if (st + 2 < nst) issue_stage(st + 2);  // into the ring slot of stage st - 2
+    if (st + kRing - 1 < nst) issue_stage(st + kRing - 1);  // into the ring slot of stage st - 1
     if (st == 0 && active) {  // the edge lists landed with stage 0
       pl = pos_at(evl, 0);
       if (!CAUSAL) pt = pos_at(evt, 0);
     }
-    const bool cur = st >= sa && st < sb;
-    if (!lag && cur) qk_tile(st);
-    const int fs = lag ? st - 1 : st;  // the tile this iteration finishes
-    if (fs >= sa && fs < sb) finish_tile(fs);
-    if (lag && cur) qk_tile(st);
+    if (st >= sa && st < sb) {
+      qk_tile(st);
+      finish_tile(st);
+    }
   }
-  // the lagging waves' last tile (no ring slot is refilled any more)
-  if (lag && nst - 1 >= sa && nst - 1 < sb) finish_tile(nst - 1);
 
   // a8: normalisation epilogue, one store per output element; the row sum
   // is spread over the four lanes qc + 16 gq
@@ -889,10 +924,9 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   uint16_t *orow = O + (int64_t)i * D + 4 * gq;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    u32x2 w2;
-    w2[0] = f32_to_bf16_bits(oacc[db][0] * inv) | (f32_to_bf16_bits(oacc[db][1] * inv) << 16);
-    w2[1] = f32_to_bf16_bits(oacc[db][2] * inv) | (f32_to_bf16_bits(oacc[db][3] * inv) << 16);
-    *(u32x2 *)(orow + 16 * db) = w2;
+    const bf16x2 h0 = __builtin_convertvector((floatx2{oacc[db][0] * inv, oacc[db][1] * inv}), bf16x2);
+    const bf16x2 h1 = __builtin_convertvector((floatx2{oacc[db][2] * inv, oacc[db][3] * inv}), bf16x2);
+    *(u32x2 *)(orow + 16 * db) = u32x2{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
   }
 }
 
