@@ -33,6 +33,8 @@
 
 #include <algorithm>
 #include <numeric>
+#include <utility>
+#include <vector>
 
 #include "plsh_binning.h"
 #include "plsh_internal.h"
@@ -998,6 +1000,31 @@ void fill_args(dev::AttnArgs &a, const void *q, const void *k, const void *v, vo
   for (int i = 0; i < dev::kMaxHeadsArg; ++i) a.order[i] = i < heads ? idx[i] : 0;
 }
 
+// Per-thread timer of the attention kernel (measurement aid): while enabled,
+// every launch records a pair of events around the attention kernel on the
+// call's stream.  The events are created on first use and reused.
+struct KernelTimer {
+  bool on = false;
+  size_t used = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+};
+thread_local KernelTimer g_timer;
+
+// the event pair for the next timed launch, or nullptr when timing is off
+std::pair<hipEvent_t, hipEvent_t> *timer_slot() {
+  if (!g_timer.on) return nullptr;
+  if (g_timer.used == g_timer.ev.size()) {
+    hipEvent_t b = nullptr, e = nullptr;
+    if (hipEventCreate(&b) != hipSuccess || hipEventCreate(&e) != hipSuccess) {
+      (void)hipGetLastError();
+      if (b) (void)hipEventDestroy(b);
+      return nullptr;
+    }
+    g_timer.ev.emplace_back(b, e);
+  }
+  return &g_timer.ev[g_timer.used++];
+}
+
 plsh_status launch_check(const char *who) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PLSH_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -1018,6 +1045,8 @@ plsh_status launch_valu(const dev::AttnArgs &a, int d, plsh_dtype dtype, int cau
                         const char *who) {
   const size_t shm = 4 * dev::valu_wave_bytes(a.s, d);
   const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(256);
+  auto *tm = timer_slot();
+  if (tm) (void)hipEventRecord(tm->first, st);
   if (dtype == PLSH_F32) {
     if (d == 64) hipLaunchKernelGGL((dev::attn_valu_kernel<float, 64>), grid, block, shm, st, a, causal);
     else hipLaunchKernelGGL((dev::attn_valu_kernel<float, 128>), grid, block, shm, st, a, causal);
@@ -1025,6 +1054,7 @@ plsh_status launch_valu(const dev::AttnArgs &a, int d, plsh_dtype dtype, int cau
     if (d == 64) hipLaunchKernelGGL((dev::attn_valu_kernel<uint16_t, 64>), grid, block, shm, st, a, causal);
     else hipLaunchKernelGGL((dev::attn_valu_kernel<uint16_t, 128>), grid, block, shm, st, a, causal);
   }
+  if (tm) (void)hipEventRecord(tm->second, st);
   return launch_check(who);
 }
 
@@ -1048,6 +1078,8 @@ plsh_status launch_mfma(const dev::AttnArgs &a, int d, int causal, hipStream_t s
     const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(64 * dev::kWaves);
     const uint8_t *w8 = (const uint8_t *)ws;
     const size_t shm = 4 * dev::ev_wave_bytes(a.s, causal != 0);
+    auto *tm = timer_slot();
+    if (tm) (void)hipEventRecord(tm->first, st);
     if (d == 64) {
       if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<64, true>), grid, block, shm, st, a, w8);
       else hipLaunchKernelGGL((dev::attn_mfma_kernel<64, false>), grid, block, shm, st, a, w8);
@@ -1055,6 +1087,7 @@ plsh_status launch_mfma(const dev::AttnArgs &a, int d, int causal, hipStream_t s
       if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<128, true>), grid, block, shm, st, a, w8);
       else hipLaunchKernelGGL((dev::attn_mfma_kernel<128, false>), grid, block, shm, st, a, w8);
     }
+    if (tm) (void)hipEventRecord(tm->second, st);
     rc = launch_check(who);
   }
   e = hipFreeAsync(ws, st);
@@ -1116,4 +1149,34 @@ extern "C" plsh_status plsh_debug_block_intervals(const plsh_tables *bt, int32_t
   hipLaunchKernelGGL(dev::debug_intervals_kernel, dim3((unsigned)((int64_t)groups * bt->heads)), dim3(64), shm,
                      (hipStream_t)stream, bt->params, bt->n, bt->heads, bt->s, groups, lohi);
   return launch_check(who);
+}
+
+extern "C" plsh_status plsh_kernel_timer(int32_t enable) {
+  clear_error();
+  g_timer.on = enable != 0;
+  g_timer.used = 0;
+  return PLSH_OK;
+}
+
+extern "C" plsh_status plsh_kernel_timer_read(int32_t *launches, double *total_ms) {
+  static const char *who = "plsh_kernel_timer_read";
+  clear_error();
+  if (!launches || !total_ms) return fail(PLSH_ERR_ARG, "%s: null pointer argument", who);
+  double sum = 0.0;
+  for (size_t i = 0; i < g_timer.used; ++i) {
+    float ms = 0.f;
+    const auto &pr = g_timer.ev[i];
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      g_timer.used = 0;
+      return fail(PLSH_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
+    }
+    sum += ms;
+  }
+  *launches = (int32_t)g_timer.used;
+  *total_ms = sum;
+  g_timer.used = 0;
+  return PLSH_OK;
 }

@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "PLSH_OK", 1: "PLSH_ERR_ARG", 2: "PLSH_ERR_TABLE", 3: "PLSH_E
 
 EXPORTED = ["plsh_sample_tables", "plsh_validate_tables", "plsh_count_work",
             "plsh_alibi_attention", "plsh_debug_block_intervals",
-            "plsh_debug_attention_reference", "plsh_last_error"]
+            "plsh_debug_attention_reference", "plsh_kernel_timer",
+            "plsh_kernel_timer_read", "plsh_last_error"]
 
 
 class PlshError(RuntimeError):
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.plsh_alibi_attention.argtypes = attn
         L.plsh_debug_attention_reference.argtypes = attn
         L.plsh_debug_block_intervals.argtypes = [TP, vp, vp]
+        L.plsh_kernel_timer.argtypes = [i32]
+        L.plsh_kernel_timer_read.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]
         for f in EXPORTED[:-1]:
             getattr(L, f).restype = ctypes.c_int
         L.plsh_last_error.restype = ctypes.c_char_p
@@ -196,3 +199,16 @@ def debug_block_intervals(tables: DeviceTables, stream: Optional[int] = None) ->
     st = tables.c_struct()
     _check(lib().plsh_debug_block_intervals(ctypes.byref(st), lohi.data_ptr(), stream))
     return lohi
+
+
+def kernel_timer(enable: bool) -> None:
+    """plsh_kernel_timer: time the attention kernel of this thread's calls."""
+    _check(lib().plsh_kernel_timer(int(bool(enable))))
+
+
+def kernel_timer_read():
+    """plsh_kernel_timer_read -> (launches, total_ms) since the last read."""
+    n = ctypes.c_int32(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib().plsh_kernel_timer_read(ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

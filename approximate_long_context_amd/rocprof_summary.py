@@ -1,0 +1,142 @@
+"""Summaries of rocprofv3 output for the measurement record.
+
+    python -m approximate_long_context_amd.rocprof_summary stats \\
+        --csv DIR/..._kernel_stats.csv --command "..." --out profiles/NAME.md
+
+writes the per-kernel duration table of a `rocprofv3 --kernel-trace --stats`
+run (with the command that produced it) as markdown.
+
+    python -m approximate_long_context_amd.rocprof_summary traffic \\
+        --fetch DIR --write DIR --calib-fetch DIR --calib-write DIR \\
+        --calib-bytes N --kernel attn_mfma_kernel --workload NAME \\
+        --kernel-sha SHA --algorithmic-bytes B --commands FILE \\
+        --out-md profiles/NAME.md --out-json profiles/traffic.json
+
+turns two counter runs of the benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per
+dispatch) into HBM bytes per launch of the named kernel.  Each counter is
+scaled by what it reads for a plain copy of known size (`bench.py
+--copy-calibration`), which reads and writes exactly N bytes.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+import sys
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        sys.exit(f"no file matches {pattern}")
+    return hits[0]
+
+
+def kernel_stats_md(csv_path: str, command: str) -> str:
+    rows = list(csv.DictReader(open(csv_path)))
+    out = ["| kernel | calls | average (us) | min (us) | max (us) | share (%) |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("|", "\\|")
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.2f} |")
+    return "Command:\n\n```\n" + command + "\n```\n\n" + "\n".join(out) + "\n"
+
+
+def counter_per_dispatch(run_dir: str, counter: str, kernel_substr: str, largest: bool = False):
+    """Mean value of `counter` per dispatch of kernels whose name contains
+    kernel_substr (largest=True: only the dispatches with the largest value,
+    i.e. the calibration copies rather than small incidental copies)."""
+    path = _one(os.path.join(run_dir, "**", "*counter_collection.csv"))
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter or kernel_substr not in r["Kernel_Name"]:
+            continue
+        key = r["Dispatch_Id"]
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        sys.exit(f"{path}: no {counter} for kernels matching {kernel_substr!r}")
+    vals = list(per.values())
+    if largest:
+        top = max(vals)
+        vals = [v for v in vals if v >= 0.99 * top]
+    return statistics.mean(vals), len(vals)
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("--csv", required=True)
+    a.add_argument("--command", required=True)
+    a.add_argument("--out", required=True)
+    a.add_argument("--title", default="rocprofv3 kernel trace")
+    t = sub.add_parser("traffic")
+    for f in ("fetch", "write", "calib_fetch", "calib_write"):
+        t.add_argument("--" + f.replace("_", "-"), required=True)
+    t.add_argument("--calib-bytes", type=int, required=True)
+    t.add_argument("--calib-kernel", default="copyBuffer")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--kernel-sha", required=True)
+    t.add_argument("--algorithmic-bytes", type=float, required=True)
+    t.add_argument("--commands", required=True, help="text file with the commands of the four runs")
+    t.add_argument("--out-md", required=True)
+    t.add_argument("--out-json", required=True)
+    args = ap.parse_args(argv)
+
+    if args.cmd == "stats":
+        path = _one(args.csv)
+        md = f"# {args.title}\n\n" + kernel_stats_md(path, args.command)
+        open(args.out, "w").write(md)
+        print(md)
+        return
+
+    fetch_kib, nf = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
+    write_kib, nw = counter_per_dispatch(args.write, "WRITE_SIZE", args.kernel)
+    cf_kib, ncf = counter_per_dispatch(args.calib_fetch, "FETCH_SIZE", args.calib_kernel, largest=True)
+    cw_kib, ncw = counter_per_dispatch(args.calib_write, "WRITE_SIZE", args.calib_kernel, largest=True)
+    f_fetch = args.calib_bytes / (cf_kib * 1024.0)
+    f_write = args.calib_bytes / (cw_kib * 1024.0)
+    read_b = fetch_kib * 1024.0 * f_fetch
+    write_b = write_kib * 1024.0 * f_write
+    total = read_b + write_b
+    rec = {"kernel": args.kernel, "kernel_sha": args.kernel_sha,
+           "bytes_per_launch": total, "read_bytes": read_b, "write_bytes": write_b,
+           "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
+           "dispatches": [nf, nw],
+           "calibration": {"bytes": args.calib_bytes, "fetch_kib": cf_kib, "write_kib": cw_kib,
+                           "fetch_scale": f_fetch, "write_scale": f_write},
+           "algorithmic_bytes": args.algorithmic_bytes,
+           "traffic_over_algorithmic": total / args.algorithmic_bytes}
+    try:
+        allrec = json.load(open(args.out_json))
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[args.workload] = rec
+    json.dump(allrec, open(args.out_json, "w"), indent=1, sort_keys=True)
+    cmds = open(args.commands).read().strip()
+    md = (f"# HBM traffic of `{args.kernel}` on {args.workload}\n\n"
+          f"Commands (FETCH_SIZE and WRITE_SIZE passes of the benchmark, then of the copy "
+          f"calibration):\n\n```\n{cmds}\n```\n\n"
+          f"| quantity | value |\n|---|---|\n"
+          f"| FETCH_SIZE per dispatch (KiB) | {fetch_kib:.1f} ({nf} dispatches) |\n"
+          f"| WRITE_SIZE per dispatch (KiB) | {write_kib:.1f} ({nw} dispatches) |\n"
+          f"| copy of {args.calib_bytes} B: FETCH_SIZE / WRITE_SIZE (KiB) | {cf_kib:.1f} / {cw_kib:.1f} |\n"
+          f"| scale factors (fetch, write) | {f_fetch:.4f}, {f_write:.4f} |\n"
+          f"| HBM bytes read / written per launch | {read_b / 1e6:.2f} MB / {write_b / 1e6:.2f} MB |\n"
+          f"| traffic per launch | {total / 1e6:.2f} MB |\n"
+          f"| algorithmic bytes per launch | {args.algorithmic_bytes / 1e6:.2f} MB |\n"
+          f"| traffic / algorithmic | {total / args.algorithmic_bytes:.3f} |\n"
+          f"| kernel source sha256[:16] | `{args.kernel_sha}` |\n")
+    open(args.out_md, "w").write(md)
+    print(md)
+
+
+if __name__ == "__main__":
+    main()

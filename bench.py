@@ -7,6 +7,12 @@ QK^T, weighted online softmax, PV, normalisation: one library call) over one
 batch of seeded synthetic inputs already resident in HBM, with the hash
 tables (drawn and built on the host once, timed separately) resident too.
 Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py --copy-calibration MIB
+
+runs a plain device-to-device copy of MIB MiB a few times instead (the known
+byte count against which the HBM byte counters are scaled) and prints one
+JSON line describing it.
 """
 
 from __future__ import annotations
@@ -35,8 +41,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def copy_calibration(mib: int) -> None:
+    """A plain copy kernel of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    dev = torch.device("cuda:0")
+    nbytes = mib << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    reps = 5
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": True, "bytes_read_per_copy": nbytes,
+                      "bytes_written_per_copy": nbytes, "copies": reps}), flush=True)
+
+
 def kernel_sha() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def kernel_name(w: W.Workload) -> str:
+    """The attention kernel the library dispatches for this workload."""
+    if w.dtype == "bf16" and w.s <= 124:
+        return f"attn_mfma_kernel<{w.d}, {'true' if w.causal else 'false'}>"
+    return f"attn_valu_kernel<{'uint16_t' if w.dtype == 'bf16' else 'float'}, {w.d}>"
 
 
 def measured_traffic(workload: str):
@@ -89,6 +117,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--error-rows", type=int, default=16)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus above 1 is not supported "
@@ -96,6 +125,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     dev = torch.device("cuda:0")
     w = W.get(args.workload)
     log(f"[bench] workload {w.name}: {w.describe()}")
@@ -118,13 +150,18 @@ def main():
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    plsh.kernel_timer(True)   # HIP events around the attention kernel of every call
     e0.record(stream)
     for _ in range(args.steps):
         plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step")
+    launches, kernel_ms_total = plsh.kernel_timer_read()
+    plsh.kernel_timer(False)
+    assert launches == args.steps, (launches, args.steps)
+    kernel_ms = kernel_ms_total / launches
+    log(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step, attention kernel {kernel_ms:.4f} ms")
 
     B, H, Hkv, n, d, s = w.batch, w.heads, w.kv_heads, w.n, w.d, w.s
     sec = ms / 1e3
@@ -132,7 +169,7 @@ def main():
     f_distinct = 4.0 * d * B * pairs_distinct
     f_alg = 4.0 * d * B * pairs_alg
     bytes_min = w.esz * B * n * d * (2 * H + 2 * Hkv)
-    ach_gbs = bytes_min / sec / 1e9
+    ach_gbs = bytes_min / (kernel_ms / 1e3) / 1e9  # the attention kernel alone
     useful_tflops = f_distinct / sec / 1e12
     traffic = measured_traffic(w.name)
 
@@ -178,9 +215,11 @@ def main():
         "pairs_alg": B * pairs_alg,
         "roofline": {"bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": ach_gbs / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "attn_mfma_kernel<128, true>" if d == 128 and w.causal else "attn kernel",
+                     "kernel": kernel_name(w),
+                     "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": bytes_min,
-                     "arith_intensity_flop_per_byte": f_distinct / bytes_min},
+                     "arith_intensity_flop_per_byte": f_distinct / bytes_min,
+                     "useful_tflops_in_kernel": f_distinct / (kernel_ms / 1e3) / 1e12},
         "cpu_baseline": cpu,
         "host_sample_ms": host_sample_ms,
         "parity_sampled_rows_max_abs": parity,

@@ -29,7 +29,8 @@
  *     even, from the stream-ordered allocator (hipMallocAsync on `stream`) and
  *     releases it on the same stream (hipFreeAsync) within the call; no other
  *     entry point allocates device memory.
- *   - The library keeps no state besides a thread-local error string.
+ *   - The library keeps no state besides a thread-local error string and the
+ *     thread-local kernel timer below.
  */
 #ifndef PLSH_H
 #define PLSH_H
@@ -171,6 +172,24 @@ plsh_status plsh_alibi_attention(const void *q, const void *k, const void *v, vo
  */
 plsh_status plsh_debug_block_intervals(const plsh_tables *boundaries, int32_t *lohi,
                                        plsh_stream_t stream);
+
+/*
+ * plsh_kernel_timer -- measurement aid (no part of the method).  With
+ * enable != 0, every later plsh_alibi_attention / plsh_debug_attention_reference
+ * call of this thread records a pair of HIP events on its stream immediately
+ * before and after its attention kernel (the block-edge pre-pass is outside
+ * the pair); enable == 0 stops recording.  Either call discards pairs not yet
+ * read.  The events are created on first use and kept for reuse by the thread.
+ */
+plsh_status plsh_kernel_timer(int32_t enable);
+
+/*
+ * plsh_kernel_timer_read -- waits for the recorded pairs of this thread,
+ * writes their number to *launches and the summed elapsed time (ms) to
+ * *total_ms, and discards them.  PLSH_ERR_ARG on null pointers, PLSH_ERR_HIP
+ * if an event cannot be read.
+ */
+plsh_status plsh_kernel_timer_read(int32_t *launches, double *total_ms);
 
 /* Thread-local, NUL-terminated description of the last non-OK status of this
  * thread ("" if none).  Valid until the thread's next plsh_* call. */

@@ -268,3 +268,21 @@ def test_error_after_bad_call_leaves_no_work(dev):
     with pytest.raises(plsh.PlshError) as e:
         plsh.attention(q.to(dev), k.to(dev), v.to(dev), w.sigma, w.s + 1, t, causal=True)
     assert e.value.status == plsh.PLSH_ERR_TABLE
+
+
+def test_kernel_timer_counts_attention_launches(dev):
+    w = small("timer", 1, 2, 1, 300, 128, "bf16", True, [2.0, 40.0], 5)
+    say("kernel timer", w.describe())
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(0, w.n, w.sigma, w.s).to(dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    plsh.kernel_timer(True)
+    try:
+        for _ in range(3):
+            plsh.attention(qd, kd, vd, w.sigma, w.s, t, causal=True)
+        launches, ms = plsh.kernel_timer_read()
+    finally:
+        plsh.kernel_timer(False)
+    assert launches == 3 and ms > 0.0
+    plsh.attention(qd, kd, vd, w.sigma, w.s, t, causal=True)
+    assert plsh.kernel_timer_read() == (0, 0.0)

@@ -193,3 +193,17 @@ def test_attention_without_device_reports_hip_error():
         pytest.skip("a GPU is present")
     st, msg = _call()
     assert st == plsh.PLSH_ERR_HIP, msg
+
+
+def test_kernel_timer_without_launches():
+    plsh.kernel_timer(True)
+    assert plsh.kernel_timer_read() == (0, 0.0)
+    plsh.kernel_timer(False)
+    assert plsh.kernel_timer_read() == (0, 0.0)
+
+
+def test_kernel_timer_read_rejects_null_pointers():
+    import ctypes
+    n = ctypes.c_int32(0)
+    assert plsh.lib().plsh_kernel_timer_read(None, None) == plsh.PLSH_ERR_ARG
+    assert plsh.lib().plsh_kernel_timer_read(ctypes.byref(n), None) == plsh.PLSH_ERR_ARG
