@@ -172,17 +172,26 @@ __device__ void wave_masks(int n, int r0, int lane, int nact, const WaveTab &w) 
   const int last = min(r0 + 31, n - 1);
   const int t = lane & 31, hh = lane >> 5;
   const int x = r0 + t;
+  for (int c0 = 0; c0 < nact; c0 += 64) {
+    // the chunk's listed samples, one per lane, so that the loop below takes
+    // its operands from registers instead of dependent LDS reads
+    const int kc = c0 + lane < nact ? w.act[c0 + lane] : 0;
+    const double dlc = w.prm[2 * kc], uc = w.prm[2 * kc + 1];
+    const int m = min(64, nact - c0);
 #pragma unroll 2
-  for (int a0 = 0; a0 < nact; a0 += 2) {
-    const int ai = a0 + hh;
-    const bool have = ai < nact;
-    const int k = have ? w.act[ai] : 0;
-    const bool valid = have && x <= last;
-    double b = 0.0;
-    if (valid) b = bin_of(x, w.prm[2 * k], w.prm[2 * k + 1]);
-    const double bp = __shfl_up(b, 1, 32);
-    const uint64_t bal = __ballot(valid && t > 0 && b != bp);
-    if (t == 0 && have) w.mask[k] = (uint32_t)(bal >> (32 * hh));
+    for (int a0 = 0; a0 < m; a0 += 2) {
+      // half-wave hh takes listed sample c0 + a0 + hh
+      const int src = min(a0 + hh, m - 1);
+      const int k = __shfl(kc, src);
+      const double dl = __shfl(dlc, src), u = __shfl(uc, src);
+      const bool have = a0 + hh < m;
+      const bool valid = have && x <= last;
+      double b = 0.0;
+      if (valid) b = bin_of(x, dl, u);
+      const double bp = __shfl_up(b, 1, 32);
+      const uint64_t bal = __ballot(valid && t > 0 && b != bp);
+      if (t == 0 && have) w.mask[k] = (uint32_t)(bal >> (32 * hh));
+    }
   }
 }
 
