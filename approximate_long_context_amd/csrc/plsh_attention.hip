@@ -385,7 +385,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
 //   V operand (8-byte transposing reads): 32 lanes read chunks 2j, 2j + 1 of
 //     8 consecutive keys: swz_key sends those keys to distinct chunk pairs.
 constexpr int kTileKeys = 32;
-constexpr int kRing = 4;
+constexpr int kRing = 4;  // (the tile loop below is written for 4 slots)
+template <int Q>
+struct SlotC {
+  static constexpr int value = Q;
+};
 constexpr int kWaves = 8;  // waves per workgroup, 16 query rows each
 
 template <int D>
@@ -411,13 +415,17 @@ __device__ __forceinline__ uint32_t swz(int key, int c) {
   return (uint32_t)(key * D * 2 + ((c ^ swz_key<D>(key)) << 4));
 }
 
-// Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16 l (lds_base wave-uniform).  Issued as inline assembly so that
+// LDS address of a pointer into LDS (the generic-to-LDS cast; on static
+// shared variables it folds to a constant)
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_void_t *)p; }
+
+// Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at LDS
+// address lds_base + 16 l (lds_base wave-uniform).  Issued as inline assembly so that
 // the ring's only ordering is the explicit vmcnt wait + barrier of each stage
 // (the compiler would otherwise wait for every outstanding copy before any
 // LDS read, since it cannot tell which ring stage a copy targets).
-__device__ __forceinline__ void dma16(const void *gsrc, const void *lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds_base);
+__device__ __forceinline__ void dma16(const void *gsrc, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gsrc), "s"(m0)
@@ -688,10 +696,10 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   u32x2 *evt = evl + ev_count(s);
   if (active && half == 0) {
     for (int c0 = 0; c0 < nch; c0 += 64)
-      if (c0 + lane < nch) dma16(rec + rec_evl_off() + 16 * (c0 + lane), evl + 2 * c0);
+      if (c0 + lane < nch) dma16(rec + rec_evl_off() + 16 * (c0 + lane), lds_addr(evl + 2 * c0));
     if (!CAUSAL)
       for (int c0 = 0; c0 < nch; c0 += 64)
-        if (c0 + lane < nch) dma16(rec + rec_evt_off(s) + 16 * (c0 + lane), evt + 2 * c0);
+        if (c0 + lane < nch) dma16(rec + rec_evt_off(s) + 16 * (c0 + lane), lds_addr(evt + 2 * c0));
   }
 
   // ---- K/V staging: a tile is 32 rows of D / 8 chunks, 4 D chunks per
@@ -701,23 +709,23 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   constexpr int CPW = 4 * D / kWaves;   // chunks per wave, stage and matrix (<= 64)
   constexpr int LPS = 2;                // loads per thread per stage (K and V)
   const char *Kb = (const char *)K, *Vb = (const char *)V;
-  auto issue_stage = [&](int st) {
-    const int q = st % kRing;
-    const int jt = U0 + kTileKeys * st;
+  // the lane's chunk of every stage: row dkey of the tile, 16 bytes at dofs
+  const int dslot = wave * CPW + lane;
+  const int dkey = dslot / CPR;
+  const int dofs = 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
+  const uint32_t kv_lds = lds_addr(&lds.kv[0][0][0]) + wave * CPW * 16;
+  auto issue_stage = [&](int st, int q) {  // q = st % kRing
     if (lane < CPW) {
-      const int slot = wave * CPW + lane;
-      const int key = slot / CPR, pos = slot % CPR;
-      const int c = pos ^ swz_key<D>(key);
-      const int64_t off = ((int64_t)min(jt + key, n - 1) * D + 8 * c) * 2;
-      dma16(Kb + off, lds.kv[q][0] + wave * CPW * 8);
-      dma16(Vb + off, lds.kv[q][1] + wave * CPW * 8);
+      const int64_t off = (int64_t)min(U0 + kTileKeys * st + dkey, n - 1) * (2 * D) + dofs;
+      dma16(Kb + off, kv_lds + (uint32_t)(2 * q) * (kTileKeys * D * 2));
+      dma16(Vb + off, kv_lds + (uint32_t)(2 * q + 1) * (kTileKeys * D * 2));
     }
   };
   // stages 0 .. kRing - 2 now; iteration st of the tile loop issues stage
   // st + kRing - 1
 #pragma unroll
   for (int pst = 0; pst < kRing - 1; ++pst)
-    if (pst < nst) issue_stage(pst);
+    if (pst < nst) issue_stage(pst, pst);
 
   // ---- running state
   constexpr int NDB = D / 16;  // 16-dim blocks of O^T
@@ -729,6 +737,8 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   int base = 0;          // the row's multiplicity just before the current tile
   int lp = 0, tp = 0;    // next unconsumed lead / trail edge
   int pl = 0, pt = 0;    // their positions (wave-uniform)
+  int lg_base = -1;      // the count whose log2 is lg
+  float lg = 0.f;
   // edge positions read at a wave-uniform index are wave-uniform
   auto pos_at = [&](const u32x2 *ev, int i) { return (int32_t)__builtin_amdgcn_readfirstlane(ev[i][0]); };
   // K operand: key 16 b + qc, chunk 4 c + gq; b = 1 lies 16 rows further
@@ -751,8 +761,10 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
 
   // a5: S^T = K Q^T for the tile of stage st, keys 16 b + 4 gq + r
   floatx4 sacc[2];
-  auto qk_tile = [&](int st) {
-    const char *kt = (const char *)lds.kv[st % kRing][0];
+  // (the ring slot is a compile-time constant, so that LDS operand offsets
+  // become immediates of the reads)
+  auto qk_tile = [&](auto slotc) {
+    const char *kt = (const char *)lds.kv[decltype(slotc)::value][0];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       u32x4 kr[NC];
@@ -782,8 +794,8 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   };
 
   // a4, a6, a7 for the tile of stage st, whose logits are in sacc
-  auto finish_tile = [&](int st) {
-    const char *vt = (const char *)lds.kv[st % kRing][1];
+  auto finish_tile = [&](int st, auto slotc) {
+    const char *vt = (const char *)lds.kv[decltype(slotc)::value][1];
     const int j0 = U0 + kTileKeys * st;
 
     // a4: multiplicity c for keys j0 + 16 b + 4 gq + r.
@@ -845,10 +857,13 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     // rare).  A tile with one count per row folds log2(c) into the exponent
     // bias; otherwise P = c * 2^(...).  P is rounded to bf16 in pairs and the
     // row sum adds exactly the rounded weights that enter PV.
-    float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-    mx = fmaxf(mx, xor16_f(mx));
-    mx = fmaxf(mx, other_half_f(mx, lane)) * kLog2e;
+    // (med3(x, y, +inf) = max(x, y) for the finite logits, one instruction
+    // without the NaN canonicalisation fmaxf needs)
+    auto mx2 = [](float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); };
+    float mx = mx2(mx2(mx2(sacc[0][0], sacc[0][1]), mx2(sacc[0][2], sacc[0][3])),
+                   mx2(mx2(sacc[1][0], sacc[1][1]), mx2(sacc[1][2], sacc[1][3])));
+    mx = mx2(mx, xor16_f(mx));
+    mx = mx2(mx, other_half_f(mx, lane)) * kLog2e;
     const bool need = mx > m2 + 8.0f;
     if (__any(need)) {
       const float mnew = need ? mx : m2;
@@ -861,7 +876,11 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     u32x4 pw;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     if (__builtin_amdgcn_readfirstlane(kind) == 0) {
-      const float bias = m2 - __builtin_amdgcn_logf(cf[0]);  // c = 0 gives bias = +inf, P = 0
+      if (__any(base != lg_base)) {  // log2 of the running count, recomputed when it changes
+        lg = __builtin_amdgcn_logf(cf[0]);
+        lg_base = base;
+      }
+      const float bias = m2 - lg;  // c = 0 gives bias = +inf, P = 0
 #pragma unroll
       for (int r = 0; r < 8; r += 2) {
         const floatx2 pf = {__builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][r & 3], kLog2e, -bias)),
@@ -903,7 +922,8 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     }
   };
 
-  for (int st = 0; st < nst; ++st) {
+  auto stage = [&](int st, auto slotc) {
+    constexpr int Qs = decltype(slotc)::value;  // st % kRing
     // this thread's loads of stage st are done once at most those of the
     // (up to two) later stages already issued are outstanding
     const int ahead = min(kRing - 2, nst - 1 - st);
@@ -913,15 +933,23 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();  // every wave's loads of stage st landed; stage st - 1 is consumed
     asm volatile("" ::: "memory");
-    if (st + kRing - 1 < nst) issue_stage(st + kRing - 1);  // into the ring slot of stage st - 1
+    if (st + kRing - 1 < nst) issue_stage(st + kRing - 1, (Qs + kRing - 1) % kRing);  // ring slot of stage st - 1
     if (st == 0 && active) {  // the edge lists landed with stage 0
       pl = pos_at(evl, 0);
       if (!CAUSAL) pt = pos_at(evt, 0);
     }
     if (st >= sa && st < sb) {
-      qk_tile(st);
-      finish_tile(st);
+      qk_tile(slotc);
+      finish_tile(st, slotc);
     }
+  };
+  // the loop runs kRing stages per iteration so that each stage's ring slot
+  // is a constant
+  for (int st0 = 0; st0 < nst; st0 += kRing) {
+    stage(st0, SlotC<0>{});
+    if (st0 + 1 < nst) stage(st0 + 1, SlotC<1>{});
+    if (st0 + 2 < nst) stage(st0 + 2, SlotC<2>{});
+    if (st0 + 3 < nst) stage(st0 + 3, SlotC<3>{});
   }
 
   // a8: normalisation epilogue, one store per output element; the row sum
