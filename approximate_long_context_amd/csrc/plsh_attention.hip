@@ -374,7 +374,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
 // LDS and matrix-core latency.
 // ---------------------------------------------------------------------------
 // K and V stream through a ring of kRing stages of 32 keys each, filled by
-// direct global->LDS loads issued kRing - 1 stages ahead.  Rows are stored
+// direct global->LDS loads issued one pair of stages ahead.  Rows are stored
 // whole (D bf16) with their 16-byte chunks XOR-swizzled by swz_key<D>(key) so
 // that both operand reads are free of bank conflicts.  The LDS has 64 banks
 // of 4 bytes, so 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read,
@@ -721,11 +721,9 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
       dma16(Vb + off, kv_lds + (uint32_t)(2 * q + 1) * (kTileKeys * D * 2));
     }
   };
-  // stages 0 .. kRing - 2 now; iteration st of the tile loop issues stage
-  // st + kRing - 1
-#pragma unroll
-  for (int pst = 0; pst < kRing - 1; ++pst)
-    if (pst < nst) issue_stage(pst, pst);
+  // stages 0 and 1 now; the pair starting at stage st issues st + 2, st + 3
+  if (nst > 0) issue_stage(0, 0);
+  if (nst > 1) issue_stage(1, 1);
 
   // ---- running state
   constexpr int NDB = D / 16;  // 16-dim blocks of O^T
@@ -862,10 +860,12 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     auto mx2 = [](float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); };
     float mx = mx2(mx2(mx2(sacc[0][0], sacc[0][1]), mx2(sacc[0][2], sacc[0][3])),
                    mx2(mx2(sacc[1][0], sacc[1][1]), mx2(sacc[1][2], sacc[1][3])));
-    mx = mx2(mx, xor16_f(mx));
-    mx = mx2(mx, other_half_f(mx, lane)) * kLog2e;
-    const bool need = mx > m2 + 8.0f;
-    if (__any(need)) {
+    // the lane's own maximum decides whether any rescale is due; only then
+    // is it combined over the four lanes of each query
+    if (__any(mx * kLog2e > m2 + 8.0f)) {
+      mx = mx2(mx, xor16_f(mx));
+      mx = mx2(mx, other_half_f(mx, lane)) * kLog2e;
+      const bool need = mx > m2 + 8.0f;
       const float mnew = need ? mx : m2;
       const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
       lsum *= alpha;
@@ -922,34 +922,34 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     }
   };
 
-  auto stage = [&](int st, auto slotc) {
-    constexpr int Qs = decltype(slotc)::value;  // st % kRing
-    // this thread's loads of stage st are done once at most those of the
-    // (up to two) later stages already issued are outstanding
-    const int ahead = min(kRing - 2, nst - 1 - st);
-    if (ahead >= 2) PLSH_WAIT_VM_LGKM0(2 * LPS);
-    else if (ahead == 1) PLSH_WAIT_VM_LGKM0(LPS);
-    else PLSH_WAIT_VM_LGKM0(0);
+  // Two stages per barrier (measured: the barrier, where every wave waits for
+  // the slowest, costs more than the shorter look-ahead): the pair starting at
+  // stage st waits for stages st, st + 1, then refills the ring slots of
+  // stages st - 2, st - 1 (consumed by every wave before the barrier) with
+  // stages st + 2, st + 3, and computes its two tiles.
+  auto pair = [&](int st, auto s0, auto s1) {
+    PLSH_WAIT_VM_LGKM0(0);
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // every wave's loads of stage st landed; stage st - 1 is consumed
+    __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (st + kRing - 1 < nst) issue_stage(st + kRing - 1, (Qs + kRing - 1) % kRing);  // ring slot of stage st - 1
+    if (st + 2 < nst) issue_stage(st + 2, (decltype(s0)::value + 2) % kRing);
+    if (st + 3 < nst) issue_stage(st + 3, (decltype(s1)::value + 2) % kRing);
     if (st == 0 && active) {  // the edge lists landed with stage 0
       pl = pos_at(evl, 0);
       if (!CAUSAL) pt = pos_at(evt, 0);
     }
     if (st >= sa && st < sb) {
-      qk_tile(slotc);
-      finish_tile(st, slotc);
+      qk_tile(s0);
+      finish_tile(st, s0);
+    }
+    if (st + 1 < nst && st + 1 >= sa && st + 1 < sb) {
+      qk_tile(s1);
+      finish_tile(st + 1, s1);
     }
   };
-  // the loop runs kRing stages per iteration so that each stage's ring slot
-  // is a constant
   for (int st0 = 0; st0 < nst; st0 += kRing) {
-    stage(st0, SlotC<0>{});
-    if (st0 + 1 < nst) stage(st0 + 1, SlotC<1>{});
-    if (st0 + 2 < nst) stage(st0 + 2, SlotC<2>{});
-    if (st0 + 3 < nst) stage(st0 + 3, SlotC<3>{});
+    pair(st0, SlotC<0>{}, SlotC<1>{});
+    if (st0 + 2 < nst) pair(st0 + 2, SlotC<2>{}, SlotC<3>{});
   }
 
   // a8: normalisation epilogue, one store per output element; the row sum

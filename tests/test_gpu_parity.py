@@ -246,6 +246,25 @@ def test_g6_batch_slice_and_determinism(dev):
     assert torch.equal(full[1:2], one)
 
 
+@pytest.mark.parametrize("wname,causal,d", [("mistral-7b-n16384-s20", True, 128),
+                                             ("qwen3-0.6b-n8192-s20", False, 64)])
+def test_full_size_repeats_bitwise(dev, wname, causal, d):
+    """Repeated full-size launches give identical bits: the K/V ring hands a
+    slot to the next copy only after every wave is done with it, so no read
+    can see a later stage's data (such a race shows as run-to-run noise)."""
+    import dataclasses
+    w = dataclasses.replace(W.get(wname), causal=causal, d=d)
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(w.hash_seed, w.n, w.sigma, w.s).to(dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    say(w.name, "repeats", "causal", causal, "d", d)
+    first = plsh.attention(qd, kd, vd, w.sigma, w.s, t, causal=causal)
+    for _ in range(5):
+        again = plsh.attention(qd, kd, vd, w.sigma, w.s, t, causal=causal)
+        assert torch.equal(first, again)
+    assert bool(torch.isfinite(first).all())
+
+
 # ------------------------------------------------------------------- G7 ---
 @pytest.mark.parametrize("causal", [False, True])
 def test_g7_huge_sigma_is_softmax_attention(dev, causal):
