@@ -372,6 +372,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
 // Output O = acc / l is written once, rounded to bf16.  16-row waves keep a
 // wave near 128 VGPRs, so four waves share each SIMD and cover each other's
 // LDS and matrix-core latency.
+// Q and O pass through LDS (ring slots that are free at the time) so that
+// every global access instruction covers whole rows: the address unit's time
+// grows with the number of 64-byte segments each group of four lanes touches,
+// and a row per lane (the MFMA operand layout) touches four per group, which
+// measured as the kernel's dominant address-unit cost.
 // ---------------------------------------------------------------------------
 // K and V stream through a ring of kRing stages of 32 keys each, filled by
 // direct global->LDS loads issued one pair of stages ahead.  Rows are stored
@@ -643,9 +648,7 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   uint16_t *O = (uint16_t *)a.out + ((int64_t)b * a.heads + h) * n * D;
 
   // ---- the four groups' key ranges first (the K/V copies need them), then
-  // the Q fragment (B operand of S^T = K Q^T: query r0 + qc, dims 32 c +
-  // 8 gq + e) and the row's diagonal-tile multiplicities, which are first
-  // needed after the first stage's wait and so overlap the first copies
+  // the row's diagonal-tile multiplicities
   int U0 = INT32_MAX, U1 = INT32_MIN, U0w = INT32_MAX, U1w = INT32_MIN;
   {
     // all four headers in one round trip: groups past the end re-read the
@@ -662,16 +665,9 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     }
   }
   constexpr int NC = D / 32;
+  // the Q fragment (B operand of S^T = K Q^T: query r0 + qc, dims 32 c +
+  // 8 gq + e), read from LDS after the first wait (see below)
   bf16x8 qf[NC];
-  {
-    const int i = r0 + qc;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (active && i < n) raw = *(const u32x4 *)(Q + (int64_t)i * D + 32 * c + 8 * gq);
-      qf[c] = __builtin_bit_cast(bf16x8, raw);
-    }
-  }
   // bytes c(t32, 16 b + 4 gq + r), and (non-causal) c(t32, 31)
   uint32_t dg[2] = {0u, 0u};
   int dlast = 0;
@@ -700,6 +696,22 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     if (!CAUSAL)
       for (int c0 = 0; c0 < nch; c0 += 64)
         if (c0 + lane < nch) dma16(rec + rec_evt_off(s) + 16 * (c0 + lane), lds_addr(evt + 2 * c0));
+  }
+
+  // ---- the wave's 16 query rows go to ring slots 2 and 3 (free until the
+  // first pair has read them) in the swizzled layout of a K tile, so that
+  // every copy instruction reads whole rows and the fragment reads are free of
+  // bank conflicts (whole rows per instruction keep the address unit's work
+  // per byte low; a row per lane would touch 16 rows per instruction)
+  constexpr int CPR_Q = D / 8;  // 16-byte chunks per row
+  const uint32_t q_lds = lds_addr(&lds.kv[2][0][0]) + wave * 32 * D;
+  if (active) {
+#pragma unroll
+    for (int c0 = 0; c0 < 16 * CPR_Q; c0 += 64) {
+      const int row = (c0 + lane) / CPR_Q, ch = (c0 + lane) % CPR_Q;
+      const int64_t off = (int64_t)min(r0 + row, n - 1) * (2 * D) + 16 * (ch ^ swz_key<D>(row));
+      dma16((const char *)Q + off, q_lds + 16 * c0);
+    }
   }
 
   // ---- K/V staging: a tile is 32 rows of D / 8 chunks, 4 D chunks per
@@ -932,6 +944,17 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    if (st == 0) {
+      // the Q fragment from the wave's staged rows, then a barrier: every wave
+      // has its fragment before slots 2, 3 take stages 2, 3
+      const char *qt = (const char *)lds.kv[2][0] + wave * 32 * D;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qt + swz<D>(qc, 4 * c + gq)));
+      PLSH_WAIT_VM_LGKM0(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
     if (st + 2 < nst) issue_stage(st + 2, (decltype(s0)::value + 2) % kRing);
     if (st + 3 < nst) issue_stage(st + 3, (decltype(s1)::value + 2) % kRing);
     if (st == 0 && active) {  // the edge lists landed with stage 0
@@ -954,18 +977,29 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
 
   // a8: normalisation epilogue, one store per output element; the row sum
   // is spread over the four lanes qc + 16 gq
+  // The wave's 16 x D output block is staged in LDS (in the two ring slots
+  // the last pair does not use: every wave is past them), then written whole
+  // rows per instruction.
   if (!active) return;
   float ltot = lsum + xor16_f(lsum);
   ltot += other_half_f(ltot, lane);
   const float inv = 1.0f / ltot;
-  const int i = r0 + qc;
-  if (i >= n) return;
-  uint16_t *orow = O + (int64_t)i * D + 4 * gq;
+  const int free_slot = (((nst - 1) >> 1) & 1) ? 0 : 2;
+  char *ob = (char *)lds.kv[free_slot][0] + wave * 32 * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const bf16x2 h0 = __builtin_convertvector((floatx2{oacc[db][0] * inv, oacc[db][1] * inv}), bf16x2);
     const bf16x2 h1 = __builtin_convertvector((floatx2{oacc[db][2] * inv, oacc[db][3] * inv}), bf16x2);
-    *(u32x2 *)(orow + 16 * db) = u32x2{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+    // row qc, dims 16 db + 4 gq .. + 3: half (gq & 1) of 16-byte chunk 2 db + gq / 2
+    *(u32x2 *)(ob + swz<D>(qc, 2 * db + (gq >> 1)) + 8 * (gq & 1)) =
+        u32x2{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+  }
+#pragma unroll
+  for (int c0 = 0; c0 < 16 * CPR_Q; c0 += 64) {
+    const int row = (c0 + lane) / CPR_Q, ch = (c0 + lane) % CPR_Q;
+    const u32x4 val = *(const u32x4 *)(ob + swz<D>(row, ch));
+    const int i = r0 + row;
+    if (i < n) *(u32x4 *)(O + (int64_t)i * D + 8 * ch) = val;
   }
 }
 
