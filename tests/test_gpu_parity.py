@@ -115,6 +115,25 @@ def test_g1_block_intervals_extreme_pitches(dev):
         assert np.array_equal(lohi[r, :, 0], lo) and np.array_equal(lohi[r, :, 1], hi), r
 
 
+def test_g1_block_intervals_integer_quotients(dev):
+    """Hashes where (x + u) / delta is an exact integer at many positions
+    (u = 0 with integer pitches, u = delta / 2 with even pitches) or lands
+    within a few ulp of one: the device's multiply-by-reciprocal bin with its
+    exact-division fallback reproduces the oracle's scan bit for bit."""
+    n = 4000
+    rows = []
+    for dl in (3.0, 5.0, 6.0, 7.0, 10.0, 49.0, 96.0, 2.5, 12.75, 0.1, 1.0 / 3.0, 1e-3):
+        for u in (0.0, dl / 2.0, dl * (1.0 - 2.0 ** -40), dl * 2.0 ** -45):
+            rows.append((dl, u))
+    params = np.array(rows, dtype=np.float64)
+    off, st = orc.tables_from_params(n, params)
+    t = plsh.Tables(n, 1, len(rows), params, off.astype(np.int32), st.astype(np.int32))
+    lohi = plsh.debug_block_intervals(t.to(dev)).cpu().numpy()
+    for r in range(len(rows)):
+        lo, hi = orc.block_intervals(n, st[off[r]:off[r + 1]])
+        assert np.array_equal(lohi[r, :, 0], lo) and np.array_equal(lohi[r, :, 1], hi), rows[r]
+
+
 def test_g1_block_intervals_512k_two_heads(dev):
     n = 524288
     s = W.long_context_s(n)
