@@ -25,8 +25,8 @@ STATUS_NAMES = {0: "PLSH_OK", 1: "PLSH_ERR_ARG", 2: "PLSH_ERR_TABLE", 3: "PLSH_E
 
 EXPORTED = ["plsh_sample_tables", "plsh_validate_tables", "plsh_count_work",
             "plsh_alibi_attention", "plsh_debug_block_intervals",
-            "plsh_debug_attention_reference", "plsh_kernel_timer",
-            "plsh_kernel_timer_read", "plsh_last_error"]
+            "plsh_debug_attention_reference", "plsh_exact_alibi_attention",
+            "plsh_kernel_timer", "plsh_kernel_timer_read", "plsh_last_error"]
 
 
 class PlshError(RuntimeError):
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.plsh_alibi_attention.argtypes = attn
         L.plsh_debug_attention_reference.argtypes = attn
         L.plsh_debug_block_intervals.argtypes = [TP, vp, vp]
+        L.plsh_exact_alibi_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                                 vp, i32, vp]
         L.plsh_kernel_timer.argtypes = [i32]
         L.plsh_kernel_timer_read.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]
         for f in EXPORTED[:-1]:
@@ -181,6 +183,29 @@ def attention(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
               out: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
     """plsh_alibi_attention on the current stream: q [B,H,n,d], k/v [B,Hkv,n,d]."""
     return _attention(lib().plsh_alibi_attention, q, k, v, sigma, s, tables, causal, out, stream)
+
+
+def exact_alibi_attention(q, k, v, sigma, causal: bool = False, out: Optional[torch.Tensor] = None,
+                          stream: Optional[int] = None) -> torch.Tensor:
+    """plsh_exact_alibi_attention (dense exact ALiBi, bf16) on the current
+    stream: q [B,H,n,d], k/v [B,Hkv,n,d]."""
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if not x.is_contiguous():
+            raise PlshError(PLSH_ERR_ARG, f"{name} must be contiguous")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise PlshError(PLSH_ERR_ARG, "q [B,H,n,d], k/v [B,Hkv,n,d] with one dtype expected")
+    B, H, n, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    sig = np.ascontiguousarray(sigma, dtype=np.float64)
+    if sig.size != H:
+        raise PlshError(PLSH_ERR_ARG, "sigma must have one entry per query head")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().plsh_exact_alibi_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, n,
+                                            H, k.shape[1], d, _dtype_code(q), _ptr(sig), int(bool(causal)),
+                                            stream))
+    return out
 
 
 def attention_reference(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,

@@ -13,6 +13,15 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 runs a plain device-to-device copy of MIB MiB a few times instead (the known
 byte count against which the HBM byte counters are scaled) and prints one
 JSON line describing it.
+
+    python bench.py --crossover
+
+times the estimator (one library call) against the dense exact-ALiBi kernel
+(plsh_exact_alibi_attention) on the Mistral-shaped workload for a range of
+sequence lengths and prints one JSON line per length.
+
+The default run also times the exact-ALiBi kernel once on the same inputs
+(outside the timed steps) and reports it as "exact_alibi_comparator".
 """
 
 from __future__ import annotations
@@ -54,6 +63,61 @@ def copy_calibration(mib: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": True, "bytes_read_per_copy": nbytes,
                       "bytes_written_per_copy": nbytes, "copies": reps}), flush=True)
+
+
+def dense_flops(w: W.Workload) -> float:
+    """QK^T and PV flops of exact attention: 4 d per (row, key) pair."""
+    pairs = w.n * (w.n + 1) / 2 if w.causal else float(w.n) * w.n
+    return 4.0 * w.d * w.batch * w.heads * pairs
+
+
+def time_calls(fn, reps: int):
+    """(ms per call by events around the calls, ms per attention kernel by the
+    library's kernel timer)."""
+    dev = torch.device("cuda:0")
+    fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    plsh.kernel_timer(True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    launches, total = plsh.kernel_timer_read()
+    plsh.kernel_timer(False)
+    assert launches == reps, (launches, reps)
+    return e0.elapsed_time(e1) / reps, total / launches
+
+
+def crossover() -> None:
+    """Estimator vs exact ALiBi over n on the Mistral-shaped workload."""
+    import dataclasses
+    dev = torch.device("cuda:0")
+    base = W.get("mistral-7b-n16384-s20")
+    for n in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
+        w = dataclasses.replace(base, n=n, name=f"mistral-shape-n{n}-s{base.s}")
+        q, k, v = W.make_qkv(w)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        dt = plsh.sample_tables(w.hash_seed, n, w.sigma, w.s).to(dev)
+        out = torch.empty_like(qd)
+        reps_lsh = 20
+        reps_exact = max(2, min(20, int(2e8 // (n * n))))
+        lsh_ms, lsh_kernel_ms = time_calls(
+            lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out), reps_lsh)
+        ex_ms, ex_kernel_ms = time_calls(
+            lambda: plsh.exact_alibi_attention(qd, kd, vd, w.sigma, causal=w.causal, out=out), reps_exact)
+        rec = {"crossover": True, "workload": w.name, "n": n, "lsh_call_ms": lsh_ms,
+               "lsh_attention_kernel_ms": lsh_kernel_ms, "exact_ms": ex_ms,
+               "exact_tflops": dense_flops(w) / (ex_kernel_ms / 1e3) / 1e12,
+               "exact_over_lsh": ex_ms / lsh_ms}
+        log(f"[crossover] n={n}: estimator {lsh_ms:.3f} ms, exact {ex_ms:.3f} ms "
+            f"({rec['exact_tflops']:.0f} TFLOP/s), ratio {rec['exact_over_lsh']:.2f}")
+        print(json.dumps(rec), flush=True)
+        del qd, kd, vd, out, dt
+        torch.cuda.empty_cache()
 
 
 def kernel_sha() -> str:
@@ -118,6 +182,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--error-rows", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--crossover", action="store_true")
+    ap.add_argument("--no-exact", action="store_true", help="skip the exact-ALiBi comparator")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus above 1 is not supported "
@@ -127,6 +193,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.crossover:
+        crossover()
         return
     dev = torch.device("cuda:0")
     w = W.get(args.workload)
@@ -187,6 +256,24 @@ def main():
     parity = float(np.abs(o - est).max())
     log(f"[bench] sampled-row parity vs oracle {parity:.3e}; error vs exact ALiBi {err_exact:.3e}")
 
+    # the dense exact-ALiBi kernel on the same inputs (informational, after
+    # the timed steps), checked against the oracle on the sampled rows
+    exact_rec = None
+    if not args.no_exact:
+        ex_out = torch.empty_like(qd)
+        ex_ms, ex_kernel_ms = time_calls(
+            lambda: plsh.exact_alibi_attention(qd, kd, vd, w.sigma, causal=w.causal, out=ex_out), 3)
+        ex_tflops = dense_flops(w) / (ex_kernel_ms / 1e3) / 1e12
+        ex_parity = float(np.abs(W.to_f64(ex_out[:, :, rows]) - exact).max())
+        exact_rec = {"kernel": "exact_mfma_kernel", "ms": ex_ms, "kernel_ms": ex_kernel_ms,
+                     "dense_tflop": dense_flops(w) / 1e12, "tflops": ex_tflops,
+                     "pct_bf16_peak": 100.0 * ex_tflops / PEAK_BF16_TFLOPS,
+                     "exact_over_lsh_call": ex_ms / ms,
+                     "parity_sampled_rows_max_abs": ex_parity}
+        log(f"[bench] exact ALiBi kernel {ex_ms:.3f} ms ({ex_tflops:.0f} TFLOP/s), "
+            f"{ex_ms / ms:.1f}x the estimator's call; parity vs oracle {ex_parity:.3e}")
+        del ex_out
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, tables, args.cpu_budget)
@@ -224,6 +311,7 @@ def main():
         "host_sample_ms": host_sample_ms,
         "parity_sampled_rows_max_abs": parity,
         "error_vs_exact_alibi": {"rows": len(rows), "max_abs": err_exact, "rel_fro": rel_fro},
+        "exact_alibi_comparator": exact_rec,
         "kernel_sha": kernel_sha(),
     }
     print(json.dumps(rec), flush=True)

@@ -174,11 +174,32 @@ plsh_status plsh_debug_block_intervals(const plsh_tables *boundaries, int32_t *l
                                        plsh_stream_t stream);
 
 /*
+ * plsh_exact_alibi_attention -- exact ALiBi attention, the dense comparator
+ * of the estimator (Problem Statement: the O(n^2) cost the method avoids;
+ * Methodology §1: the bias exp(-|i-j|/sigma) as a Laplacian kernel):
+ *   out_i = sum_j exp(q_i.k_j - |i-j|/sigma_h) v_j / sum_j exp(q_i.k_j - |i-j|/sigma_h)
+ * over j in [0, n), or j <= i when causal; logits with scale 1 as in
+ * plsh_alibi_attention.  Every key is visited (no table, no sampling).
+ *   q, k, v, out, batch, n, heads, kv_heads, d, sigma, causal, stream as for
+ *   plsh_alibi_attention; dtype must be PLSH_BF16 (MFMA kernel; fp32
+ *   accumulation, P rounded to bf16 for the PV product, out rounded to
+ *   nearest-even bf16).
+ * No device memory is allocated.  Errors: PLSH_ERR_ARG (null pointer, sizes
+ * < 1, heads % kv_heads != 0, sigma not finite or <= 0, aliasing,
+ * misalignment), PLSH_ERR_UNSUPPORTED (dtype not bf16, d not 64/128,
+ * batch*heads*n*d >= 2^31, heads > 128), PLSH_ERR_HIP (launch error).
+ */
+plsh_status plsh_exact_alibi_attention(const void *q, const void *k, const void *v, void *out,
+                                       int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                       int32_t d, plsh_dtype dtype, const double *sigma,
+                                       int32_t causal, plsh_stream_t stream);
+
+/*
  * plsh_kernel_timer -- measurement aid (no part of the method).  With
  * enable != 0, every later plsh_alibi_attention / plsh_debug_attention_reference
- * call of this thread records a pair of HIP events on its stream immediately
- * before and after its attention kernel (the block-edge pre-pass is outside
- * the pair); enable == 0 stops recording.  Either call discards pairs not yet
+ * / plsh_exact_alibi_attention call of this thread records a pair of HIP
+ * events on its stream immediately before and after its attention kernel
+ * (the block-edge pre-pass is outside the pair); enable == 0 stops recording.  Either call discards pairs not yet
  * read.  The events are created on first use and kept for reuse by the thread.
  */
 plsh_status plsh_kernel_timer(int32_t enable);

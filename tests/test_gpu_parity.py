@@ -324,3 +324,66 @@ def test_kernel_timer_counts_attention_launches(dev):
     assert launches == 3 and ms > 0.0
     plsh.attention(qd, kd, vd, w.sigma, w.s, t, causal=True)
     assert plsh.kernel_timer_read() == (0, 0.0)
+
+
+# -------------------------------------------------- exact ALiBi comparator ---
+def run_exact(dev, w: W.Workload, rows=None):
+    """GPU exact ALiBi (fp64 numpy) and the oracle's O1 on the same inputs."""
+    q, k, v = W.make_qkv(w)
+    say(w.name, "exact", "B", w.batch, "H", w.heads, "Hkv", w.kv_heads, "n", w.n, "d", w.d,
+        "causal", w.causal, "rows", None if rows is None else len(rows))
+    out = plsh.exact_alibi_attention(q.to(dev), k.to(dev), v.to(dev), w.sigma, causal=w.causal)
+    torch.cuda.synchronize()
+    o = W.to_f64(out)
+    ref = orc.exact_alibi(W.to_f64(q), W.to_f64(k), W.to_f64(v), w.sigma, w.causal, rows=rows)
+    return (o if rows is None else o[:, :, rows]), ref, (q, k, v)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_alibi_ragged_gqa(dev, d, causal):
+    """Several tiles, a ragged tail, GQA, heads of very different sigma."""
+    w = small("exact-ragged", 2, 4, 2, 1000, d, "bf16", causal, [1.3, 9.0, 60.0, 700.0], 1)
+    o, ref, _ = run_exact(dev, w)
+    check_bf16(o, ref, what=f"exact d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("n", [1, 17, 32, 33, 128, 129, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_alibi_small_n(dev, n, causal):
+    w = small("exact-small", 1, 2, 1, n, 64, "bf16", causal, [2.0, 50.0], 1)
+    o, ref, _ = run_exact(dev, w)
+    check_bf16(o, ref, what=f"exact n={n} causal={causal}")
+
+
+@pytest.mark.parametrize("wname,nrows", [("mistral-7b-n16384-s20", 40), ("qwen3-0.6b-n8192-s20", 48)])
+def test_exact_alibi_full_size_sampled_rows(dev, wname, nrows):
+    """Full-size workloads; the oracle evaluates seeded sampled rows."""
+    w = W.get(wname)
+    rows = W.sample_rows(w.n, nrows, seed=23)
+    o, ref, _ = run_exact(dev, w, rows=rows)
+    check_bf16(o, ref, what=f"exact {w.name}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_alibi_huge_sigma_is_softmax_attention(dev, causal):
+    """sigma -> inf removes the bias: plain softmax attention (library
+    attention in fp32 on the CPU)."""
+    w = small("exact-huge-sigma", 1, 2, 1, 600, 128, "bf16", causal, [1e12, 1e12], 1)
+    q, k, v = W.make_qkv(w)
+    out = plsh.exact_alibi_attention(q.to(dev), k.to(dev), v.to(dev), w.sigma, causal=causal)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.float(), k.float().repeat_interleave(2, 1), v.float().repeat_interleave(2, 1),
+        is_causal=causal, scale=1.0)
+    check_bf16(out.cpu().double().numpy(), ref.double().numpy(), what="exact huge sigma")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_alibi_tiny_sigma_returns_v_bitwise(dev, causal):
+    """sigma -> 0: every other key is down-weighted by exp(-|i-j|/sigma) to
+    zero, so each row returns its own value vector exactly."""
+    w = small("exact-tiny-sigma", 1, 2, 2, 777, 64, "bf16", causal, [1e-3, 1e-3], 1)
+    q, k, v = W.make_qkv(w)
+    out = plsh.exact_alibi_attention(q.to(dev), k.to(dev), v.to(dev), w.sigma, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), v)

@@ -207,3 +207,41 @@ def test_kernel_timer_read_rejects_null_pointers():
     n = ctypes.c_int32(0)
     assert plsh.lib().plsh_kernel_timer_read(None, None) == plsh.PLSH_ERR_ARG
     assert plsh.lib().plsh_kernel_timer_read(ctypes.byref(n), None) == plsh.PLSH_ERR_ARG
+
+
+def _exact_call(**over):
+    L, a, keep = _attn_args(**over)
+    st = L.plsh_exact_alibi_attention(a["q"], a["k"], a["v"], a["out"], a["batch"], a["n"], a["heads"],
+                                      a["kv_heads"], a["d"], a["dtype"], a["sigma"], a["causal"],
+                                      a["stream"])
+    return st, L.plsh_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), plsh.PLSH_ERR_ARG),
+    (dict(sigma=None), plsh.PLSH_ERR_ARG),
+    (dict(n=0), plsh.PLSH_ERR_ARG),
+    (dict(kv_heads=3), plsh.PLSH_ERR_ARG),
+    (dict(d=96), plsh.PLSH_ERR_UNSUPPORTED),
+    (dict(dtype=plsh.PLSH_F32), plsh.PLSH_ERR_UNSUPPORTED),
+    (dict(n=1 << 30), plsh.PLSH_ERR_UNSUPPORTED),
+    (dict(out=0x10000 + 64), plsh.PLSH_ERR_ARG),
+    (dict(q=0x10004), plsh.PLSH_ERR_ARG),
+])
+def test_exact_attention_argument_errors(over, status):
+    """plsh_exact_alibi_attention validates like the estimator (no table)."""
+    st, msg = _exact_call(**over)
+    assert st == status, msg
+    assert msg
+
+
+def test_exact_attention_rejects_bad_sigma_and_needs_a_device():
+    import torch
+    L, a, keep = _attn_args()
+    bad = np.array([2.0, 0.0, 8.0, 16.0])
+    st = L.plsh_exact_alibi_attention(a["q"], a["k"], a["v"], a["out"], 1, 64, 4, 2, 64, plsh.PLSH_BF16,
+                                      bad.ctypes.data, 1, None)
+    assert st == plsh.PLSH_ERR_ARG
+    if not torch.cuda.is_available():
+        st, msg = _exact_call()
+        assert st == plsh.PLSH_ERR_HIP, msg
