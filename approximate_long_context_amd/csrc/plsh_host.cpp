@@ -121,6 +121,40 @@ extern "C" plsh_status plsh_sample_tables(uint64_t seed, int32_t n, int32_t head
   return PLSH_OK;
 }
 
+extern "C" plsh_status plsh_build_tables(int32_t n, int32_t heads, int32_t s, const double *params,
+                                         int32_t *offsets, int32_t *starts, int64_t starts_capacity,
+                                         int64_t *starts_needed) {
+  clear_error();
+  if (!params || !offsets || !starts_needed) return fail(PLSH_ERR_ARG, "plsh_build_tables: null pointer argument");
+  if (n < 1 || heads < 1 || s < 1)
+    return fail(PLSH_ERR_ARG, "plsh_build_tables: need n >= 1, heads >= 1, s >= 1 (got %d, %d, %d)", n, heads, s);
+  if (starts && starts_capacity < 0) return fail(PLSH_ERR_ARG, "plsh_build_tables: negative starts_capacity");
+  const int64_t rows = (int64_t)heads * s;
+  for (int64_t r = 0; r < rows; ++r) {
+    const double delta = params[2 * r], u = params[2 * r + 1];
+    if (!finite_pos(delta) || !(u >= 0.0) || !(u < delta))
+      return fail(PLSH_ERR_ARG, "plsh_build_tables: row %lld: need delta > 0 finite and 0 <= u < delta",
+                  (long long)r);
+  }
+  std::vector<int32_t> all, one;
+  offsets[0] = 0;
+  for (int64_t r = 0; r < rows; ++r) {
+    one.clear();
+    hash_starts(n, params[2 * r], params[2 * r + 1], one);
+    if ((int64_t)all.size() + (int64_t)one.size() > (int64_t)INT32_MAX)
+      return fail(PLSH_ERR_CAPACITY, "plsh_build_tables: table exceeds 2^31 entries");
+    all.insert(all.end(), one.begin(), one.end());
+    offsets[r + 1] = (int32_t)all.size();
+  }
+  *starts_needed = (int64_t)all.size();
+  if (!starts) return PLSH_OK;
+  if (starts_capacity < (int64_t)all.size())
+    return fail(PLSH_ERR_CAPACITY, "plsh_build_tables: starts needs %lld entries, capacity %lld",
+                (long long)all.size(), (long long)starts_capacity);
+  memcpy(starts, all.data(), all.size() * sizeof(int32_t));
+  return PLSH_OK;
+}
+
 extern "C" plsh_status plsh_validate_tables(const plsh_tables *t) {
   clear_error();
   if (!t || !t->params || !t->offsets || !t->starts)

@@ -23,7 +23,7 @@ PLSH_BF16, PLSH_F32 = 0, 1
 STATUS_NAMES = {0: "PLSH_OK", 1: "PLSH_ERR_ARG", 2: "PLSH_ERR_TABLE", 3: "PLSH_ERR_UNSUPPORTED",
                 4: "PLSH_ERR_CAPACITY", 5: "PLSH_ERR_HIP"}
 
-EXPORTED = ["plsh_sample_tables", "plsh_validate_tables", "plsh_count_work",
+EXPORTED = ["plsh_sample_tables", "plsh_build_tables", "plsh_validate_tables", "plsh_count_work",
             "plsh_alibi_attention", "plsh_debug_block_intervals",
             "plsh_debug_attention_reference", "plsh_exact_alibi_attention",
             "plsh_kernel_timer", "plsh_kernel_timer_read", "plsh_last_error"]
@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
         i32, i64, u64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
         TP = ctypes.POINTER(_Tables)
         L.plsh_sample_tables.argtypes = [u64, i32, i32, vp, i32, vp, vp, vp, i64, ctypes.POINTER(i64)]
+        L.plsh_build_tables.argtypes = [i32, i32, i32, vp, vp, vp, i64, ctypes.POINTER(i64)]
         L.plsh_validate_tables.argtypes = [TP]
         L.plsh_count_work.argtypes = [TP, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
         attn = [vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp, i32, TP, i32, vp]
@@ -136,6 +137,30 @@ def sample_tables(seed: int, n: int, sigma: Sequence[float], s: int) -> Tables:
     _check(L.plsh_sample_tables(seed, n, heads, _ptr(sig), s, _ptr(params), _ptr(offsets),
                                 _ptr(starts), starts.size, ctypes.byref(need)))
     return Tables(n, heads, s, params, offsets, starts[:need.value])
+
+
+def build_tables(n: int, heads: int, s: int, params) -> Tables:
+    """plsh_build_tables: the table of caller-given (delta, u) rows,
+    [heads*s, 2] float64 (two-call protocol)."""
+    L = lib()
+    prm = np.ascontiguousarray(params, dtype=np.float64).reshape(heads * s, 2)
+    offsets = np.empty(heads * s + 1, dtype=np.int32)
+    need = ctypes.c_int64(0)
+    _check(L.plsh_build_tables(n, heads, s, _ptr(prm), _ptr(offsets), None, 0, ctypes.byref(need)))
+    starts = np.empty(max(need.value, 1), dtype=np.int32)
+    _check(L.plsh_build_tables(n, heads, s, _ptr(prm), _ptr(offsets), _ptr(starts), starts.size,
+                               ctypes.byref(need)))
+    return Tables(n, heads, s, prm.copy(), offsets, starts[:need.value])
+
+
+def fixed_block_tables(n: int, width: Sequence[float], s: int = 1) -> Tables:
+    """The "fixed blocks" baseline: per head one deterministic hash of pitch
+    width[h] and offset 0 (blocks [0, w), [w, 2w), ... for integer w),
+    repeated for the s samples."""
+    w = np.asarray(width, dtype=np.float64)
+    params = np.zeros((len(w) * s, 2), dtype=np.float64)
+    params[:, 0] = np.repeat(w, s)
+    return build_tables(n, len(w), s, params)
 
 
 def validate_tables(t: Tables) -> None:

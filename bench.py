@@ -274,6 +274,22 @@ def main():
             f"{ex_ms / ms:.1f}x the estimator's call; parity vs oracle {ex_parity:.3e}")
         del ex_out
 
+    # the "fixed blocks" baseline (one deterministic hash per head, pitch
+    # 2 sigma = the mean random pitch, offset 0) through the same kernel:
+    # its error against exact ALiBi on the same sampled rows, and its time
+    fixed_rec = None
+    if not args.no_exact:
+        ft = plsh.fixed_block_tables(n, [2.0 * x for x in w.sigma], 1).to(dev)
+        fx_out = torch.empty_like(qd)
+        fx_ms, _ = time_calls(lambda: plsh.attention(qd, kd, vd, w.sigma, 1, ft, causal=w.causal, out=fx_out), 5)
+        fo = W.to_f64(fx_out[:, :, rows])
+        fixed_rec = {"table": "pitch 2 sigma_h, offset 0, s = 1", "ms": fx_ms,
+                     "error_vs_exact_alibi": {"rows": len(rows), "max_abs": float(np.abs(fo - exact).max()),
+                                              "rel_fro": float(np.linalg.norm(fo - exact) / np.linalg.norm(exact))}}
+        log(f"[bench] fixed blocks: {fx_ms:.3f} ms, rel. error vs exact {fixed_rec['error_vs_exact_alibi']['rel_fro']:.3f}"
+            f" (estimator {rel_fro:.3f})")
+        del fx_out, ft
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, tables, args.cpu_budget)
@@ -312,6 +328,7 @@ def main():
         "parity_sampled_rows_max_abs": parity,
         "error_vs_exact_alibi": {"rows": len(rows), "max_abs": err_exact, "rel_fro": rel_fro},
         "exact_alibi_comparator": exact_rec,
+        "fixed_blocks_baseline": fixed_rec,
         "kernel_sha": kernel_sha(),
     }
     print(json.dumps(rec), flush=True)

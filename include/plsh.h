@@ -100,6 +100,24 @@ plsh_status plsh_sample_tables(uint64_t seed, int32_t n, int32_t heads, const do
                                int64_t starts_capacity, int64_t *starts_needed);
 
 /*
+ * plsh_build_tables -- the boundary table of caller-given hashes: for every
+ * row r = h*s + k of params ([heads*s][2] = {delta, u}, host), the block
+ * starts of bin(x) = floor((x + u) / delta) (Methodology §1; the same scan as
+ * plsh_sample_tables, which draws the parameters itself).  Deterministic
+ * tables -- e.g. "fixed blocks" of constant width w with offset 0, every
+ * sample alike (Experimental Validation: the baseline the method beats) --
+ * are built this way.  Two-call protocol as plsh_sample_tables: with
+ * starts == NULL it fills offsets ([heads*s + 1]) and *starts_needed; the
+ * second call also fills starts.
+ * Errors: PLSH_ERR_ARG (null pointer, n/heads/s < 1, a row without
+ * delta > 0 finite and 0 <= u < delta), PLSH_ERR_CAPACITY (starts_capacity
+ * too small, or more than 2^31 - 1 entries).
+ */
+plsh_status plsh_build_tables(int32_t n, int32_t heads, int32_t s, const double *params,
+                              int32_t *offsets, int32_t *starts, int64_t starts_capacity,
+                              int64_t *starts_needed);
+
+/*
  * plsh_validate_tables -- check a table (all arrays HOST pointers): sizes > 0,
  * every delta finite and > 0, 0 <= u < delta, offsets[0] == 0 and
  * non-decreasing, each row strictly increasing from 0 to n, and every row's

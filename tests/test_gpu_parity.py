@@ -387,3 +387,30 @@ def test_exact_alibi_tiny_sigma_returns_v_bitwise(dev, causal):
     out = plsh.exact_alibi_attention(q.to(dev), k.to(dev), v.to(dev), w.sigma, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(out.cpu(), v)
+
+
+# ------------------------------------------------- fixed-blocks baseline ---
+@pytest.mark.parametrize("causal", [False, True])
+def test_fixed_blocks_estimator_matches_oracle(dev, causal):
+    """The deterministic "fixed blocks" table (pitch 2 sigma, offset 0) runs
+    through the same kernel; the oracle derives its blocks from the same
+    parameters."""
+    w = small("fixed-blocks", 2, 4, 2, 1000, 128, "bf16", causal, [1.3, 9.0, 60.0, 700.0], 1)
+    t = plsh.fixed_block_tables(w.n, [2.0 * x for x in w.sigma], s=1)
+    o, ref, _ = run_case(dev, w, tables=t)
+    check_bf16(o, ref, what=f"fixed blocks causal={causal}")
+
+
+def test_fixed_blocks_repeated_samples_agree(dev):
+    """s identical hashes give M~ = M, so s = 4 and s = 1 are the same
+    estimate.  The kernel folds log2(c) into the exponent on tiles of one
+    count, so the bits may differ by rounding: the two agree to the bf16
+    tolerance."""
+    w = small("fixed-repeat", 1, 4, 2, 900, 64, "bf16", True, [2.0, 9.0, 60.0, 300.0], 1)
+    q, k, v = W.make_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    width = [2.0 * x for x in w.sigma]
+    o1 = plsh.attention(qd, kd, vd, w.sigma, 1, plsh.fixed_block_tables(w.n, width, 1).to(dev), causal=True)
+    o4 = plsh.attention(qd, kd, vd, w.sigma, 4, plsh.fixed_block_tables(w.n, width, 4).to(dev), causal=True)
+    torch.cuda.synchronize()
+    check_bf16(W.to_f64(o4), W.to_f64(o1), what="fixed blocks s=4 vs s=1")

@@ -245,3 +245,46 @@ def test_exact_attention_rejects_bad_sigma_and_needs_a_device():
     if not torch.cuda.is_available():
         st, msg = _exact_call()
         assert st == plsh.PLSH_ERR_HIP, msg
+
+
+@pytest.mark.parametrize("width", [1.0, 7.0, 7.5, 64.0, 1e6])
+def test_fixed_block_tables_match_oracle_scan(width):
+    """Fixed blocks (pitch w, offset 0) through plsh_build_tables equal the
+    oracle's own scan of the same hash; integer w gives starts 0, w, 2w, ..."""
+    n = 1000
+    t = plsh.fixed_block_tables(n, [width, 2.0 * width], s=3)
+    plsh.validate_tables(t)
+    off, st = orc.tables_from_params(n, t.params)
+    assert np.array_equal(t.offsets, off) and np.array_equal(t.starts, st)
+    if float(width).is_integer():
+        r0 = t.starts[t.offsets[0]:t.offsets[1]]
+        want = np.unique(np.append(np.arange(0, n, int(width)), n))
+        assert np.array_equal(r0, want)
+
+
+def test_build_tables_reproduces_the_sampler():
+    t = plsh.sample_tables(11, 3000, [1.19, 16.0, 256.0], 7)
+    b = plsh.build_tables(3000, 3, 7, t.params)
+    assert np.array_equal(t.offsets, b.offsets) and np.array_equal(t.starts, b.starts)
+
+
+@pytest.mark.parametrize("row", [(0.0, 0.0), (-1.0, 0.0), (float("nan"), 0.0), (4.0, -0.5), (4.0, 4.0),
+                                 (float("inf"), 0.0)])
+def test_build_tables_rejects_bad_rows(row):
+    params = np.array([[8.0, 1.0], row], dtype=np.float64)
+    with pytest.raises(plsh.PlshError) as e:
+        plsh.build_tables(100, 1, 2, params)
+    assert e.value.status == plsh.PLSH_ERR_ARG
+
+
+def test_build_tables_capacity_protocol():
+    L = plsh.lib()
+    params = np.array([[3.0, 0.0]], dtype=np.float64)
+    offsets = np.empty(2, dtype=np.int32)
+    need = ctypes.c_int64(0)
+    assert L.plsh_build_tables(30, 1, 1, params.ctypes.data, offsets.ctypes.data, None, 0,
+                               ctypes.byref(need)) == plsh.PLSH_OK
+    assert need.value == 11
+    small_buf = np.empty(5, dtype=np.int32)
+    assert L.plsh_build_tables(30, 1, 1, params.ctypes.data, offsets.ctypes.data, small_buf.ctypes.data, 5,
+                               ctypes.byref(need)) == plsh.PLSH_ERR_CAPACITY
