@@ -61,6 +61,12 @@ struct AttnArgs {
   const double *params;
   int32_t batch, n, heads, kv_heads, s;
   int32_t groups;  // query-row tiles per (batch, head)
+  int32_t pstride;  // rows of params between consecutive heads (s for a whole table)
+  // when o32 is set, the MFMA kernel writes fp32 O ([batch, heads, n, d]) and
+  // the row's natural-log sum lse = ln sum_j c_ij exp(q_i.k_j) ([batch, heads,
+  // n]) instead of bf16 out
+  float *o32;
+  float *lse;
   int32_t order[kMaxHeadsArg];  // head processed in slot i, heaviest sigma first
 };
 
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
   const T *V = (const T *)a.v + ((int64_t)b * a.kv_heads + kvh) * n * D;
   T *O = (T *)a.out + ((int64_t)b * a.heads + h) * n * D;
 
-  wave_setup(a.params + 2 * (int64_t)h * s, s, n, r0, lane, w);
+  wave_setup(a.params + 2 * (int64_t)h * a.pstride, s, n, r0, lane, w);
 
   constexpr int E = D / 64;
   for (int t = 0; t < 32 && r0 + t < n; ++t) {
@@ -484,8 +490,8 @@ __host__ __device__ constexpr size_t rec_bytes(int s) { return rec_diag_off(s) +
 constexpr int kMaxMfmaSamples = 124;
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(256) void edges_kernel(const double *params, int n, int heads, int s, int g32,
-                                                    uint8_t *ws) {
+__global__ __launch_bounds__(256) void edges_kernel(const double *params, int pstride, int n, int heads, int s,
+                                                    int g32, uint8_t *ws) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = lane & 31, hh = lane >> 5;
@@ -497,7 +503,8 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int n,
   const WaveTab w = carve_wavetab(wb, s);
   uint32_t *hist = (uint32_t *)(wb + wavetab_bytes(s));  // [32 rows][16 dwords]: up 0..7, down 8..15
   for (int i = lane; i < 32 * 16; i += 64) hist[i] = 0u;
-  const int nact = wave_ends(params + 2 * (int64_t)h * s, s, n, r0, lane, w);
+  // head h's s hashes are rows h * pstride .. + s - 1 of params
+  const int nact = wave_ends(params + 2 * (int64_t)h * pstride, s, n, r0, lane, w);
   wave_sync();
   wave_masks(n, r0, lane, nact, w);
   wave_sync();
@@ -984,6 +991,19 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   float ltot = lsum + xor16_f(lsum);
   ltot += other_half_f(ltot, lane);
   const float inv = 1.0f / ltot;
+  if (a.o32) {
+    // fp32 partials for a log-sum-exp combine: O (normalised) and lse, in
+    // natural-log units (the running max m2 is in log2 units)
+    const int io = r0 + qc;
+    if (io < n) {
+      const int64_t row = ((int64_t)b * a.heads + h) * n + io;
+      float *orow = a.o32 + row * D + 4 * gq;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) *(floatx4 *)(orow + 16 * db) = oacc[db] * inv;
+      if (gq == 0) a.lse[row] = (m2 + __log2f(ltot)) * 0.6931471805599453f;
+    }
+    return;
+  }
   const int free_slot = (((nst - 1) >> 1) & 1) ? 0 : 2;
   char *ob = (char *)lds.kv[free_slot][0] + wave * 32 * D;
 #pragma unroll
@@ -1238,6 +1258,38 @@ void exact_mfma_kernel(ExactArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Log-sum-exp combine of per-sample partials (the unfused form of
+// Methodology §3: s short attentions, each normalised on its own, recombined
+// into the one ratio of sums):
+//   out_i = sum_k e^{lse_k,i} O_k,i / sum_k e^{lse_k,i}
+// o32 [s][rows][D] and lse [s][rows] fp32; one wave per row, lane l holds
+// dims l, l + 64.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const float *o32, const float *lse, int s, int64_t rows,
+                                                      uint16_t *out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int E = D / 64;
+  float mx = -INFINITY;
+  for (int k = 0; k < s; ++k) mx = fmaxf(mx, lse[(int64_t)k * rows + row]);
+  float acc[E], den = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int k = 0; k < s; ++k) {
+    const float wk = expf(lse[(int64_t)k * rows + row] - mx);
+    den += wk;
+    const float *ok = o32 + ((int64_t)k * rows + row) * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(wk, ok[lane + 64 * e], acc[e]);
+  }
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[row * D + lane + 64 * e] = (uint16_t)f32_to_bf16_bits(acc[e] * inv);
+}
+
 }  // namespace dev
 
 // ---------------------------------------------------------------------------
@@ -1299,6 +1351,9 @@ void fill_args(dev::AttnArgs &a, const void *q, const void *k, const void *v, vo
   a.kv_heads = kv_heads;
   a.s = s;
   a.groups = (n + 127) / 128;
+  a.pstride = s;
+  a.o32 = nullptr;
+  a.lse = nullptr;
   // heavy heads first: per-row work grows with sigma
   int idx[dev::kMaxHeadsArg];
   std::iota(idx, idx + heads, 0);
@@ -1377,8 +1432,8 @@ plsh_status launch_mfma(const dev::AttnArgs &a, int d, int causal, hipStream_t s
   const int items = a.heads * g32;
   const dim3 egrid((unsigned)((items + 3) / 4)), eblock(256);
   const size_t eshm = 4 * (dev::wavetab_bytes(a.s) + 32 * 16 * 4);
-  if (causal) hipLaunchKernelGGL(dev::edges_kernel<true>, egrid, eblock, eshm, st, a.params, a.n, a.heads, a.s, g32, (uint8_t *)ws);
-  else hipLaunchKernelGGL(dev::edges_kernel<false>, egrid, eblock, eshm, st, a.params, a.n, a.heads, a.s, g32, (uint8_t *)ws);
+  if (causal) hipLaunchKernelGGL(dev::edges_kernel<true>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)ws);
+  else hipLaunchKernelGGL(dev::edges_kernel<false>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)ws);
   plsh_status rc = launch_check(who);
   if (rc == PLSH_OK) {
     const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(64 * dev::kWaves);
@@ -1522,6 +1577,56 @@ extern "C" plsh_status plsh_exact_alibi_attention(const void *q, const void *k, 
   a.groups = (n + 127) / 128;
   for (int i = 0; i < dev::kMaxHeadsArg; ++i) a.slope2[i] = i < heads ? (float)(1.4426950408889634 / sigma[i]) : 0.f;
   return launch_exact(a, d, causal != 0, (hipStream_t)stream, who);
+}
+
+// The unfused form of the estimator (an ablation of the sample fusion): s
+// single-sample passes of the same kernels writing fp32 partials, then the
+// log-sum-exp combine.
+extern "C" plsh_status plsh_alibi_attention_unfused(const void *q, const void *k, const void *v, void *out,
+                                                    int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                                    int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                                    const plsh_tables *boundaries, int32_t causal,
+                                                    plsh_stream_t stream) {
+  static const char *who = "plsh_alibi_attention_unfused";
+  clear_error();
+  plsh_status st = check_common(q, k, v, out, batch, n, heads, kv_heads, d, dtype, sigma, s, boundaries, who);
+  if (st != PLSH_OK) return st;
+  if (dtype != PLSH_BF16) return fail(PLSH_ERR_UNSUPPORTED, "%s: only bf16 is supported", who);
+  if ((st = have_device(who)) != PLSH_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  const int64_t rows = (int64_t)batch * heads * n;
+  const size_t bytes = (size_t)s * rows * ((size_t)d + 1) * sizeof(float);
+  void *ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, hs);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PLSH_ERR_HIP, "%s: partials allocation of %zu bytes failed: %s", who, bytes, hipGetErrorString(e));
+  }
+  float *o32 = (float *)ws;
+  float *lse = o32 + (size_t)s * rows * d;
+  plsh_status rc = PLSH_OK;
+  for (int32_t kk = 0; kk < s && rc == PLSH_OK; ++kk) {
+    dev::AttnArgs a;
+    fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
+    a.params = boundaries->params + 2 * kk;  // sample kk of every head: rows h * s + kk
+    a.pstride = s;
+    a.s = 1;
+    a.o32 = o32 + (size_t)kk * rows * d;
+    a.lse = lse + (size_t)kk * rows;
+    rc = launch_mfma(a, d, causal != 0, hs, who);
+  }
+  if (rc == PLSH_OK) {
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    if (d == 64) hipLaunchKernelGGL(dev::combine_kernel<64>, grid, block, 0, hs, o32, lse, s, rows, (uint16_t *)out);
+    else hipLaunchKernelGGL(dev::combine_kernel<128>, grid, block, 0, hs, o32, lse, s, rows, (uint16_t *)out);
+    rc = launch_check(who);
+  }
+  e = hipFreeAsync(ws, hs);
+  if (e != hipSuccess && rc == PLSH_OK) {
+    (void)hipGetLastError();
+    return fail(PLSH_ERR_HIP, "%s: partials release failed: %s", who, hipGetErrorString(e));
+  }
+  return rc;
 }
 
 extern "C" plsh_status plsh_kernel_timer(int32_t enable) {

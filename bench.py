@@ -71,7 +71,7 @@ def dense_flops(w: W.Workload) -> float:
     return 4.0 * w.d * w.batch * w.heads * pairs
 
 
-def time_calls(fn, reps: int):
+def time_calls(fn, reps: int, launches_per_call: int = 1):
     """(ms per call by events around the calls, ms per attention kernel by the
     library's kernel timer)."""
     dev = torch.device("cuda:0")
@@ -88,7 +88,7 @@ def time_calls(fn, reps: int):
     torch.cuda.synchronize()
     launches, total = plsh.kernel_timer_read()
     plsh.kernel_timer(False)
-    assert launches == reps, (launches, reps)
+    assert launches == reps * launches_per_call, (launches, reps, launches_per_call)
     return e0.elapsed_time(e1) / reps, total / launches
 
 
@@ -290,6 +290,20 @@ def main():
             f" (estimator {rel_fro:.3f})")
         del fx_out, ft
 
+    # the unfused form (s single-sample passes writing fp32 partials, then a
+    # log-sum-exp combine): what the sample fusion saves
+    unfused_rec = None
+    if not args.no_exact:
+        uf_out = torch.empty_like(qd)
+        uf_ms, _ = time_calls(lambda: plsh.attention_unfused(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal,
+                                                              out=uf_out), 3, w.s)
+        uf_parity = float(np.abs(W.to_f64(uf_out[:, :, rows]) - est).max())
+        unfused_rec = {"ms": uf_ms, "over_fused_call": uf_ms / ms,
+                       "partials_bytes": w.s * B * H * n * (d + 1) * 4,
+                       "parity_sampled_rows_max_abs": uf_parity}
+        log(f"[bench] unfused: {uf_ms:.3f} ms ({uf_ms / ms:.1f}x the fused call), parity vs oracle {uf_parity:.3e}")
+        del uf_out
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, tables, args.cpu_budget)
@@ -329,6 +343,7 @@ def main():
         "error_vs_exact_alibi": {"rows": len(rows), "max_abs": err_exact, "rel_fro": rel_fro},
         "exact_alibi_comparator": exact_rec,
         "fixed_blocks_baseline": fixed_rec,
+        "unfused_ablation": unfused_rec,
         "kernel_sha": kernel_sha(),
     }
     print(json.dumps(rec), flush=True)

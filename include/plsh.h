@@ -192,6 +192,25 @@ plsh_status plsh_debug_block_intervals(const plsh_tables *boundaries, int32_t *l
                                        plsh_stream_t stream);
 
 /*
+ * plsh_alibi_attention_unfused -- the same estimate computed the way the
+ * pages state the reduction (Methodology §3, Theorem 2.2: s short-context
+ * attentions without positional bias): for each sample k a pass over every
+ * row's block B_k(i) alone, writing fp32 partials (O_k normalised over the
+ * block, lse_k = ln sum_{j in B_k(i)} exp(q_i.k_j)), then a log-sum-exp
+ * combine out_i = sum_k e^{lse_k} O_k / sum_k e^{lse_k}.  An ablation of the
+ * sample fusion of plsh_alibi_attention (same arguments, same result up to
+ * rounding); bf16 only.  Device memory: s * batch * heads * n * (d + 1) * 4
+ * bytes of partials from the stream-ordered allocator on `stream`, released
+ * within the call, plus each pass's pre-pass workspace.
+ * Errors: as plsh_alibi_attention, and PLSH_ERR_UNSUPPORTED for fp32.
+ */
+plsh_status plsh_alibi_attention_unfused(const void *q, const void *k, const void *v, void *out,
+                                         int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                         int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                         const plsh_tables *boundaries, int32_t causal,
+                                         plsh_stream_t stream);
+
+/*
  * plsh_exact_alibi_attention -- exact ALiBi attention, the dense comparator
  * of the estimator (Problem Statement: the O(n^2) cost the method avoids;
  * Methodology §1: the bias exp(-|i-j|/sigma) as a Laplacian kernel):

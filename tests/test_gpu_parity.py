@@ -414,3 +414,34 @@ def test_fixed_blocks_repeated_samples_agree(dev):
     o4 = plsh.attention(qd, kd, vd, w.sigma, 4, plsh.fixed_block_tables(w.n, width, 4).to(dev), causal=True)
     torch.cuda.synchronize()
     check_bf16(W.to_f64(o4), W.to_f64(o1), what="fixed blocks s=4 vs s=1")
+
+
+# ------------------------------------------- unfused reduction (ablation) ---
+def run_unfused(dev, w: W.Workload, rows=None):
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(w.hash_seed, w.n, w.sigma, w.s)
+    say(w.name, "unfused", "B", w.batch, "H", w.heads, "n", w.n, "d", w.d, "s", w.s, "causal", w.causal)
+    out = plsh.attention_unfused(q.to(dev), k.to(dev), v.to(dev), w.sigma, w.s, t.to(dev), causal=w.causal)
+    torch.cuda.synchronize()
+    o = W.to_f64(out)
+    off, st = orc.tables_from_params(w.n, t.params)
+    tabs = orc.starts_per_head(off, st, w.heads, w.s)
+    ref = orc.lsh_estimate(W.to_f64(q), W.to_f64(k), W.to_f64(v), tabs, w.causal, rows=rows)
+    return (o if rows is None else o[:, :, rows]), ref
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_unfused_matches_oracle(dev, d, causal):
+    """s single-sample passes plus the log-sum-exp combine give the same
+    estimate (Methodology §3 reduction, stated per sample)."""
+    w = small("unfused", 2, 4, 2, 1000, d, "bf16", causal, [1.3, 9.0, 60.0, 700.0], 7)
+    o, ref = run_unfused(dev, w)
+    check_bf16(o, ref, what=f"unfused d={d} causal={causal}")
+
+
+def test_unfused_full_size_sampled_rows(dev):
+    w = W.get("mistral-7b-n16384-s20")
+    rows = W.sample_rows(w.n, 32, seed=29)
+    o, ref = run_unfused(dev, w, rows=rows)
+    check_bf16(o, ref, what="unfused mistral")
