@@ -183,7 +183,8 @@ def main():
     ap.add_argument("--error-rows", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--crossover", action="store_true")
-    ap.add_argument("--no-exact", action="store_true", help="skip the exact-ALiBi comparator")
+    ap.add_argument("--no-comparators", action="store_true",
+                    help="skip the exact-ALiBi, fixed-blocks and unfused comparisons (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus above 1 is not supported "
@@ -259,7 +260,7 @@ def main():
     # the dense exact-ALiBi kernel on the same inputs (informational, after
     # the timed steps), checked against the oracle on the sampled rows
     exact_rec = None
-    if not args.no_exact:
+    if not args.no_comparators:
         ex_out = torch.empty_like(qd)
         ex_ms, ex_kernel_ms = time_calls(
             lambda: plsh.exact_alibi_attention(qd, kd, vd, w.sigma, causal=w.causal, out=ex_out), 3)
@@ -278,7 +279,7 @@ def main():
     # 2 sigma = the mean random pitch, offset 0) through the same kernel:
     # its error against exact ALiBi on the same sampled rows, and its time
     fixed_rec = None
-    if not args.no_exact:
+    if not args.no_comparators:
         ft = plsh.fixed_block_tables(n, [2.0 * x for x in w.sigma], 1).to(dev)
         fx_out = torch.empty_like(qd)
         fx_ms, _ = time_calls(lambda: plsh.attention(qd, kd, vd, w.sigma, 1, ft, causal=w.causal, out=fx_out), 5)
@@ -293,7 +294,7 @@ def main():
     # the unfused form (s single-sample passes writing fp32 partials, then a
     # log-sum-exp combine): what the sample fusion saves
     unfused_rec = None
-    if not args.no_exact:
+    if not args.no_comparators:
         uf_out = torch.empty_like(qd)
         uf_ms, _ = time_calls(lambda: plsh.attention_unfused(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal,
                                                               out=uf_out), 3, w.s)
