@@ -585,6 +585,15 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int ps
   *(u32x4 *)(rec + rec_diag_off(s) + 32 * t + 16 * hh) = c;
 }
 
+// max of three finite floats in one instruction (the compiler's max of
+// floats first quiets each operand's NaN payload, one extra instruction per
+// operand; logits are never NaN)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // x from lane l ^ 16 (within each 32-lane half; ds_swizzle bit mode, no
 // memory access)
 __device__ __forceinline__ float xor16_f(float x) {
@@ -874,11 +883,10 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     // rare).  A tile with one count per row folds log2(c) into the exponent
     // bias; otherwise P = c * 2^(...).  P is rounded to bf16 in pairs and the
     // row sum adds exactly the rounded weights that enter PV.
-    // (med3(x, y, +inf) = max(x, y) for the finite logits, one instruction
-    // without the NaN canonicalisation fmaxf needs)
-    auto mx2 = [](float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); };
-    float mx = mx2(mx2(mx2(sacc[0][0], sacc[0][1]), mx2(sacc[0][2], sacc[0][3])),
-                   mx2(mx2(sacc[1][0], sacc[1][1]), mx2(sacc[1][2], sacc[1][3])));
+    // (raw v_max3_f32: one instruction per three finite logits)
+    auto mx2 = [](float x, float y) { return max3f(x, y, y); };
+    float mx = max3f(max3f(sacc[0][0], sacc[0][1], sacc[0][2]), max3f(sacc[0][3], sacc[1][0], sacc[1][1]),
+                     max3f(sacc[1][2], sacc[1][3], sacc[1][3]));
     // the lane's own maximum decides whether any rescale is due; only then
     // is it combined over the four lanes of each query
     if (__any(mx * kLog2e > m2 + 8.0f)) {
@@ -1160,8 +1168,8 @@ void exact_mfma_kernel(ExactArgs a) {
         if ((CAUSAL && j > i) || j >= n) x[r] = -INFINITY;
       }
     }
-    auto mx2 = [](float u, float w) { return __builtin_fmaxf(u, w); };
-    float mx = mx2(mx2(mx2(x[0], x[1]), mx2(x[2], x[3])), mx2(mx2(x[4], x[5]), mx2(x[6], x[7])));
+    auto mx2 = [](float u, float w) { return max3f(u, w, w); };
+    float mx = max3f(max3f(x[0], x[1], x[2]), max3f(x[3], x[4], x[5]), max3f(x[6], x[7], x[7]));
     if (__any(mx > m2 + 8.0f)) {
       mx = mx2(mx, xor16_f(mx));
       mx = mx2(mx, other_half_f(mx, lane));
