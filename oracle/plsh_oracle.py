@@ -39,6 +39,9 @@ Parity status per function:
   lsh_estimate_multiplicity pinned (brute force)
   mask_mean / matrix_errors pinned (variance identity, 1/sqrt(s) slope)
   work_counts              pinned (brute-force pair enumeration)
+  lsh_estimate_grad /      pinned (central finite differences of the
+  lsh_grad_rows /          block-walk lsh_estimate; subsets against the
+  lsh_grad_keys            dense gradient)
 """
 
 from __future__ import annotations
@@ -67,6 +70,9 @@ __all__ = [
     "mask_mean",
     "matrix_errors",
     "work_counts",
+    "lsh_estimate_grad",
+    "lsh_grad_rows",
+    "lsh_grad_keys",
 ]
 
 # --------------------------------------------------------------------------
@@ -374,3 +380,110 @@ def work_counts(n: int, tables: List[List[np.ndarray]], causal: bool) -> Tuple[i
         else:
             distinct += int((uhi - ulo).sum())
     return alg, distinct
+
+
+# --------------------------------------------------------------------------
+# O6: gradients of the estimate for fixed hash tables (the pages train with
+# the method: Experimental Validation).  With P_ij = c_ij e^{q_i.k_j} /
+# sum_l c_il e^{q_i.k_l} and T~_i = sum_j P_ij v_j, an upstream gradient dO
+# gives (c is a constant of the tables; the softmax Jacobian):
+#   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . v_j,   D_i = sum_j P_ij dP_ij,
+#   dS_ij = P_ij (dP_ij - D_i),   dQ_i = sum_j dS_ij k_j,   dK_j = sum_i dS_ij q_i.
+# K and V gradients of a GQA group add over the group's query heads.
+# --------------------------------------------------------------------------
+def lsh_estimate_grad(q, k, v, do, tables, causal):
+    """(dq, dk, dv) of sum(do * T~) for every element, dense per head (small n)."""
+    B, H, n, d = q.shape
+    Hkv = k.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            c = multiplicity_dense(n, tables[h], causal).astype(np.float64)
+            lg = q[b, h] @ k[b, g].T
+            lg = np.where(c > 0, lg, -np.inf)
+            w = c * np.exp(lg - lg.max(axis=1, keepdims=True))
+            p = w / w.sum(axis=1, keepdims=True)
+            dp = do[b, h] @ v[b, g].T
+            dvec = (p * dp).sum(axis=1, keepdims=True)
+            ds = p * (dp - dvec)
+            dq[b, h] = ds @ k[b, g]
+            dk[b, g] += ds.T @ q[b, h]
+            dv[b, g] += p.T @ do[b, h]
+    return dq, dk, dv
+
+
+def _row_probs(qi, kh, starts_list, i, n, causal):
+    """Keys j with c_ij > 0 of row i and their normalised weights P_ij."""
+    lo, hi = n, 0
+    ivals = []
+    for st in starts_list:
+        a, bnd = _interval_of(st, i)
+        if causal:
+            bnd = min(bnd, i + 1)
+        ivals.append((a, bnd))
+        lo, hi = min(lo, a), max(hi, bnd)
+    js = np.arange(lo, hi)
+    c = np.zeros(len(js))
+    for a, bnd in ivals:
+        c[(js >= a) & (js < bnd)] += 1.0
+    lg = kh[js] @ qi
+    w = c * np.exp(lg - lg.max())
+    return js, w / w.sum()
+
+
+def _interval_of(starts, x):
+    idx = np.searchsorted(starts, x, side="right") - 1
+    return int(starts[idx]), int(starts[idx + 1])
+
+
+def lsh_grad_rows(q, k, v, do, tables, causal, rows):
+    """dq at the given query rows ([B, H, len(rows), d]): row-local."""
+    B, H, n, d = q.shape
+    Hkv = k.shape[1]
+    out = np.zeros((B, H, len(rows), d))
+    for b in range(B):
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            for r, i in enumerate(rows):
+                js, p = _row_probs(q[b, h, i], k[b, g], tables[h], int(i), n, causal)
+                dp = v[b, g, js] @ do[b, h, i]
+                ds = p * (dp - (p * dp).sum())
+                out[b, h, r] = ds @ k[b, g, js]
+    return out
+
+
+def lsh_grad_keys(q, k, v, do, tables, causal, keys):
+    """(dk, dv) at the given key positions ([B, Hkv, len(keys), d]).  The rows
+    that weigh key j are those sharing a block with j in some hash (the
+    same-bin relation is symmetric), i >= j when causal; each needs its own
+    normalisation over its blocks."""
+    B, H, n, d = q.shape
+    Hkv = k.shape[1]
+    dk = np.zeros((B, Hkv, len(keys), d))
+    dv = np.zeros((B, Hkv, len(keys), d))
+    for b in range(B):
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            for r, j in enumerate(keys):
+                j = int(j)
+                lo, hi = n, 0
+                for st in tables[h]:
+                    a, bnd = _interval_of(st, j)
+                    lo, hi = min(lo, a), max(hi, bnd)
+                if causal:
+                    lo = j
+                for i in range(lo, hi):
+                    js, p = _row_probs(q[b, h, i], k[b, g], tables[h], i, n, causal)
+                    hit = np.nonzero(js == j)[0]
+                    if len(hit) == 0:
+                        continue
+                    dp = v[b, g, js] @ do[b, h, i]
+                    dvec = (p * dp).sum()
+                    pij = p[hit[0]]
+                    dv[b, g, r] += pij * do[b, h, i]
+                    dk[b, g, r] += pij * (dp[hit[0]] - dvec) * q[b, h, i]
+    return dk, dv
+

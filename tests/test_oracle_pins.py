@@ -431,3 +431,48 @@ def test_sampler_stream_is_splitmix64():
     6457827717110365317, 3203168211198807973, 9817491932198370423 first."""
     want = [6457827717110365317, 3203168211198807973, 9817491932198370423]
     assert [orc.splitmix64(1234567, i) for i in range(3)] == want
+
+
+# ------------------------------------------------------------- O6 (grad) ---
+@pytest.mark.parametrize("causal", [False, True])
+def test_o6_gradient_matches_finite_differences(causal):
+    """The gradient formulas (softmax Jacobian with constant multiplicities)
+    against central differences of the block-walk estimate lsh_estimate, an
+    independent formulation of the forward pass, for every input element."""
+    rng = np.random.default_rng(61 + causal)
+    n, d = 18, 3
+    q, k, v = _rand_qkv(rng, 1, 2, 1, n, d, scale=0.8)
+    do = rng.standard_normal(q.shape)
+    _, tables = _tables(7, [3.0, 8.0], 3, n)
+    dq, dk, dv = orc.lsh_estimate_grad(q, k, v, do, tables, causal)
+
+    def loss(qq, kk, vv):
+        return float((do * orc.lsh_estimate(qq, kk, vv, tables, causal)).sum())
+
+    eps = 1e-6
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += eps
+            a2[idx] -= eps
+            args1 = [q, k, v]; args2 = [q, k, v]
+            args1[which] = a1; args2[which] = a2
+            num[idx] = (loss(*args1) - loss(*args2)) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_o6_row_and_key_subsets_match_dense_gradient(causal):
+    rng = np.random.default_rng(71 + causal)
+    n, d = 150, 8
+    q, k, v = _rand_qkv(rng, 2, 4, 2, n, d, scale=0.5)
+    do = rng.standard_normal(q.shape)
+    _, tables = _tables(13, [1.5, 6.0, 20.0, 90.0], 5, n)
+    dq, dk, dv = orc.lsh_estimate_grad(q, k, v, do, tables, causal)
+    rows = np.array([0, 1, 37, 98, 149])
+    np.testing.assert_allclose(orc.lsh_grad_rows(q, k, v, do, tables, causal, rows), dq[:, :, rows],
+                               rtol=1e-10, atol=1e-12)
+    gk, gv = orc.lsh_grad_keys(q, k, v, do, tables, causal, rows)
+    np.testing.assert_allclose(gk, dk[:, :, rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(gv, dv[:, :, rows], rtol=1e-10, atol=1e-12)
