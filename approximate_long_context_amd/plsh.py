@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "PLSH_OK", 1: "PLSH_ERR_ARG", 2: "PLSH_ERR_TABLE", 3: "PLSH_E
 
 EXPORTED = ["plsh_sample_tables", "plsh_build_tables", "plsh_validate_tables", "plsh_count_work",
             "plsh_alibi_attention", "plsh_debug_block_intervals",
-            "plsh_debug_attention_reference", "plsh_alibi_attention_unfused", "plsh_exact_alibi_attention",
+            "plsh_debug_attention_reference", "plsh_alibi_attention_unfused",
+            "plsh_alibi_attention_backward", "plsh_exact_alibi_attention",
             "plsh_kernel_timer", "plsh_kernel_timer_read", "plsh_last_error"]
 
 
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.plsh_alibi_attention.argtypes = attn
         L.plsh_debug_attention_reference.argtypes = attn
         L.plsh_alibi_attention_unfused.argtypes = attn
+        L.plsh_alibi_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                    ctypes.c_int, vp, i32, TP, i32, vp]
         L.plsh_debug_block_intervals.argtypes = [TP, vp, vp]
         L.plsh_exact_alibi_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                                                  vp, i32, vp]
@@ -216,6 +219,31 @@ def attention_unfused(q, k, v, sigma, s, tables: DeviceTables, causal: bool = Fa
     """plsh_alibi_attention_unfused: s single-sample passes plus a
     log-sum-exp combine (ablation of the sample fusion)."""
     return _attention(lib().plsh_alibi_attention_unfused, q, k, v, sigma, s, tables, causal, out, stream)
+
+
+def attention_backward(q, k, v, dout, sigma, s, tables: DeviceTables, causal: bool = False,
+                       stream: Optional[int] = None):
+    """plsh_alibi_attention_backward: (dq, dk, dv) for the upstream gradient
+    dout of plsh_alibi_attention's output (fixed tables)."""
+    for name, x in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        if not x.is_contiguous():
+            raise PlshError(PLSH_ERR_ARG, f"{name} must be contiguous")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or dout.shape != q.shape or \
+            len({q.dtype, k.dtype, v.dtype, dout.dtype}) != 1:
+        raise PlshError(PLSH_ERR_ARG, "q/dout [B,H,n,d], k/v [B,Hkv,n,d] with one dtype expected")
+    B, H, n, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    sig = np.ascontiguousarray(sigma, dtype=np.float64)
+    if sig.size != H:
+        raise PlshError(PLSH_ERR_ARG, "sigma must have one entry per query head")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = tables.c_struct()
+    _check(lib().plsh_alibi_attention_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, n, H,
+                                               k.shape[1], d, _dtype_code(q), _ptr(sig), s,
+                                               ctypes.byref(st), int(bool(causal)), stream))
+    return dq, dk, dv
 
 
 def exact_alibi_attention(q, k, v, sigma, causal: bool = False, out: Optional[torch.Tensor] = None,

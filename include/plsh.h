@@ -192,6 +192,38 @@ plsh_status plsh_debug_block_intervals(const plsh_tables *boundaries, int32_t *l
                                        plsh_stream_t stream);
 
 /*
+ * plsh_alibi_attention_backward -- gradients of the estimate of
+ * plsh_alibi_attention for fixed tables (the pages train with the method,
+ * Experimental Validation).  With P_ij = c_ij e^{q_i.k_j} / sum_l c_il
+ * e^{q_i.k_l} (c from the tables, a constant) and the upstream gradient dO:
+ *   dV_j = sum_i P_ij dO_i,  dS_ij = P_ij (dO_i.v_j - dO_i.O_i),
+ *   dQ_i = sum_j dS_ij k_j,  dK_j = sum_i dS_ij q_i,
+ * dK and dV summed over the query heads of each GQA group.
+ *   dout        DEVICE [batch, heads, n, d], the dtype of q
+ *   dq          DEVICE [batch, heads, n, d] output
+ *   dk, dv      DEVICE [batch, kv_heads, n, d] outputs
+ *   the other arguments as for plsh_alibi_attention; bf16, s <= 124.
+ * Launches: a pass of the estimator keeping O in fp32 and each row's
+ * normaliser; a per-row pass for D_i = dO_i.O_i; the dQ kernel (rows as in
+ * the estimator); the dK/dV kernel (key positions in place of rows, using
+ * c_ij = c_ji; one workgroup per 128 key positions of a KV head, looping over
+ * that head's query heads).  Each kernel is preceded by its block-edge
+ * pre-pass.  dq, dk, dv are written whole (no accumulation into them).
+ * Device memory: 4 * (batch*heads*n*(d + 1) + 2*batch*heads*ceil32(n)) bytes
+ * of statistics from the stream-ordered allocator on `stream`, released
+ * within the call, plus the pre-pass workspaces.  dout, dk, dv 16-byte
+ * aligned; dq, dk, dv must not overlap q, k, v, dout or each other.
+ * Errors: as plsh_alibi_attention (null dout, dq, dk or dv, misalignment and
+ * aliasing: PLSH_ERR_ARG), and PLSH_ERR_UNSUPPORTED for fp32 or s > 124.
+ */
+plsh_status plsh_alibi_attention_backward(const void *q, const void *k, const void *v,
+                                          const void *dout, void *dq, void *dk, void *dv,
+                                          int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                          int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                          const plsh_tables *boundaries, int32_t causal,
+                                          plsh_stream_t stream);
+
+/*
  * plsh_alibi_attention_unfused -- the same estimate computed the way the
  * pages state the reduction (Methodology §3, Theorem 2.2: s short-context
  * attentions without positional bias): for each sample k a pass over every

@@ -445,3 +445,93 @@ def test_unfused_full_size_sampled_rows(dev):
     rows = W.sample_rows(w.n, 32, seed=29)
     o, ref = run_unfused(dev, w, rows=rows)
     check_bf16(o, ref, what="unfused mistral")
+
+
+# ------------------------------------------------------------ backward ---
+def grad_inputs(w: W.Workload, seed: int = 3):
+    q, k, v = W.make_qkv(w)
+    g = torch.Generator().manual_seed(seed)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    t = plsh.sample_tables(w.hash_seed, w.n, w.sigma, w.s)
+    off, st = orc.tables_from_params(w.n, t.params)
+    tabs = orc.starts_per_head(off, st, w.heads, w.s)
+    return q, k, v, do, t, tabs
+
+
+def check_grad(gpu, ref, what, tol=2e-2, floor=0.0):
+    """max |gpu - ref| relative to max(max |ref|, floor), per (batch, head)
+    slab.  floor is for references that vanish by cancellation (n = 1: P = 1,
+    so dP - D = 0 exactly, while the GPU forms dP = dO.V and D = dO.O in two
+    fp32 sums): there the error is measured against the size of the terms that
+    cancel."""
+    worst = 0.0
+    for b in range(ref.shape[0]):
+        for h in range(ref.shape[1]):
+            den = max(float(np.abs(ref[b, h]).max()), floor)
+            err = float(np.abs(gpu[b, h] - ref[b, h]).max())
+            worst = max(worst, err / den if den > 0 else (0.0 if err == 0 else np.inf))
+    say(what, f"grad rel err={worst:.3e}")
+    assert worst <= tol, (what, worst)
+
+
+def cancel_floor(q, k, v, do):
+    """2^-16 times a bound on |dP| |k| and |dP| |q| (|dP| <= d max|dO| max|V|):
+    fp32 rounding of sums of such terms stays far below it."""
+    d = q.shape[-1]
+    qf, kf, vf, df = (float(x.float().abs().max()) for x in (q, k, v, do))
+    return 2.0 ** -16 * d * df * vf * max(qf, kf)
+
+
+def run_backward(dev, w, causal):
+    q, k, v, do, t, tabs = grad_inputs(w)
+    say(w.name, "backward", "n", w.n, "d", w.d, "heads", w.heads, w.kv_heads, "s", w.s, "causal", causal)
+    dq, dk, dv = plsh.attention_backward(q.to(dev), k.to(dev), v.to(dev), do.to(dev), w.sigma, w.s, t.to(dev),
+                                         causal=causal)
+    torch.cuda.synchronize()
+    return (q, k, v, do, tabs), (W.to_f64(dq), W.to_f64(dk), W.to_f64(dv))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_oracle(dev, d, causal):
+    """Gradients of the estimate for fixed tables: GQA (two query heads per
+    KV head), n = 700 (several 128-position tiles and a ragged tail), sigma
+    from a few positions to the whole sequence."""
+    w = small("bwd", 2, 4, 2, 700, d, "bf16", causal, [1.3, 9.0, 60.0, 700.0], 7)
+    (q, k, v, do, tabs), (gq, gk, gv) = run_backward(dev, w, causal)
+    rq, rk, rv = orc.lsh_estimate_grad(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do), tabs, causal)
+    check_grad(gq, rq, f"dq d={d} causal={causal}")
+    check_grad(gk, rk, f"dk d={d} causal={causal}")
+    check_grad(gv, rv, f"dv d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("n,causal", [(1, False), (1, True), (31, True), (333, False), (333, True)])
+def test_backward_ragged_gqa(dev, n, causal):
+    """Odd lengths (a head's statistics rows not a multiple of 4), three
+    query heads per KV head, and n = 1 (P = 1: dq = dk = 0, dv = dout)."""
+    w = small("bwd-ragged", 1, 6, 2, n, 64, "bf16", causal, [0.7, 3.0, 17.0, 90.0, 400.0, 5000.0], 5)
+    (q, k, v, do, tabs), (gq, gk, gv) = run_backward(dev, w, causal)
+    rq, rk, rv = orc.lsh_estimate_grad(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do), tabs, causal)
+    fl = cancel_floor(q, k, v, do)
+    check_grad(gq, rq, f"dq n={n} causal={causal}", floor=fl)
+    check_grad(gk, rk, f"dk n={n} causal={causal}", floor=fl)
+    check_grad(gv, rv, f"dv n={n} causal={causal}")
+
+
+def test_backward_full_size_sampled(dev):
+    """The 32-head, n = 16384, s = 20 causal workload: dq at sampled rows of
+    every head, dk and dv at sampled keys of the lightest and heaviest KV
+    heads (the oracle walks every row sharing a block with each key)."""
+    w = W.get("mistral-7b-n16384-s20")
+    (q, k, v, do, tabs), (gq, gk, gv) = run_backward(dev, w, w.causal)
+    qf, kf, vf, dof = W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do)
+    rows = W.sample_rows(w.n, 16, seed=31)
+    rq = orc.lsh_grad_rows(qf, kf, vf, dof, tabs, w.causal, rows)
+    check_grad(gq[:, :, rows], rq, "dq mistral sampled rows")
+    keys = W.sample_rows(w.n, 6, seed=37)
+    grp = w.heads // w.kv_heads
+    for g in (0, w.kv_heads - 1):
+        hs = slice(g * grp, (g + 1) * grp)
+        rk, rv = orc.lsh_grad_keys(qf[:, hs], kf[:, g:g + 1], vf[:, g:g + 1], dof[:, hs], tabs[hs], w.causal, keys)
+        check_grad(gk[:, g:g + 1][:, :, keys], rk, f"dk mistral kv head {g}")
+        check_grad(gv[:, g:g + 1][:, :, keys], rv, f"dv mistral kv head {g}")

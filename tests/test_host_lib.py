@@ -247,6 +247,53 @@ def test_exact_attention_rejects_bad_sigma_and_needs_a_device():
         assert st == plsh.PLSH_ERR_HIP, msg
 
 
+def _bwd_call(**over):
+    L, a, keep = _attn_args(**over)
+    b = dict(dout=0x50000, dq=0x60000, dk=0x70000, dv=0x80000)
+    b.update({k: v for k, v in over.items() if k in b})
+    st = L.plsh_alibi_attention_backward(a["q"], a["k"], a["v"], b["dout"], b["dq"], b["dk"], b["dv"],
+                                         a["batch"], a["n"], a["heads"], a["kv_heads"], a["d"], a["dtype"],
+                                         a["sigma"], a["s"], a["tables"], a["causal"], a["stream"])
+    return st, L.plsh_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dout=None), plsh.PLSH_ERR_ARG),
+    (dict(dq=None), plsh.PLSH_ERR_ARG),
+    (dict(dk=None), plsh.PLSH_ERR_ARG),
+    (dict(dv=None), plsh.PLSH_ERR_ARG),
+    (dict(dk=0x70008), plsh.PLSH_ERR_ARG),
+    (dict(dq=0x50000 + 128), plsh.PLSH_ERR_ARG),   # dq overlaps dout
+    (dict(dk=0x20000), plsh.PLSH_ERR_ARG),         # dk is k
+    (dict(dv=0x70000 + 64), plsh.PLSH_ERR_ARG),    # dv overlaps dk
+    (dict(n=0), plsh.PLSH_ERR_ARG),
+    (dict(d=96), plsh.PLSH_ERR_UNSUPPORTED),
+    (dict(dtype=plsh.PLSH_F32), plsh.PLSH_ERR_UNSUPPORTED),
+])
+def test_backward_argument_errors(over, status):
+    """plsh_alibi_attention_backward rejects bad arguments before any launch
+    (q, k, v, dout at 64 KiB steps; each gradient 16 KiB at most here)."""
+    st, msg = _bwd_call(**over)
+    assert st == status, msg
+    assert msg
+
+
+def test_backward_rejects_more_than_124_samples():
+    L, a, keep = _attn_args()
+    params = np.zeros((4 * 125, 2))
+    tb = plsh._Tables(64, 4, 125, params.ctypes.data, None, None)
+    st, msg = _bwd_call(s=125, tables=ctypes.byref(tb))
+    assert st == plsh.PLSH_ERR_UNSUPPORTED, msg
+
+
+def test_backward_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, msg = _bwd_call()
+    assert st == plsh.PLSH_ERR_HIP, msg
+
+
 @pytest.mark.parametrize("width", [1.0, 7.0, 7.5, 64.0, 1e6])
 def test_fixed_block_tables_match_oracle_scan(width):
     """Fixed blocks (pitch w, offset 0) through plsh_build_tables equal the
