@@ -3,7 +3,9 @@
     python -m approximate_long_context_amd.build
 
 Device code is compiled without fast-math (the block predicate must be
-bit-exact with the host table) and without packed-fp32 instructions.
+bit-exact with the host table) and without packed-fp32 instructions; the
+device sampler (plsh_sample.hip) also without contraction of multiply-adds
+(its draws must round exactly as the host sampler's).
 """
 
 from __future__ import annotations
@@ -42,8 +44,12 @@ def build(verbose: bool = False) -> str:
     _run(["g++", "-std=c++17", "-O2", "-fPIC", "-ffp-contract=off", "-Wall", "-c",
           os.path.join(CSRC, "plsh_host.cpp"), "-o", host_obj])
     _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "plsh_attention.hip"), "-o", dev_obj])
+    # the device sampler: no contraction, so its draws round as the host's
+    samp_obj = os.path.join(objdir, "plsh_sample.o")
+    _run([HIPCC, *COMMON, *DEVICE, "-ffp-contract=off", "-c", os.path.join(CSRC, "plsh_sample.hip"),
+          "-o", samp_obj])
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", host_obj, dev_obj, "-o", tmp])
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", host_obj, dev_obj, samp_obj, "-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -38,6 +38,7 @@
 
 #include "plsh_binning.h"
 #include "plsh_internal.h"
+#include "plsh_hip_status.h"
 
 namespace plsh {
 namespace dev {
@@ -67,12 +68,17 @@ struct AttnArgs {
   // n]) instead of bf16 out
   float *o32;
   float *lse;
-  // backward (attn_dq_kernel): the upstream gradient dO ([batch, heads, n,
-  // d], the dtype of q), each row's normaliser in log2 units lse2 = log2
-  // sum_j c_ij 2^(q_i.k_j log2 e), and D_i = dO_i . O_i ([batch, heads, n])
+  // backward: the upstream gradient dO ([batch, heads, n, d], the dtype of
+  // q), each row's normaliser in log2 units lse2 = log2 sum_j c_ij 2^(q_i.k_j
+  // log2 e), and D_i = dO_i . O_i, both [batch, heads, ns] with ns = n rounded
+  // up to a multiple of 32 (rows n .. ns - 1 hold 0).  When stat_lse2 is set
+  // the MFMA kernel writes these two arrays (stat_lse2, stat_dvec) instead of
+  // out; the dQ and dK/dV kernels read them (lse2, dvec).
   const void *dout;
   const float *lse2;
   const float *dvec;
+  float *stat_lse2;
+  float *stat_dvec;
   int32_t order[kMaxHeadsArg];  // head processed in slot i, heaviest sigma first
 };
 
@@ -1001,10 +1007,37 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   // The wave's 16 x D output block is staged in LDS (in the two ring slots
   // the last pair does not use: every wave is past them), then written whole
   // rows per instruction.
-  if (!active) return;
+  const int ns = (n + 31) & ~31;
+  const int64_t srow = ((int64_t)b * a.heads + h) * ns + r0 + qc;
+  if (!active) {
+    if (a.stat_lse2 && r0 < ns && gq == 0) a.stat_lse2[srow] = a.stat_dvec[srow] = 0.f;
+    return;
+  }
   float ltot = lsum + xor16_f(lsum);
   ltot += other_half_f(ltot, lane);
   const float inv = 1.0f / ltot;
+  if (a.stat_lse2) {
+    // backward statistics of the row: lse2 and D = dO . O (O in fp32, before
+    // its rounding); the lane holds dims 16 db + 4 gq .. + 3
+    const int io = r0 + qc;
+    const uint16_t *dOr = (const uint16_t *)a.dout + (((int64_t)b * a.heads + h) * n + min(io, n - 1)) * D + 4 * gq;
+    float acc = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const u32x2 raw = *(const u32x2 *)(dOr + 16 * db);
+      acc = fmaf(__uint_as_float(raw[0] << 16), oacc[db][0], acc);
+      acc = fmaf(__uint_as_float(raw[0] & 0xFFFF0000u), oacc[db][1], acc);
+      acc = fmaf(__uint_as_float(raw[1] << 16), oacc[db][2], acc);
+      acc = fmaf(__uint_as_float(raw[1] & 0xFFFF0000u), oacc[db][3], acc);
+    }
+    acc += xor16_f(acc);
+    acc += other_half_f(acc, lane);
+    if (gq == 0) {
+      a.stat_lse2[srow] = io < n ? m2 + __log2f(ltot) : 0.f;
+      a.stat_dvec[srow] = io < n ? acc * inv : 0.f;
+    }
+    return;
+  }
   if (a.o32) {
     // fp32 partials for a log-sum-exp combine: O (normalised) and lse, in
     // natural-log units (the running max m2 is in log2 units)
@@ -1778,7 +1811,7 @@ void attn_dkv_kernel(AttnArgs a, const uint8_t *ws, uint16_t *dk_out, uint16_t *
     start += cnt;
   }
   const int g = start + (tu - t0c) / 8;
-  const int kvh = unit / a.batch;
+  const int kvh = a.order[unit / a.batch];  // KV heads here, heaviest group first
   const int b = unit % a.batch;
   const int grpsz = a.heads / a.kv_heads;
   const int grp = wave >> 1, half = wave & 1;
@@ -2096,34 +2129,6 @@ void attn_dkv_kernel(AttnArgs a, const uint8_t *ws, uint16_t *dk_out, uint16_t *
   }
 }
 
-// Backward statistics: D_i = dO_i . O_i (O recomputed in fp32 by a pass of the
-// estimator) and the normaliser in log2 units, lse2 = lse / ln 2.  Both go to
-// arrays whose heads are padded with zeros to ns = a multiple of 32 rows.
-// One wave per padded row; lane l holds dims l, l + 64.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t *dout, const float *o32, const float *lse,
-                                                       float *lse2, float *dvec, int n, int ns, int64_t heads) {
-  const int64_t prow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (prow >= heads * ns) return;
-  const int64_t bh = prow / ns;
-  const int i = (int)(prow - bh * ns);
-  const int lane = threadIdx.x & 63;
-  float acc = 0.f, l2 = 0.f;
-  if (i < n) {
-    const int64_t row = bh * n + i;
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e)
-      acc = fmaf(bf16_bits_to_f32(dout[row * D + lane + 64 * e]), o32[row * D + lane + 64 * e], acc);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    l2 = lse[row] * kLog2e;
-  }
-  if (lane == 0) {
-    dvec[prow] = acc;
-    lse2[prow] = l2;
-  }
-}
-
 }  // namespace dev
 
 // ---------------------------------------------------------------------------
@@ -2191,6 +2196,8 @@ void fill_args(dev::AttnArgs &a, const void *q, const void *k, const void *v, vo
   a.dout = nullptr;
   a.lse2 = nullptr;
   a.dvec = nullptr;
+  a.stat_lse2 = nullptr;
+  a.stat_dvec = nullptr;
   // heavy heads first: per-row work grows with sigma
   int idx[dev::kMaxHeadsArg];
   std::iota(idx, idx + heads, 0);
@@ -2223,22 +2230,6 @@ std::pair<hipEvent_t, hipEvent_t> *timer_slot() {
   return &g_timer.ev[g_timer.used++];
 }
 
-plsh_status launch_check(const char *who) {
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PLSH_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
-  return PLSH_OK;
-}
-
-plsh_status have_device(const char *who) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(PLSH_ERR_HIP, "%s: no HIP device: %s", who, hipGetErrorString(e));
-  }
-  return PLSH_OK;
-}
-
 plsh_status launch_valu(const dev::AttnArgs &a, int d, plsh_dtype dtype, int causal, hipStream_t st,
                         const char *who) {
   const size_t shm = 4 * dev::valu_wave_bytes(a.s, d);
@@ -2256,65 +2247,83 @@ plsh_status launch_valu(const dev::AttnArgs &a, int d, plsh_dtype dtype, int cau
   return launch_check(who);
 }
 
-// mode 0: the estimator (attn_mfma_kernel); 1: its backward dQ (attn_dq_kernel);
-// 2: its backward dK, dV into dk, dv (attn_dkv_kernel, over non-causal records)
-plsh_status launch_mfma(const dev::AttnArgs &a, int d, int causal, hipStream_t st, const char *who, int mode = 0,
-                        void *dk = nullptr, void *dv = nullptr) {
+// The block-edge records of every (head, 32-row group), causal or not, into a
+// workspace from the stream-ordered allocator (released by free_records).
+plsh_status build_records(const dev::AttnArgs &a, bool causal, hipStream_t st, const char *who, void **ws) {
   const int g32 = (a.n + 31) / 32;
   const size_t ws_bytes = (size_t)a.heads * g32 * dev::rec_bytes(a.s);
-  void *ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, ws_bytes, st);
+  *ws = nullptr;
+  hipError_t e = hipMallocAsync(ws, ws_bytes, st);
   if (e != hipSuccess) {
     (void)hipGetLastError();
+    *ws = nullptr;
     return fail(PLSH_ERR_HIP, "%s: workspace allocation of %zu bytes failed: %s", who, ws_bytes,
                 hipGetErrorString(e));
   }
   const int items = a.heads * g32;
   const dim3 egrid((unsigned)((items + 3) / 4)), eblock(256);
   const size_t eshm = 4 * (dev::wavetab_bytes(a.s) + 32 * 16 * 4);
-  if (causal && mode != 2) hipLaunchKernelGGL(dev::edges_kernel<true>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)ws);
-  else hipLaunchKernelGGL(dev::edges_kernel<false>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)ws);
-  plsh_status rc = launch_check(who);
-  if (rc == PLSH_OK) {
-    const int64_t units = mode == 2 ? (int64_t)a.batch * a.kv_heads : (int64_t)a.batch * a.heads;
-    const dim3 grid((unsigned)(a.groups * units)), block(64 * dev::kWaves);
-    const uint8_t *w8 = (const uint8_t *)ws;
-    const size_t shm = 4 * dev::ev_wave_bytes(a.s, causal != 0 && mode != 2);
-    auto *tm = timer_slot();
-    if (tm) (void)hipEventRecord(tm->first, st);
-    if (mode == 2) {
-      uint16_t *k16 = (uint16_t *)dk, *v16 = (uint16_t *)dv;
-      if (d == 64) {
-        if (causal) hipLaunchKernelGGL((dev::attn_dkv_kernel<64, true>), grid, block, shm, st, a, w8, k16, v16);
-        else hipLaunchKernelGGL((dev::attn_dkv_kernel<64, false>), grid, block, shm, st, a, w8, k16, v16);
-      } else {
-        if (causal) hipLaunchKernelGGL((dev::attn_dkv_kernel<128, true>), grid, block, shm, st, a, w8, k16, v16);
-        else hipLaunchKernelGGL((dev::attn_dkv_kernel<128, false>), grid, block, shm, st, a, w8, k16, v16);
-      }
-    } else if (mode == 1) {
-      if (d == 64) {
-        if (causal) hipLaunchKernelGGL((dev::attn_dq_kernel<64, true>), grid, block, shm, st, a, w8);
-        else hipLaunchKernelGGL((dev::attn_dq_kernel<64, false>), grid, block, shm, st, a, w8);
-      } else {
-        if (causal) hipLaunchKernelGGL((dev::attn_dq_kernel<128, true>), grid, block, shm, st, a, w8);
-        else hipLaunchKernelGGL((dev::attn_dq_kernel<128, false>), grid, block, shm, st, a, w8);
-      }
-    } else if (d == 64) {
-      if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<64, true>), grid, block, shm, st, a, w8);
-      else hipLaunchKernelGGL((dev::attn_mfma_kernel<64, false>), grid, block, shm, st, a, w8);
-    } else {
-      if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<128, true>), grid, block, shm, st, a, w8);
-      else hipLaunchKernelGGL((dev::attn_mfma_kernel<128, false>), grid, block, shm, st, a, w8);
-    }
-    if (tm) (void)hipEventRecord(tm->second, st);
-    rc = launch_check(who);
-  }
-  e = hipFreeAsync(ws, st);
+  if (causal) hipLaunchKernelGGL(dev::edges_kernel<true>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)*ws);
+  else hipLaunchKernelGGL(dev::edges_kernel<false>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)*ws);
+  return launch_check(who);
+}
+
+plsh_status free_records(void *ws, hipStream_t st, const char *who, plsh_status rc) {
+  if (!ws) return rc;
+  const hipError_t e = hipFreeAsync(ws, st);
   if (e != hipSuccess && rc == PLSH_OK) {
     (void)hipGetLastError();
     return fail(PLSH_ERR_HIP, "%s: workspace release failed: %s", who, hipGetErrorString(e));
   }
   return rc;
+}
+
+// One MFMA kernel over records ws (causal records for modes 0 and 1 of a
+// causal call, non-causal ones otherwise).  mode 0: the estimator
+// (attn_mfma_kernel); 1: its backward dQ (attn_dq_kernel); 2: its backward
+// dK, dV into dk, dv (attn_dkv_kernel).
+plsh_status launch_attn(const dev::AttnArgs &a, int d, int causal, hipStream_t st, const char *who, int mode,
+                        const void *ws, void *dk = nullptr, void *dv = nullptr) {
+  const int64_t units = mode == 2 ? (int64_t)a.batch * a.kv_heads : (int64_t)a.batch * a.heads;
+  const dim3 grid((unsigned)(a.groups * units)), block(64 * dev::kWaves);
+  const uint8_t *w8 = (const uint8_t *)ws;
+  const size_t shm = 4 * dev::ev_wave_bytes(a.s, causal != 0 && mode != 2);
+  auto *tm = timer_slot();
+  if (tm) (void)hipEventRecord(tm->first, st);
+  if (mode == 2) {
+    uint16_t *k16 = (uint16_t *)dk, *v16 = (uint16_t *)dv;
+    if (d == 64) {
+      if (causal) hipLaunchKernelGGL((dev::attn_dkv_kernel<64, true>), grid, block, shm, st, a, w8, k16, v16);
+      else hipLaunchKernelGGL((dev::attn_dkv_kernel<64, false>), grid, block, shm, st, a, w8, k16, v16);
+    } else {
+      if (causal) hipLaunchKernelGGL((dev::attn_dkv_kernel<128, true>), grid, block, shm, st, a, w8, k16, v16);
+      else hipLaunchKernelGGL((dev::attn_dkv_kernel<128, false>), grid, block, shm, st, a, w8, k16, v16);
+    }
+  } else if (mode == 1) {
+    if (d == 64) {
+      if (causal) hipLaunchKernelGGL((dev::attn_dq_kernel<64, true>), grid, block, shm, st, a, w8);
+      else hipLaunchKernelGGL((dev::attn_dq_kernel<64, false>), grid, block, shm, st, a, w8);
+    } else {
+      if (causal) hipLaunchKernelGGL((dev::attn_dq_kernel<128, true>), grid, block, shm, st, a, w8);
+      else hipLaunchKernelGGL((dev::attn_dq_kernel<128, false>), grid, block, shm, st, a, w8);
+    }
+  } else if (d == 64) {
+    if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<64, true>), grid, block, shm, st, a, w8);
+    else hipLaunchKernelGGL((dev::attn_mfma_kernel<64, false>), grid, block, shm, st, a, w8);
+  } else {
+    if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<128, true>), grid, block, shm, st, a, w8);
+    else hipLaunchKernelGGL((dev::attn_mfma_kernel<128, false>), grid, block, shm, st, a, w8);
+  }
+  if (tm) (void)hipEventRecord(tm->second, st);
+  return launch_check(who);
+}
+
+// The estimator: its records, then attn_mfma_kernel.
+plsh_status launch_mfma(const dev::AttnArgs &a, int d, int causal, hipStream_t st, const char *who) {
+  void *ws = nullptr;
+  plsh_status rc = build_records(a, causal != 0, st, who, &ws);
+  if (rc == PLSH_OK) rc = launch_attn(a, d, causal, st, who, 0, ws);
+  return free_records(ws, st, who, rc);
 }
 
 // Exact ALiBi: the same checks as the estimator minus the table, bf16 only.
@@ -2520,43 +2529,53 @@ extern "C" plsh_status plsh_alibi_attention_backward(const void *q, const void *
     return fail(PLSH_ERR_UNSUPPORTED, "%s: bf16 with s <= %d only", who, dev::kMaxMfmaSamples);
   if ((st = have_device(who)) != PLSH_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
-  const int64_t rows = (int64_t)batch * heads * n;
   const int ns = (n + 31) & ~31;
   const int64_t prows = (int64_t)batch * heads * ns;
-  const size_t bytes = ((size_t)rows * ((size_t)d + 1) + 2 * (size_t)prows) * sizeof(float);
-  void *ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, hs);
+  const size_t bytes = 2 * (size_t)prows * sizeof(float);
+  void *stats = nullptr;
+  hipError_t e = hipMallocAsync(&stats, bytes, hs);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(PLSH_ERR_HIP, "%s: statistics allocation of %zu bytes failed: %s", who, bytes, hipGetErrorString(e));
   }
-  float *o32 = (float *)ws;
-  float *lse = o32 + (size_t)rows * d;
-  float *lse2 = lse + rows;
+  float *lse2 = (float *)stats;
   float *dvec = lse2 + prows;
   dev::AttnArgs a;
   fill_args(a, q, k, v, dq, batch, n, heads, kv_heads, sigma, s, boundaries);
-  // statistics: the estimate in fp32 and each row's normaliser
-  a.o32 = o32;
-  a.lse = lse;
-  plsh_status rc = launch_mfma(a, d, causal != 0, hs, who);
+  a.dout = dout;
+  // the records of the estimator serve its statistics pass and dQ; dK/dV
+  // takes non-causal ones (the same records when the call is not causal)
+  void *rec = nullptr, *rec_nc = nullptr;
+  plsh_status rc = build_records(a, causal != 0, hs, who, &rec);
   if (rc == PLSH_OK) {
-    const dim3 grid((unsigned)((prows + 3) / 4)), block(256);
-    const int64_t bh = (int64_t)batch * heads;
-    if (d == 64) hipLaunchKernelGGL(dev::bwd_prep_kernel<64>, grid, block, 0, hs, (const uint16_t *)dout, o32, lse, lse2, dvec, n, ns, bh);
-    else hipLaunchKernelGGL(dev::bwd_prep_kernel<128>, grid, block, 0, hs, (const uint16_t *)dout, o32, lse, lse2, dvec, n, ns, bh);
-    rc = launch_check(who);
+    // statistics: each row's normaliser and D = dO . O
+    a.stat_lse2 = lse2;
+    a.stat_dvec = dvec;
+    rc = launch_attn(a, d, causal != 0, hs, who, 0, rec);
   }
   if (rc == PLSH_OK) {
-    a.o32 = nullptr;
-    a.lse = nullptr;
-    a.dout = dout;
+    a.stat_lse2 = nullptr;
+    a.stat_dvec = nullptr;
     a.lse2 = lse2;
     a.dvec = dvec;
-    rc = launch_mfma(a, d, causal != 0, hs, who, 1);
+    rc = launch_attn(a, d, causal != 0, hs, who, 1, rec);
   }
-  if (rc == PLSH_OK) rc = launch_mfma(a, d, causal != 0, hs, who, 2, dk, dv);
-  e = hipFreeAsync(ws, hs);
+  if (rc == PLSH_OK && causal) rc = build_records(a, false, hs, who, &rec_nc);
+  if (rc == PLSH_OK) {
+    // dK/dV workgroups run per KV head: the group with the largest summed
+    // sigma first
+    const int grp = heads / kv_heads;
+    std::vector<double> w(kv_heads, 0.0);
+    for (int h = 0; h < heads; ++h) w[h / grp] += sigma[h];
+    int idx[dev::kMaxHeadsArg];
+    std::iota(idx, idx + kv_heads, 0);
+    std::stable_sort(idx, idx + kv_heads, [&](int x, int y) { return w[x] > w[y]; });
+    for (int i = 0; i < dev::kMaxHeadsArg; ++i) a.order[i] = i < kv_heads ? idx[i] : 0;
+    rc = launch_attn(a, d, causal != 0, hs, who, 2, causal ? rec_nc : rec, dk, dv);
+  }
+  rc = free_records(rec_nc, hs, who, rc);
+  rc = free_records(rec, hs, who, rc);
+  e = hipFreeAsync(stats, hs);
   if (e != hipSuccess && rc == PLSH_OK) {
     (void)hipGetLastError();
     return fail(PLSH_ERR_HIP, "%s: statistics release failed: %s", who, hipGetErrorString(e));

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "plsh_binning.h"
+#include "plsh_draw.h"
 #include "plsh_internal.h"
 
 namespace plsh {
@@ -37,22 +38,6 @@ plsh_status fail(plsh_status st, const char *fmt, ...) {
 void clear_error() { g_last_error.clear(); }
 
 namespace {
-
-// SplitMix64 (Steele, Lea & Flood 2014) read as a counter-based generator:
-// output #i of the stream started at state `seed`.
-inline uint64_t splitmix64_at(uint64_t seed, uint64_t i) {
-  uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-
-inline double unit_open(uint64_t z) { return ((double)(z >> 11) + 0.5) * 0x1p-53; }
-inline double unit_halfopen(uint64_t z) { return (double)(z >> 11) * 0x1p-53; }
-
-inline uint64_t draw_index(uint64_t head, uint64_t sample, uint64_t j) {
-  return ((head << 32) | sample) * 4 + j;
-}
 
 // Block starts of one hash: 0, each bin change, n.  Walks block by block.
 void hash_starts(int32_t n, double delta, double u, std::vector<int32_t> &out) {
@@ -95,11 +80,8 @@ extern "C" plsh_status plsh_sample_tables(uint64_t seed, int32_t n, int32_t head
   for (int32_t h = 0; h < heads; ++h) {
     const double sg = sigma[h];
     for (int32_t k = 0; k < s; ++k) {
-      const double u1 = unit_open(splitmix64_at(seed, draw_index(h, k, 0)));
-      const double u2 = unit_open(splitmix64_at(seed, draw_index(h, k, 1)));
-      const double u3 = unit_halfopen(splitmix64_at(seed, draw_index(h, k, 2)));
-      const double delta = -sg * (log(u1) + log(u2));   // Erlang-2 = Gamma(2, sigma)
-      const double u = delta * u3;                       // U[0, delta)
+      double delta, u;  // Erlang-2 = Gamma(2, sigma) pitch, offset in [0, delta)
+      draw::hash_params(seed, (uint64_t)h, (uint64_t)k, sg, &delta, &u);
       const int64_t r = (int64_t)h * s + k;
       params[2 * r] = delta;
       params[2 * r + 1] = u;

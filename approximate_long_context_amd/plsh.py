@@ -27,7 +27,7 @@ EXPORTED = ["plsh_sample_tables", "plsh_build_tables", "plsh_validate_tables", "
             "plsh_alibi_attention", "plsh_debug_block_intervals",
             "plsh_debug_attention_reference", "plsh_alibi_attention_unfused",
             "plsh_alibi_attention_backward", "plsh_exact_alibi_attention",
-            "plsh_kernel_timer", "plsh_kernel_timer_read", "plsh_last_error"]
+            "plsh_sample_params_device", "plsh_kernel_timer", "plsh_kernel_timer_read", "plsh_last_error"]
 
 
 class PlshError(RuntimeError):
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         L.plsh_debug_block_intervals.argtypes = [TP, vp, vp]
         L.plsh_exact_alibi_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                                                  vp, i32, vp]
+        L.plsh_sample_params_device.argtypes = [u64, i32, vp, i32, vp, vp]
         L.plsh_kernel_timer.argtypes = [i32]
         L.plsh_kernel_timer_read.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]
         for f in EXPORTED[:-1]:
@@ -141,6 +142,28 @@ def sample_tables(seed: int, n: int, sigma: Sequence[float], s: int) -> Tables:
     _check(L.plsh_sample_tables(seed, n, heads, _ptr(sig), s, _ptr(params), _ptr(offsets),
                                 _ptr(starts), starts.size, ctypes.byref(need)))
     return Tables(n, heads, s, params, offsets, starts[:need.value])
+
+
+def sample_params_device(seed: int, sigma: Sequence[float], s: int, device,
+                         stream: Optional[int] = None) -> torch.Tensor:
+    """plsh_sample_params_device: float64 [heads * s, 2] (delta, u) drawn on
+    the GPU, bit for bit those of sample_tables(seed, ...)."""
+    sig = np.ascontiguousarray(sigma, dtype=np.float64)
+    params = torch.empty((sig.size * s, 2), dtype=torch.float64, device=device)
+    if stream is None:
+        stream = torch.cuda.current_stream(params.device).cuda_stream
+    _check(lib().plsh_sample_params_device(seed, sig.size, _ptr(sig), s, params.data_ptr(), stream))
+    return params
+
+
+def device_sampled_tables(seed: int, n: int, sigma: Sequence[float], s: int, device,
+                          stream: Optional[int] = None) -> "DeviceTables":
+    """Tables for the attention entry points with parameters drawn on the GPU
+    (per-step resampling without a host round trip).  The attention kernels
+    read only params; offsets and starts stay empty."""
+    params = sample_params_device(seed, sigma, s, device, stream)
+    empty = torch.empty(0, dtype=torch.int32, device=params.device)
+    return DeviceTables(n, len(sigma), s, params, empty, empty)
 
 
 def build_tables(n: int, heads: int, s: int, params) -> Tables:

@@ -20,8 +20,11 @@ times the estimator (one library call) against the dense exact-ALiBi kernel
 (plsh_exact_alibi_attention) on the Mistral-shaped workload for a range of
 sequence lengths and prints one JSON line per length.
 
-The default run also times the exact-ALiBi kernel once on the same inputs
-(outside the timed steps) and reports it as "exact_alibi_comparator".
+The default run also times, outside the timed steps and on the same inputs,
+the exact-ALiBi kernel ("exact_alibi_comparator"), fixed blocks through the
+estimator ("fixed_blocks_baseline"), the unfused per-sample form
+("unfused_ablation") and the backward for fixed tables ("backward");
+--no-comparators skips them (profiling runs).
 """
 
 from __future__ import annotations
@@ -305,6 +308,32 @@ def main():
         log(f"[bench] unfused: {uf_ms:.3f} ms ({uf_ms / ms:.1f}x the fused call), parity vs oracle {uf_parity:.3e}")
         del uf_out
 
+    # the backward for fixed tables (a statistics pass of the estimator, the
+    # D = dO.O pass, the dQ kernel, the dK/dV kernel): its call time, and dq
+    # on the sampled rows against the oracle's row-local gradient
+    bwd_rec = None
+    if not args.no_comparators:
+        g = torch.Generator().manual_seed(3)
+        do = torch.randn(q.shape, generator=g).to(q.dtype)
+        dod = do.to(dev)
+        res = {}
+
+        def bwd():
+            res["g"] = plsh.attention_backward(qd, kd, vd, dod, w.sigma, w.s, dt, causal=w.causal)
+
+        bw_ms, _ = time_calls(bwd, 3, 3)
+        rq = orc.lsh_grad_rows(qf, kf, vf, W.to_f64(do), tabs, w.causal, rows)
+        gq = W.to_f64(res["g"][0][:, :, rows])
+        bw_err = float(np.abs(gq - rq).max() / np.abs(rq).max())
+        # the five products of a pair (S, dP, dV, dQ, dK; 10 d flops) count as useful
+        bw_tflops = 2.5 * f_distinct / (bw_ms / 1e3) / 1e12
+        bwd_rec = {"ms": bw_ms, "over_forward_call": bw_ms / ms, "useful_tflops": bw_tflops,
+                   "useful_pct_bf16_peak": 100.0 * bw_tflops / PEAK_BF16_TFLOPS,
+                   "dq_sampled_rows_rel_err": bw_err}
+        log(f"[bench] backward: {bw_ms:.3f} ms ({bw_ms / ms:.1f}x the forward call, {bw_tflops:.0f} useful "
+            f"TFLOP/s); dq sampled rows rel. err {bw_err:.2e}")
+        del dod, res
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, tables, args.cpu_budget)
@@ -345,6 +374,7 @@ def main():
         "exact_alibi_comparator": exact_rec,
         "fixed_blocks_baseline": fixed_rec,
         "unfused_ablation": unfused_rec,
+        "backward": bwd_rec,
         "kernel_sha": kernel_sha(),
     }
     print(json.dumps(rec), flush=True)

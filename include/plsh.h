@@ -181,6 +181,27 @@ plsh_status plsh_alibi_attention(const void *q, const void *k, const void *v, vo
                                  plsh_stream_t stream);
 
 /*
+ * plsh_sample_params_device -- the hash parameters of plsh_sample_tables,
+ * drawn on the GPU (Methodology §1 random binning, §2 Gamma(2, sigma)
+ * pitch): params[h*s + k] = (delta, u) of sample k of head h, bit for bit
+ * those plsh_sample_tables writes for the same seed (same counter-based
+ * generator positions and the same IEEE double operations, including the
+ * logarithm of the Erlang-2 draw).  For resampling the tables at every
+ * training step on the device: the attention entry points read only params
+ * (offsets and starts of a plsh_tables may be null there).
+ *   seed    generator seed (one per step for per-step resampling)
+ *   heads   1 .. 128; sigma HOST double [heads], finite and > 0
+ *   s       1 .. 255 samples per head
+ *   params  DEVICE double [heads*s][2] output, 16-byte aligned
+ *   stream  HIP stream for the launch (one kernel, one thread per row)
+ * Errors: PLSH_ERR_ARG (null pointer, heads or s < 1, bad sigma, alignment),
+ * PLSH_ERR_UNSUPPORTED (heads > 128, s > 255), PLSH_ERR_HIP (no device,
+ * launch error).
+ */
+plsh_status plsh_sample_params_device(uint64_t seed, int32_t heads, const double *sigma, int32_t s,
+                                      double *params, plsh_stream_t stream);
+
+/*
  * plsh_debug_block_intervals -- writes, for every (head h, sample k, position
  * i), the block [lo, hi) containing i as recomputed on the GPU by the same
  * per-tile interval code the attention kernel runs (Methodology §1 blocks):
@@ -203,15 +224,16 @@ plsh_status plsh_debug_block_intervals(const plsh_tables *boundaries, int32_t *l
  *   dq          DEVICE [batch, heads, n, d] output
  *   dk, dv      DEVICE [batch, kv_heads, n, d] outputs
  *   the other arguments as for plsh_alibi_attention; bf16, s <= 124.
- * Launches: a pass of the estimator keeping O in fp32 and each row's
- * normaliser; a per-row pass for D_i = dO_i.O_i; the dQ kernel (rows as in
- * the estimator); the dK/dV kernel (key positions in place of rows, using
- * c_ij = c_ji; one workgroup per 128 key positions of a KV head, looping over
- * that head's query heads).  Each kernel is preceded by its block-edge
- * pre-pass.  dq, dk, dv are written whole (no accumulation into them).
- * Device memory: 4 * (batch*heads*n*(d + 1) + 2*batch*heads*ceil32(n)) bytes
- * of statistics from the stream-ordered allocator on `stream`, released
- * within the call, plus the pre-pass workspaces.  dout, dk, dv 16-byte
+ * Launches: the block-edge pre-pass; a pass of the estimator that writes,
+ * in place of O, each row's normaliser and D_i = dO_i.O_i (O in fp32); the
+ * dQ kernel (rows as in the estimator, same records); for causal calls a
+ * non-causal pre-pass; the dK/dV kernel (key positions in place of rows,
+ * using c_ij = c_ji; one workgroup per 128 key positions of a KV head,
+ * looping over that head's query heads).  dq, dk, dv are written whole (no
+ * accumulation into them).
+ * Device memory: 8 * batch*heads*ceil32(n) bytes of statistics from the
+ * stream-ordered allocator on `stream`, released within the call, plus the
+ * pre-pass workspaces.  dout, dk, dv 16-byte
  * aligned; dq, dk, dv must not overlap q, k, v, dout or each other.
  * Errors: as plsh_alibi_attention (null dout, dq, dk or dv, misalignment and
  * aliasing: PLSH_ERR_ARG), and PLSH_ERR_UNSUPPORTED for fp32 or s > 124.

@@ -31,6 +31,8 @@ Readings of what the pages leave open (each is listed in the design notes):
 Parity status per function:
   sample_params            pinned (law: quadrature + KS; exact bit-match
                            against the host sampler is a product check)
+  series_ln                pinned (math.log to 1 ulp over every exponent the
+                           draws reach; exact at 1 and powers of two)
   bins / tables_from_params pinned (collision probability, structure)
   exact_alibi              pinned (library attention with additive bias;
                            sigma -> inf limit)
@@ -56,6 +58,7 @@ __all__ = [
     "unit_open",
     "unit_halfopen",
     "sample_params",
+    "series_ln",
     "bins",
     "block_starts",
     "tables_from_params",
@@ -106,13 +109,42 @@ def _draw_index(head: int, sample: int, draw: int) -> int:
     return ((head << 32) | sample) * 4 + draw
 
 
+# Natural log for the draws.  The pages fix the law of the pitch (Gamma(2,
+# sigma)) but no way of computing it; the draws use a logarithm made of IEEE
+# double +, -, *, / alone, so that any implementation taking the same steps
+# (host or device) draws the same bits: x = m 2^e with m in [sqrt(1/2),
+# sqrt(2)) (exact), f = (m - 1) / (m + 1), ln m = 2 atanh f = 2 f (1 + f^2 p)
+# with p = 1/3 + f^2/5 + ... + f^22/25 summed by Horner from the last term,
+# and ln x = (e ln2_hi + ln m) + e ln2_lo.  |f| <= 0.172, so the first
+# omitted term is below 2^-60 of ln m.
+_LN2_HI = float.fromhex("0x1.62e42ff000000p-1")     # ln 2 to 32 significant bits
+_LN2_LO = float.fromhex("-0x1.718432a1b0e26p-35")   # ln 2 - _LN2_HI, rounded
+_SQRT2 = float.fromhex("0x1.6a09e667f3bcdp+0")      # sqrt(2), rounded
+
+
+def series_ln(x: float) -> float:
+    """ln x for finite x > 0 (normal), by the atanh series above."""
+    m, e = math.frexp(x)           # x = m 2^e, m in [1/2, 1)
+    m, e = m * 2.0, e - 1          # m in [1, 2)
+    if m >= _SQRT2:
+        m, e = m * 0.5, e + 1      # m in [sqrt(1/2), sqrt(2))
+    f = (m - 1.0) / (m + 1.0)
+    f2 = f * f
+    p = 1.0 / 25.0
+    for k in range(11, 0, -1):
+        p = 1.0 / (2 * k + 1) + f2 * p
+    lnm = 2.0 * f + (2.0 * f) * (f2 * p)
+    return (e * _LN2_HI + lnm) + e * _LN2_LO
+
+
 def sample_params(seed: int, sigma: Sequence[float], s: int) -> np.ndarray:
     """Random-binning hash parameters (delta, u) for every (head, sample).
 
     Methodology §1 (random binning features on positions) and §2 (Gamma law
     of the bins): pitch delta ~ Gamma(2, sigma) drawn as the sum of two
     exponentials, delta = -sigma (ln U1 + ln U2); offset u = delta * U3 with
-    U3 ~ U[0, 1).  Returns float64 [heads * s, 2], row h * s + k.
+    U3 ~ U[0, 1); ln is series_ln.  Returns float64 [heads * s, 2], row
+    h * s + k.
     """
     heads = len(sigma)
     out = np.empty((heads * s, 2), dtype=np.float64)
@@ -122,7 +154,7 @@ def sample_params(seed: int, sigma: Sequence[float], s: int) -> np.ndarray:
             u1 = unit_open(splitmix64(seed, _draw_index(h, k, 0)))
             u2 = unit_open(splitmix64(seed, _draw_index(h, k, 1)))
             u3 = unit_halfopen(splitmix64(seed, _draw_index(h, k, 2)))
-            delta = -sg * (math.log(u1) + math.log(u2))
+            delta = -sg * (series_ln(u1) + series_ln(u2))
             out[h * s + k, 0] = delta
             out[h * s + k, 1] = delta * u3
     return out

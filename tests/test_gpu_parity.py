@@ -447,6 +447,47 @@ def test_unfused_full_size_sampled_rows(dev):
     check_bf16(o, ref, what="unfused mistral")
 
 
+# ------------------------------------------------------- device sampler ---
+@pytest.mark.parametrize("seed,sigma,s", [
+    (0, W.alibi_sigmas(32), 20),
+    (2 ** 64 - 1, [1e-3, 1e12], 255),
+    (123456789, [0.5 + 3.0 * h for h in range(128)], 7),
+    (7, [1.19], 1),
+])
+def test_device_sampler_bit_exact_with_host(dev, seed, sigma, s):
+    """Methodology §1-§2 draws on the GPU equal the host sampler's and the
+    oracle's bit for bit, including the extremes of sigma and seed."""
+    say("device sampler", seed, len(sigma), s)
+    p = plsh.sample_params_device(seed, sigma, s, dev)
+    torch.cuda.synchronize()
+    got = p.cpu().numpy()
+    host = plsh.sample_tables(seed, 64, sigma, s).params
+    assert np.array_equal(got.view(np.uint64), host.view(np.uint64))
+    assert np.array_equal(got, orc.sample_params(seed, sigma, s))
+
+
+def test_device_sampled_tables_drive_attention_bitwise(dev):
+    """Per-step resampling on the GPU: for two consecutive seeds the
+    estimator with device-drawn parameters equals, bit for bit, the
+    estimator with the host tables of the same seed, and the two steps
+    differ."""
+    w = W.get("qwen3-0.6b-n8192-s20")
+    q, k, v = W.make_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    outs = []
+    for step in range(2):
+        seed = w.hash_seed + step
+        say("device tables step", step, w.name)
+        a = plsh.attention(qd, kd, vd, w.sigma, w.s, plsh.device_sampled_tables(seed, w.n, w.sigma, w.s, dev),
+                           causal=w.causal)
+        b = plsh.attention(qd, kd, vd, w.sigma, w.s, plsh.sample_tables(seed, w.n, w.sigma, w.s).to(dev),
+                           causal=w.causal)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        outs.append(a)
+    assert not torch.equal(outs[0], outs[1])
+
+
 # ------------------------------------------------------------ backward ---
 def grad_inputs(w: W.Workload, seed: int = 3):
     q, k, v = W.make_qkv(w)

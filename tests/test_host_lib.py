@@ -294,6 +294,38 @@ def test_backward_without_device_reports_hip_error():
     assert st == plsh.PLSH_ERR_HIP, msg
 
 
+def _sample_dev_call(seed=1, heads=4, sigma=(2.0, 4.0, 8.0, 16.0), s=3, params=0x10000):
+    sig = np.ascontiguousarray(sigma, dtype=np.float64)
+    L = plsh.lib()
+    st = L.plsh_sample_params_device(seed, heads, sig.ctypes.data if sigma is not None else None, s, params, None)
+    return st, L.plsh_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(sigma=None), plsh.PLSH_ERR_ARG),
+    (dict(params=None), plsh.PLSH_ERR_ARG),
+    (dict(heads=0), plsh.PLSH_ERR_ARG),
+    (dict(s=0), plsh.PLSH_ERR_ARG),
+    (dict(heads=129, sigma=[1.0] * 129), plsh.PLSH_ERR_UNSUPPORTED),
+    (dict(s=256), plsh.PLSH_ERR_UNSUPPORTED),
+    (dict(sigma=(2.0, float("inf"), 8.0, 16.0)), plsh.PLSH_ERR_ARG),
+    (dict(sigma=(2.0, -1.0, 8.0, 16.0)), plsh.PLSH_ERR_ARG),
+    (dict(params=0x10008), plsh.PLSH_ERR_ARG),
+])
+def test_device_sampler_argument_errors(over, status):
+    st, msg = _sample_dev_call(**over)
+    assert st == status, msg
+    assert msg
+
+
+def test_device_sampler_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, msg = _sample_dev_call()
+    assert st == plsh.PLSH_ERR_HIP, msg
+
+
 @pytest.mark.parametrize("width", [1.0, 7.0, 7.5, 64.0, 1e6])
 def test_fixed_block_tables_match_oracle_scan(width):
     """Fixed blocks (pitch w, offset 0) through plsh_build_tables equal the

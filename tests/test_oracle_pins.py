@@ -433,6 +433,31 @@ def test_sampler_stream_is_splitmix64():
     assert [orc.splitmix64(1234567, i) for i in range(3)] == want
 
 
+def test_series_ln_matches_library_log():
+    """The draws' logarithm against the C library's (math.log) over every
+    binary exponent the uniforms reach (2^-54 .. 1) and a little beyond,
+    with mantissas spread over [1, 2) plus the reduction boundary sqrt(2):
+    within 2 ulp, within 1 ulp once |e| >= 2 (the e ln 2 part dominates),
+    exactly 0 at 1 and within 1 ulp of k ln 2 at 2^k."""
+    rng = np.random.default_rng(12)
+    r2 = math.sqrt(2.0)
+    edge = [1.0, r2, float(np.nextafter(r2, 0.0)), float(np.nextafter(r2, 3.0)), float(np.nextafter(2.0, 0.0))]
+    for e in range(-60, 3):
+        worst = 0.0
+        for m in list(rng.uniform(1.0, 2.0, 300)) + edge:
+            x = math.ldexp(float(m), e)
+            want = math.log(x)
+            got = orc.series_ln(x)
+            if want == 0.0:
+                assert got == 0.0
+                continue
+            worst = max(worst, abs(got - want) / math.ulp(want))
+        assert worst <= (1.0 if abs(e) >= 2 else 2.0), (e, worst)
+    assert orc.series_ln(1.0) == 0.0
+    for k in range(-54, 4):
+        assert abs(orc.series_ln(math.ldexp(1.0, k)) - k * math.log(2.0)) <= math.ulp(k * math.log(2.0) or 1.0)
+
+
 # ------------------------------------------------------------- O6 (grad) ---
 @pytest.mark.parametrize("causal", [False, True])
 def test_o6_gradient_matches_finite_differences(causal):
