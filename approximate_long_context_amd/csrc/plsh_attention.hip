@@ -623,13 +623,16 @@ __host__ __device__ constexpr size_t ev_wave_bytes(int s, bool causal) {
   return (size_t)(causal ? 8 : 16) * ev_count(s);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WALK = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves), amdgpu_waves_per_eu(4, 4)))
 void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   using L = MfmaLds<D>;
   __shared__ __attribute__((aligned(16))) L lds;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
-  const int s = a.s, n = a.n;
+  // WALK: the samples one by one (a.s of them), each through its own
+  // single-sample records (0/1 masks); otherwise all samples fused, s = a.s
+  const int s = WALK ? 1 : a.s, n = a.n;
+  const int nwalk = WALK ? a.s : 1;
   // the wave index is wave-uniform; saying so keeps all per-wave control flow
   // on the scalar unit
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -667,339 +670,354 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   const int t32 = 16 * half + qc;              // the lane's row within its group
   const int g32 = (n + 31) / 32;
   const size_t rb = rec_bytes(s);
-  const uint8_t *rec_wg = ws + ((size_t)h * g32 + 4 * g) * rb;
-  const uint8_t *rec = rec_wg + (size_t)grp * rb;
 
   const uint16_t *Q = (const uint16_t *)a.q + ((int64_t)b * a.heads + h) * n * D;
   const uint16_t *K = (const uint16_t *)a.k + ((int64_t)b * a.kv_heads + kvh) * n * D;
   const uint16_t *V = (const uint16_t *)a.v + ((int64_t)b * a.kv_heads + kvh) * n * D;
   uint16_t *O = (uint16_t *)a.out + ((int64_t)b * a.heads + h) * n * D;
 
-  // ---- the four groups' key ranges first (the K/V copies need them), then
-  // the row's diagonal-tile multiplicities
-  int U0 = INT32_MAX, U1 = INT32_MIN, U0w = INT32_MAX, U1w = INT32_MIN;
-  {
-    // all four headers in one round trip: groups past the end re-read the
-    // last valid one (their ranges then add nothing)
-    const int wlast = min(3, (n - 1 - g * 128) / 32);
-    int4 hdr[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) hdr[w] = *(const int4 *)(rec_wg + (size_t)min(w, wlast) * rb);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      U0 = min(U0, hdr[w].y);
-      U1 = max(U1, hdr[w].z);
-      if (w == grp) { U0w = hdr[w].y; U1w = hdr[w].z; }
-    }
-  }
   constexpr int NC = D / 32;
   // the Q fragment (B operand of S^T = K Q^T: query r0 + qc, dims 32 c +
   // 8 gq + e), read from LDS after the first wait (see below)
   bf16x8 qf[NC];
-  // bytes c(t32, 16 b + 4 gq + r), and (non-causal) c(t32, 31)
-  uint32_t dg[2] = {0u, 0u};
-  int dlast = 0;
-  if (active) {
-    const uint8_t *drow = rec + rec_diag_off(s) + 32 * t32;
-    dg[0] = *(const uint32_t *)(drow + 4 * gq);
-    dg[1] = *(const uint32_t *)(drow + 16 + 4 * gq);
-    if (!CAUSAL) dlast = (int)(*(const uint32_t *)(drow + 28) >> 24);
-  }
-  // stage st covers keys [U0 + 32 st, U0 + 32 st + 32)
-  const int nst = (U1 > U0) ? (U1 - U0) / kTileKeys : 0;
-  // Everything loaded so far is needed before the first tile.  Waiting here,
-  // before the first K/V copies are issued, measured faster than letting the
-  // first stage waits cover these loads.
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
-
-  // the group's sorted edge lists, copied by its first wave into the group's
-  // LDS slice (16 bytes = two edges per lane and instruction); they are
-  // complete for both waves after the first stage's barrier
-  const int nch = ev_count(s) / 2;
-  u32x2 *evl = (u32x2 *)(dyn + (size_t)grp * ev_wave_bytes(s, CAUSAL));
-  u32x2 *evt = evl + ev_count(s);
-  if (active && half == 0) {
-    for (int c0 = 0; c0 < nch; c0 += 64)
-      if (c0 + lane < nch) dma16(rec + rec_evl_off() + 16 * (c0 + lane), lds_addr(evl + 2 * c0));
-    if (!CAUSAL)
-      for (int c0 = 0; c0 < nch; c0 += 64)
-        if (c0 + lane < nch) dma16(rec + rec_evt_off(s) + 16 * (c0 + lane), lds_addr(evt + 2 * c0));
-  }
-
-  // ---- the wave's 16 query rows go to ring slots 2 and 3 (free until the
-  // first pair has read them) in the swizzled layout of a K tile, so that
-  // every copy instruction reads whole rows and the fragment reads are free of
-  // bank conflicts (whole rows per instruction keep the address unit's work
-  // per byte low; a row per lane would touch 16 rows per instruction)
-  constexpr int CPR_Q = D / 8;  // 16-byte chunks per row
-  const uint32_t q_lds = lds_addr(&lds.kv[2][0][0]) + wave * 32 * D;
-  if (active) {
-#pragma unroll
-    for (int c0 = 0; c0 < 16 * CPR_Q; c0 += 64) {
-      const int row = (c0 + lane) / CPR_Q, ch = (c0 + lane) % CPR_Q;
-      const int64_t off = (int64_t)min(r0 + row, n - 1) * (2 * D) + 16 * (ch ^ swz_key<D>(row));
-      dma16((const char *)Q + off, q_lds + 16 * c0);
-    }
-  }
-
-  // ---- K/V staging: a tile is 32 rows of D / 8 chunks, 4 D chunks per
-  // matrix; wave w copies chunks [w CPW, (w + 1) CPW) with its first CPW
-  // lanes.  Keys past the end read row n - 1, whose products get c = 0.
-  constexpr int CPR = D / 8;            // chunks per row
-  constexpr int CPW = 4 * D / kWaves;   // chunks per wave, stage and matrix (<= 64)
-  constexpr int LPS = 2;                // loads per thread per stage (K and V)
-  const char *Kb = (const char *)K, *Vb = (const char *)V;
-  // the lane's chunk of every stage: row dkey of the tile, 16 bytes at dofs
-  const int dslot = wave * CPW + lane;
-  const int dkey = dslot / CPR;
-  const int dofs = 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
-  const uint32_t kv_lds = lds_addr(&lds.kv[0][0][0]) + wave * CPW * 16;
-  auto issue_stage = [&](int st, int q) {  // q = st % kRing
-    if (lane < CPW) {
-      const int64_t off = (int64_t)min(U0 + kTileKeys * st + dkey, n - 1) * (2 * D) + dofs;
-      dma16(Kb + off, kv_lds + (uint32_t)(2 * q) * (kTileKeys * D * 2));
-      dma16(Vb + off, kv_lds + (uint32_t)(2 * q + 1) * (kTileKeys * D * 2));
-    }
-  };
-  // stages 0 and 1 now; the pair starting at stage st issues st + 2, st + 3
-  if (nst > 0) issue_stage(0, 0);
-  if (nst > 1) issue_stage(1, 1);
-
-  // ---- running state
-  constexpr int NDB = D / 16;  // 16-dim blocks of O^T
+  constexpr int CPR_Q = D / 8;  // 16-byte chunks per query row
+  constexpr int NDB = D / 16;   // 16-dim blocks of O^T
   floatx4 oacc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m2 = -INFINITY;  // running max, log2 units
-  float lsum = 0.f;      // this lane's share of the row sum
-  int base = 0;          // the row's multiplicity just before the current tile
-  int lp = 0, tp = 0;    // next unconsumed lead / trail edge
-  int pl = 0, pt = 0;    // their positions (wave-uniform)
-  int lg_base = -1;      // the count whose log2 is lg
-  float lg = 0.f;
-  // edge positions read at a wave-uniform index are wave-uniform
-  auto pos_at = [&](const u32x2 *ev, int i) { return (int32_t)__builtin_amdgcn_readfirstlane(ev[i][0]); };
-  // K operand: key 16 b + qc, chunk 4 c + gq; b = 1 lies 16 rows further
-  uint32_t kofs[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) kofs[c] = swz<D>(qc, 4 * c + gq);
-  // V operand (v_ds_read_b64_tr_b16): in each 16-lane group gq, lane r names
-  // the row (key 4 gq + r / 4, dims 16 db + 4 (r % 4) .. + 3), and lane i
-  // receives V[4 gq + e][16 db + i], e = 0..3; keys + 16 lie 16 rows further
-  uint32_t vofs[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int dim = 16 * db + 4 * (qc & 3);
-    vofs[db] = swz<D>(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1);
-  }
-
-  // this wave's tiles are the stages [sa, sb)
-  const int sa = active ? (U0w - U0) / kTileKeys : 0;
-  const int sb = active ? (U1w - U0) / kTileKeys : 0;
-
-  // a5: S^T = K Q^T for the tile of stage st, keys 16 b + 4 gq + r
-  floatx4 sacc[2];
-  // (the ring slot is a compile-time constant, so that LDS operand offsets
-  // become immediates of the reads)
-  auto qk_tile = [&](auto slotc) {
-    const char *kt = (const char *)lds.kv[decltype(slotc)::value][0];
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      u32x4 kr[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kr[c] = *(const u32x4 *)(kt + kofs[c] + 32 * D * bb);
-      sacc[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc[bb], 0, 0, 0);
-    }
-  };
-
-  // Visits, in order, the edges of a sorted list at positions < jend starting
-  // at index ptr (position pp), and advances ptr / pp past them.  Lane l reads
-  // edge ptr + l, so up to 64 edges are found with one LDS read and a ballot
-  // (the list ends in 16 sentinels at INT32_MAX; reads stay inside it).
-  const int ev_last = s + kSentinels - 1;
-  auto edges_in_tile = [&](const u32x2 *ev, int &ptr, int &pp, int jend, auto &&visit) {
-    while (pp < jend) {
-      const u32x2 e = ev[min(ptr + lane, ev_last)];
-      const int k = __popcll(__ballot((int32_t)e[0] < jend));  // a prefix of the lanes
-      for (int i = 0; i < k; ++i)
-        visit((int32_t)__builtin_amdgcn_readlane(e[0], i), __builtin_amdgcn_readlane(e[1], i));
-      ptr += k;
-      pp = k < 64 ? (int32_t)__builtin_amdgcn_readlane(e[0], k) : pos_at(ev, ptr);
-    }
-  };
-
-  // a4, a6, a7 for the tile of stage st, whose logits are in sacc
-  auto finish_tile = [&](int st, auto slotc) {
-    const char *vt = (const char *)lds.kv[decltype(slotc)::value][1];
-    const int j0 = U0 + kTileKeys * st;
-
-    // a4: multiplicity c for keys j0 + 16 b + 4 gq + r.
-    //  * diagonal tile: the row's bytes of the precomputed table;
-    //  * a tile holding sample edges (lower block ends = leads on the left of
-    //    the diagonal, upper ends = trails on the right; positions are
-    //    wave-uniform): c = base +- sum over edges of w_e(row) [key >= pos_e],
-    //    four keys per byte-counter word;
-    //  * otherwise c = base for all keys of the tile.
-    const int jend = j0 + kTileKeys;
-    float cf[8];
-    int kind;  // 0: one count for the tile, 1: per-key counts
-    if (j0 == rg) {
-      // (kept here: hoisted out of the loop, the conversion would wait for
-      // the table load, and with it for every K/V copy issued after it)
-      uint32_t d0 = dg[0], d1 = dg[1];
-      asm volatile("" : "+v"(d0), "+v"(d1));
-#pragma unroll
-      for (int r = 0; r < 8; ++r) cf[r] = (float)((((r >> 2) ? d1 : d0) >> (8 * (r & 3))) & 0xFFu);
-      // the table already counts every edge at or before the tile's end
-      edges_in_tile(evl, lp, pl, jend, [](int, uint32_t) {});
-      if (!CAUSAL) {
-        edges_in_tile(evt, tp, pt, jend, [](int, uint32_t) {});
-        base = dlast;
-      }
-      kind = 1;
-    } else if (pl < jend || (!CAUSAL && pt < jend)) {
-      // the lane's keys are words gq and gq + 4 of the tile's step rows
-      const uint32_t *srow = &lds.step[0][gq];
-      uint32_t cw[2] = {(uint32_t)base * 0x01010101u, (uint32_t)base * 0x01010101u};
-      // leads: the sample's block of the row starts at pos
-      edges_in_tile(evl, lp, pl, jend, [&](int pos, uint32_t W) {
-        const uint32_t w = (W >> t32) & 1u;
-        const uint32_t *sr = srow + 8 * (pos - j0);
-        cw[0] += w * sr[0];
-        cw[1] += w * sr[4];
-        base += (int)w;
-      });
-      // trails: the sample's block of the row ends before pos
-      if (!CAUSAL)
-        edges_in_tile(evt, tp, pt, jend, [&](int pos, uint32_t W) {
-          const uint32_t w = (W >> t32) & 1u;
-          const uint32_t *sr = srow + 8 * (pos - j0);
-          cw[0] -= w * sr[0];
-          cw[1] -= w * sr[4];
-          base -= (int)w;
-        });
-#pragma unroll
-      for (int r = 0; r < 8; ++r) cf[r] = (float)((cw[r >> 2] >> (8 * (r & 3))) & 0xFFu);
-      kind = 1;
-    } else {
-      cf[0] = (float)base;
-      kind = 0;
-    }
-
-    // a6: weighted online softmax in the log2 domain.  The running max is
-    // raised only when a logit exceeds it by more than 2^8 (the result does
-    // not depend on the max used, and a rescale of the accumulators is then
-    // rare).  A tile with one count per row folds log2(c) into the exponent
-    // bias; otherwise P = c * 2^(...).  P is rounded to bf16 in pairs and the
-    // row sum adds exactly the rounded weights that enter PV.
-    // (raw v_max3_f32: one instruction per three finite logits)
-    auto mx2 = [](float x, float y) { return max3f(x, y, y); };
-    float mx = max3f(max3f(sacc[0][0], sacc[0][1], sacc[0][2]), max3f(sacc[0][3], sacc[1][0], sacc[1][1]),
-                     max3f(sacc[1][2], sacc[1][3], sacc[1][3]));
-    // the lane's own maximum decides whether any rescale is due; only then
-    // is it combined over the four lanes of each query
-    if (__any(mx * kLog2e > m2 + 8.0f)) {
-      mx = mx2(mx, xor16_f(mx));
-      mx = mx2(mx, other_half_f(mx, lane)) * kLog2e;
-      const bool need = mx > m2 + 8.0f;
-      const float mnew = need ? mx : m2;
-      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      m2 = mnew;
-    }
-    u32x4 pw;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    if (__builtin_amdgcn_readfirstlane(kind) == 0) {
-      if (__any(base != lg_base)) {  // log2 of the running count, recomputed when it changes
-        lg = __builtin_amdgcn_logf(cf[0]);
-        lg_base = base;
-      }
-      const float bias = m2 - lg;  // c = 0 gives bias = +inf, P = 0
-#pragma unroll
-      for (int r = 0; r < 8; r += 2) {
-        const floatx2 pf = {__builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][r & 3], kLog2e, -bias)),
-                            __builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][(r & 3) + 1], kLog2e, -bias))};
-        const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
-        pw[r >> 1] = __builtin_bit_cast(uint32_t, pb);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 8; r += 2) {
-        const floatx2 pf = {cf[r] * __builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][r & 3], kLog2e, -m2)),
-                            cf[r + 1] * __builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][(r & 3) + 1], kLog2e, -m2))};
-        const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
-        pw[r >> 1] = __builtin_bit_cast(uint32_t, pb);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
-      }
-    }
-    const bf16x8 pk = __builtin_bit_cast(bf16x8, pw);
-
-    // a7: O^T += V^T P^T, the V operand read in two batches of 16-dim blocks
-    constexpr int NB = NDB < 4 ? NDB : 4;
-#pragma unroll
-    for (int d0 = 0; d0 < NDB; d0 += NB) {
-      u32x4 vop[NB];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const char *va = vt + vofs[d0 + j];
-        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)va);
-        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(va + 16 * 2 * D));
-        vop[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
-                       __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
-                       __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
-                       __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        oacc[d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[j]), pk, oacc[d0 + j], 0, 0, 0);
-    }
-  };
-
-  // Two stages per barrier (measured: the barrier, where every wave waits for
-  // the slowest, costs more than the shorter look-ahead): the pair starting at
-  // stage st waits for stages st, st + 1, then refills the ring slots of
-  // stages st - 2, st - 1 (consumed by every wave before the barrier) with
-  // stages st + 2, st + 3, and computes its two tiles.
-  auto pair = [&](int st, auto s0, auto s1) {
-    PLSH_WAIT_VM_LGKM0(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (st == 0) {
-      // the Q fragment from the wave's staged rows, then a barrier: every wave
-      // has its fragment before slots 2, 3 take stages 2, 3
-      const char *qt = (const char *)lds.kv[2][0] + wave * 32 * D;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qt + swz<D>(qc, 4 * c + gq)));
+  float m2;    // running max, log2 units
+  float lsum;  // this lane's share of the row sum
+  int nst = 0;
+  for (int kk = 0; kk < nwalk; ++kk) {
+    if (kk > 0) {
+      // every wave is past the previous sample's tiles before its edge
+      // lists and ring slots are refilled
       PLSH_WAIT_VM_LGKM0(0);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
-    if (st + 2 < nst) issue_stage(st + 2, (decltype(s0)::value + 2) % kRing);
-    if (st + 3 < nst) issue_stage(st + 3, (decltype(s1)::value + 2) % kRing);
-    if (st == 0 && active) {  // the edge lists landed with stage 0
-      pl = pos_at(evl, 0);
-      if (!CAUSAL) pt = pos_at(evt, 0);
+    const uint8_t *rec_wg = ws + ((size_t)(WALK ? h * nwalk + kk : h) * g32 + 4 * g) * rb;
+    const uint8_t *rec = rec_wg + (size_t)grp * rb;
+    // ---- the four groups' key ranges first (the K/V copies need them), then
+    // the row's diagonal-tile multiplicities
+    int U0 = INT32_MAX, U1 = INT32_MIN, U0w = INT32_MAX, U1w = INT32_MIN;
+    {
+      // all four headers in one round trip: groups past the end re-read the
+      // last valid one (their ranges then add nothing)
+      const int wlast = min(3, (n - 1 - g * 128) / 32);
+      int4 hdr[4];
+  #pragma unroll
+      for (int w = 0; w < 4; ++w) hdr[w] = *(const int4 *)(rec_wg + (size_t)min(w, wlast) * rb);
+  #pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        U0 = min(U0, hdr[w].y);
+        U1 = max(U1, hdr[w].z);
+        if (w == grp) { U0w = hdr[w].y; U1w = hdr[w].z; }
+      }
     }
-    if (st >= sa && st < sb) {
-      qk_tile(s0);
-      finish_tile(st, s0);
+    // bytes c(t32, 16 b + 4 gq + r), and (non-causal) c(t32, 31)
+    uint32_t dg[2] = {0u, 0u};
+    int dlast = 0;
+    if (active) {
+      const uint8_t *drow = rec + rec_diag_off(s) + 32 * t32;
+      dg[0] = *(const uint32_t *)(drow + 4 * gq);
+      dg[1] = *(const uint32_t *)(drow + 16 + 4 * gq);
+      if (!CAUSAL) dlast = (int)(*(const uint32_t *)(drow + 28) >> 24);
     }
-    if (st + 1 < nst && st + 1 >= sa && st + 1 < sb) {
-      qk_tile(s1);
-      finish_tile(st + 1, s1);
+    // stage st covers keys [U0 + 32 st, U0 + 32 st + 32)
+    nst = (U1 > U0) ? (U1 - U0) / kTileKeys : 0;
+    // Everything loaded so far is needed before the first tile.  Waiting here,
+    // before the first K/V copies are issued, measured faster than letting the
+    // first stage waits cover these loads.
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+
+    // the group's sorted edge lists, copied by its first wave into the group's
+    // LDS slice (16 bytes = two edges per lane and instruction); they are
+    // complete for both waves after the first stage's barrier
+    const int nch = ev_count(s) / 2;
+    u32x2 *evl = (u32x2 *)(dyn + (size_t)grp * ev_wave_bytes(s, CAUSAL));
+    u32x2 *evt = evl + ev_count(s);
+    if (active && half == 0) {
+      for (int c0 = 0; c0 < nch; c0 += 64)
+        if (c0 + lane < nch) dma16(rec + rec_evl_off() + 16 * (c0 + lane), lds_addr(evl + 2 * c0));
+      if (!CAUSAL)
+        for (int c0 = 0; c0 < nch; c0 += 64)
+          if (c0 + lane < nch) dma16(rec + rec_evt_off(s) + 16 * (c0 + lane), lds_addr(evt + 2 * c0));
     }
-  };
-  for (int st0 = 0; st0 < nst; st0 += kRing) {
-    pair(st0, SlotC<0>{}, SlotC<1>{});
-    if (st0 + 2 < nst) pair(st0 + 2, SlotC<2>{}, SlotC<3>{});
+
+    // ---- the wave's 16 query rows go to ring slots 2 and 3 (free until the
+    // first pair has read them) in the swizzled layout of a K tile, so that
+    // every copy instruction reads whole rows and the fragment reads are free of
+    // bank conflicts (whole rows per instruction keep the address unit's work
+    // per byte low; a row per lane would touch 16 rows per instruction)
+    const uint32_t q_lds = lds_addr(&lds.kv[2][0][0]) + wave * 32 * D;
+    if (active && kk == 0) {  // (staged once)
+  #pragma unroll
+      for (int c0 = 0; c0 < 16 * CPR_Q; c0 += 64) {
+        const int row = (c0 + lane) / CPR_Q, ch = (c0 + lane) % CPR_Q;
+        const int64_t off = (int64_t)min(r0 + row, n - 1) * (2 * D) + 16 * (ch ^ swz_key<D>(row));
+        dma16((const char *)Q + off, q_lds + 16 * c0);
+      }
+    }
+
+    // ---- K/V staging: a tile is 32 rows of D / 8 chunks, 4 D chunks per
+    // matrix; wave w copies chunks [w CPW, (w + 1) CPW) with its first CPW
+    // lanes.  Keys past the end read row n - 1, whose products get c = 0.
+    constexpr int CPR = D / 8;            // chunks per row
+    constexpr int CPW = 4 * D / kWaves;   // chunks per wave, stage and matrix (<= 64)
+    constexpr int LPS = 2;                // loads per thread per stage (K and V)
+    const char *Kb = (const char *)K, *Vb = (const char *)V;
+    // the lane's chunk of every stage: row dkey of the tile, 16 bytes at dofs
+    const int dslot = wave * CPW + lane;
+    const int dkey = dslot / CPR;
+    const int dofs = 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
+    const uint32_t kv_lds = lds_addr(&lds.kv[0][0][0]) + wave * CPW * 16;
+    auto issue_stage = [&](int st, int q) {  // q = st % kRing
+      if (lane < CPW) {
+        const int64_t off = (int64_t)min(U0 + kTileKeys * st + dkey, n - 1) * (2 * D) + dofs;
+        dma16(Kb + off, kv_lds + (uint32_t)(2 * q) * (kTileKeys * D * 2));
+        dma16(Vb + off, kv_lds + (uint32_t)(2 * q + 1) * (kTileKeys * D * 2));
+      }
+    };
+    // stages 0 and 1 now; the pair starting at stage st issues st + 2, st + 3
+    if (nst > 0) issue_stage(0, 0);
+    if (nst > 1) issue_stage(1, 1);
+
+    // ---- running state
+    if (kk == 0) {  // (over every sample when walking them)
+  #pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+      m2 = -INFINITY;
+      lsum = 0.f;
+    }
+    int base = 0;          // the row's multiplicity just before the current tile
+    int lp = 0, tp = 0;    // next unconsumed lead / trail edge
+    int pl = 0, pt = 0;    // their positions (wave-uniform)
+    int lg_base = -1;      // the count whose log2 is lg
+    float lg = 0.f;
+    // edge positions read at a wave-uniform index are wave-uniform
+    auto pos_at = [&](const u32x2 *ev, int i) { return (int32_t)__builtin_amdgcn_readfirstlane(ev[i][0]); };
+    // K operand: key 16 b + qc, chunk 4 c + gq; b = 1 lies 16 rows further
+    uint32_t kofs[NC];
+  #pragma unroll
+    for (int c = 0; c < NC; ++c) kofs[c] = swz<D>(qc, 4 * c + gq);
+    // V operand (v_ds_read_b64_tr_b16): in each 16-lane group gq, lane r names
+    // the row (key 4 gq + r / 4, dims 16 db + 4 (r % 4) .. + 3), and lane i
+    // receives V[4 gq + e][16 db + i], e = 0..3; keys + 16 lie 16 rows further
+    uint32_t vofs[NDB];
+  #pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int dim = 16 * db + 4 * (qc & 3);
+      vofs[db] = swz<D>(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1);
+    }
+
+    // this wave's tiles are the stages [sa, sb)
+    const int sa = active ? (U0w - U0) / kTileKeys : 0;
+    const int sb = active ? (U1w - U0) / kTileKeys : 0;
+
+    // a5: S^T = K Q^T for the tile of stage st, keys 16 b + 4 gq + r
+    floatx4 sacc[2];
+    // (the ring slot is a compile-time constant, so that LDS operand offsets
+    // become immediates of the reads)
+    auto qk_tile = [&](auto slotc) {
+      const char *kt = (const char *)lds.kv[decltype(slotc)::value][0];
+  #pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        u32x4 kr[NC];
+  #pragma unroll
+        for (int c = 0; c < NC; ++c) kr[c] = *(const u32x4 *)(kt + kofs[c] + 32 * D * bb);
+        sacc[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int c = 0; c < NC; ++c)
+          sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[c]), qf[c], sacc[bb], 0, 0, 0);
+      }
+    };
+
+    // Visits, in order, the edges of a sorted list at positions < jend starting
+    // at index ptr (position pp), and advances ptr / pp past them.  Lane l reads
+    // edge ptr + l, so up to 64 edges are found with one LDS read and a ballot
+    // (the list ends in 16 sentinels at INT32_MAX; reads stay inside it).
+    const int ev_last = s + kSentinels - 1;
+    auto edges_in_tile = [&](const u32x2 *ev, int &ptr, int &pp, int jend, auto &&visit) {
+      while (pp < jend) {
+        const u32x2 e = ev[min(ptr + lane, ev_last)];
+        const int k = __popcll(__ballot((int32_t)e[0] < jend));  // a prefix of the lanes
+        for (int i = 0; i < k; ++i)
+          visit((int32_t)__builtin_amdgcn_readlane(e[0], i), __builtin_amdgcn_readlane(e[1], i));
+        ptr += k;
+        pp = k < 64 ? (int32_t)__builtin_amdgcn_readlane(e[0], k) : pos_at(ev, ptr);
+      }
+    };
+
+    // a4, a6, a7 for the tile of stage st, whose logits are in sacc
+    auto finish_tile = [&](int st, auto slotc) {
+      const char *vt = (const char *)lds.kv[decltype(slotc)::value][1];
+      const int j0 = U0 + kTileKeys * st;
+
+      // a4: multiplicity c for keys j0 + 16 b + 4 gq + r.
+      //  * diagonal tile: the row's bytes of the precomputed table;
+      //  * a tile holding sample edges (lower block ends = leads on the left of
+      //    the diagonal, upper ends = trails on the right; positions are
+      //    wave-uniform): c = base +- sum over edges of w_e(row) [key >= pos_e],
+      //    four keys per byte-counter word;
+      //  * otherwise c = base for all keys of the tile.
+      const int jend = j0 + kTileKeys;
+      float cf[8];
+      int kind;  // 0: one count for the tile, 1: per-key counts
+      if (j0 == rg) {
+        // (kept here: hoisted out of the loop, the conversion would wait for
+        // the table load, and with it for every K/V copy issued after it)
+        uint32_t d0 = dg[0], d1 = dg[1];
+        asm volatile("" : "+v"(d0), "+v"(d1));
+  #pragma unroll
+        for (int r = 0; r < 8; ++r) cf[r] = (float)((((r >> 2) ? d1 : d0) >> (8 * (r & 3))) & 0xFFu);
+        // the table already counts every edge at or before the tile's end
+        edges_in_tile(evl, lp, pl, jend, [](int, uint32_t) {});
+        if (!CAUSAL) {
+          edges_in_tile(evt, tp, pt, jend, [](int, uint32_t) {});
+          base = dlast;
+        }
+        kind = 1;
+      } else if (pl < jend || (!CAUSAL && pt < jend)) {
+        // the lane's keys are words gq and gq + 4 of the tile's step rows
+        const uint32_t *srow = &lds.step[0][gq];
+        uint32_t cw[2] = {(uint32_t)base * 0x01010101u, (uint32_t)base * 0x01010101u};
+        // leads: the sample's block of the row starts at pos
+        edges_in_tile(evl, lp, pl, jend, [&](int pos, uint32_t W) {
+          const uint32_t w = (W >> t32) & 1u;
+          const uint32_t *sr = srow + 8 * (pos - j0);
+          cw[0] += w * sr[0];
+          cw[1] += w * sr[4];
+          base += (int)w;
+        });
+        // trails: the sample's block of the row ends before pos
+        if (!CAUSAL)
+          edges_in_tile(evt, tp, pt, jend, [&](int pos, uint32_t W) {
+            const uint32_t w = (W >> t32) & 1u;
+            const uint32_t *sr = srow + 8 * (pos - j0);
+            cw[0] -= w * sr[0];
+            cw[1] -= w * sr[4];
+            base -= (int)w;
+          });
+  #pragma unroll
+        for (int r = 0; r < 8; ++r) cf[r] = (float)((cw[r >> 2] >> (8 * (r & 3))) & 0xFFu);
+        kind = 1;
+      } else {
+        cf[0] = (float)base;
+        kind = 0;
+      }
+
+      // a6: weighted online softmax in the log2 domain.  The running max is
+      // raised only when a logit exceeds it by more than 2^8 (the result does
+      // not depend on the max used, and a rescale of the accumulators is then
+      // rare).  A tile with one count per row folds log2(c) into the exponent
+      // bias; otherwise P = c * 2^(...).  P is rounded to bf16 in pairs and the
+      // row sum adds exactly the rounded weights that enter PV.
+      // (raw v_max3_f32: one instruction per three finite logits)
+      auto mx2 = [](float x, float y) { return max3f(x, y, y); };
+      float mx = max3f(max3f(sacc[0][0], sacc[0][1], sacc[0][2]), max3f(sacc[0][3], sacc[1][0], sacc[1][1]),
+                       max3f(sacc[1][2], sacc[1][3], sacc[1][3]));
+      // the lane's own maximum decides whether any rescale is due; only then
+      // is it combined over the four lanes of each query
+      if (__any(mx * kLog2e > m2 + 8.0f)) {
+        mx = mx2(mx, xor16_f(mx));
+        mx = mx2(mx, other_half_f(mx, lane)) * kLog2e;
+        const bool need = mx > m2 + 8.0f;
+        const float mnew = need ? mx : m2;
+        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+        lsum *= alpha;
+  #pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        m2 = mnew;
+      }
+      u32x4 pw;
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      if (__builtin_amdgcn_readfirstlane(kind) == 0) {
+        if (__any(base != lg_base)) {  // log2 of the running count, recomputed when it changes
+          lg = __builtin_amdgcn_logf(cf[0]);
+          lg_base = base;
+        }
+        const float bias = m2 - lg;  // c = 0 gives bias = +inf, P = 0
+  #pragma unroll
+        for (int r = 0; r < 8; r += 2) {
+          const floatx2 pf = {__builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][r & 3], kLog2e, -bias)),
+                              __builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][(r & 3) + 1], kLog2e, -bias))};
+          const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+          pw[r >> 1] = __builtin_bit_cast(uint32_t, pb);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
+        }
+      } else {
+  #pragma unroll
+        for (int r = 0; r < 8; r += 2) {
+          const floatx2 pf = {cf[r] * __builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][r & 3], kLog2e, -m2)),
+                              cf[r + 1] * __builtin_amdgcn_exp2f(fmaf(sacc[r >> 2][(r & 3) + 1], kLog2e, -m2))};
+          const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+          pw[r >> 1] = __builtin_bit_cast(uint32_t, pb);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
+        }
+      }
+      const bf16x8 pk = __builtin_bit_cast(bf16x8, pw);
+
+      // a7: O^T += V^T P^T, the V operand read in two batches of 16-dim blocks
+      constexpr int NB = NDB < 4 ? NDB : 4;
+  #pragma unroll
+      for (int d0 = 0; d0 < NDB; d0 += NB) {
+        u32x4 vop[NB];
+  #pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const char *va = vt + vofs[d0 + j];
+          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)va);
+          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(va + 16 * 2 * D));
+          vop[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+        }
+  #pragma unroll
+        for (int j = 0; j < NB; ++j)
+          oacc[d0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vop[j]), pk, oacc[d0 + j], 0, 0, 0);
+      }
+    };
+
+    // Two stages per barrier (measured: the barrier, where every wave waits for
+    // the slowest, costs more than the shorter look-ahead): the pair starting at
+    // stage st waits for stages st, st + 1, then refills the ring slots of
+    // stages st - 2, st - 1 (consumed by every wave before the barrier) with
+    // stages st + 2, st + 3, and computes its two tiles.
+    auto pair = [&](int st, auto s0, auto s1) {
+      PLSH_WAIT_VM_LGKM0(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (st == 0 && kk == 0) {
+        // the Q fragment from the wave's staged rows, then a barrier: every wave
+        // has its fragment before slots 2, 3 take stages 2, 3
+        const char *qt = (const char *)lds.kv[2][0] + wave * 32 * D;
+  #pragma unroll
+        for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qt + swz<D>(qc, 4 * c + gq)));
+        PLSH_WAIT_VM_LGKM0(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      if (st + 2 < nst) issue_stage(st + 2, (decltype(s0)::value + 2) % kRing);
+      if (st + 3 < nst) issue_stage(st + 3, (decltype(s1)::value + 2) % kRing);
+      if (st == 0 && active) {  // the edge lists landed with stage 0
+        pl = pos_at(evl, 0);
+        if (!CAUSAL) pt = pos_at(evt, 0);
+      }
+      if (st >= sa && st < sb) {
+        qk_tile(s0);
+        finish_tile(st, s0);
+      }
+      if (st + 1 < nst && st + 1 >= sa && st + 1 < sb) {
+        qk_tile(s1);
+        finish_tile(st + 1, s1);
+      }
+    };
+    for (int st0 = 0; st0 < nst; st0 += kRing) {
+      pair(st0, SlotC<0>{}, SlotC<1>{});
+      if (st0 + 2 < nst) pair(st0 + 2, SlotC<2>{}, SlotC<3>{});
+    }
   }
 
   // a8: normalisation epilogue, one store per output element; the row sum
@@ -2278,16 +2296,17 @@ plsh_status free_records(void *ws, hipStream_t st, const char *who, plsh_status 
   return rc;
 }
 
-// One MFMA kernel over records ws (causal records for modes 0 and 1 of a
+// One MFMA kernel over records ws (causal records for modes 0, 1 and 3 of a
 // causal call, non-causal ones otherwise).  mode 0: the estimator
 // (attn_mfma_kernel); 1: its backward dQ (attn_dq_kernel); 2: its backward
-// dK, dV into dk, dv (attn_dkv_kernel).
+// dK, dV into dk, dv (attn_dkv_kernel); 3: the estimator walking the samples
+// one by one over single-sample records (attn_mfma_kernel<.., true>).
 plsh_status launch_attn(const dev::AttnArgs &a, int d, int causal, hipStream_t st, const char *who, int mode,
                         const void *ws, void *dk = nullptr, void *dv = nullptr) {
   const int64_t units = mode == 2 ? (int64_t)a.batch * a.kv_heads : (int64_t)a.batch * a.heads;
   const dim3 grid((unsigned)(a.groups * units)), block(64 * dev::kWaves);
   const uint8_t *w8 = (const uint8_t *)ws;
-  const size_t shm = 4 * dev::ev_wave_bytes(a.s, causal != 0 && mode != 2);
+  const size_t shm = 4 * dev::ev_wave_bytes(mode == 3 ? 1 : a.s, causal != 0 && mode != 2);
   auto *tm = timer_slot();
   if (tm) (void)hipEventRecord(tm->first, st);
   if (mode == 2) {
@@ -2298,6 +2317,14 @@ plsh_status launch_attn(const dev::AttnArgs &a, int d, int causal, hipStream_t s
     } else {
       if (causal) hipLaunchKernelGGL((dev::attn_dkv_kernel<128, true>), grid, block, shm, st, a, w8, k16, v16);
       else hipLaunchKernelGGL((dev::attn_dkv_kernel<128, false>), grid, block, shm, st, a, w8, k16, v16);
+    }
+  } else if (mode == 3) {
+    if (d == 64) {
+      if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<64, true, true>), grid, block, shm, st, a, w8);
+      else hipLaunchKernelGGL((dev::attn_mfma_kernel<64, false, true>), grid, block, shm, st, a, w8);
+    } else {
+      if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<128, true, true>), grid, block, shm, st, a, w8);
+      else hipLaunchKernelGGL((dev::attn_mfma_kernel<128, false, true>), grid, block, shm, st, a, w8);
     }
   } else if (mode == 1) {
     if (d == 64) {
@@ -2494,6 +2521,35 @@ extern "C" plsh_status plsh_alibi_attention_unfused(const void *q, const void *k
     return fail(PLSH_ERR_HIP, "%s: partials release failed: %s", who, hipGetErrorString(e));
   }
   return rc;
+}
+
+// The estimate with the samples walked one by one (see include/plsh.h).
+extern "C" plsh_status plsh_alibi_attention_walk(const void *q, const void *k, const void *v, void *out,
+                                                 int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                                 int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                                 const plsh_tables *boundaries, int32_t causal,
+                                                 plsh_stream_t stream) {
+  static const char *who = "plsh_alibi_attention_walk";
+  clear_error();
+  plsh_status st = check_common(q, k, v, out, batch, n, heads, kv_heads, d, dtype, sigma, s, boundaries, who);
+  if (st != PLSH_OK) return st;
+  if (dtype != PLSH_BF16) return fail(PLSH_ERR_UNSUPPORTED, "%s: only bf16 is supported", who);
+  if ((int64_t)heads * s > INT32_MAX / ((n + 31) / 32))
+    return fail(PLSH_ERR_UNSUPPORTED, "%s: heads * s * ceil(n / 32) records exceed 2^31", who);
+  if ((st = have_device(who)) != PLSH_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  dev::AttnArgs a;
+  fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
+  // single-sample records: (head h, sample k) as pseudo-head h s + k, whose
+  // parameters are row h s + k of the table
+  dev::AttnArgs ar = a;
+  ar.heads = heads * s;
+  ar.s = 1;
+  ar.pstride = 1;
+  void *rec = nullptr;
+  plsh_status rc = build_records(ar, causal != 0, hs, who, &rec);
+  if (rc == PLSH_OK) rc = launch_attn(a, d, causal != 0, hs, who, 3, rec);
+  return free_records(rec, hs, who, rc);
 }
 
 // Gradients of the estimate for fixed tables (see include/plsh.h).

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "PLSH_OK", 1: "PLSH_ERR_ARG", 2: "PLSH_ERR_TABLE", 3: "PLSH_E
 
 EXPORTED = ["plsh_sample_tables", "plsh_build_tables", "plsh_validate_tables", "plsh_count_work",
             "plsh_alibi_attention", "plsh_debug_block_intervals",
-            "plsh_debug_attention_reference", "plsh_alibi_attention_unfused",
+            "plsh_debug_attention_reference", "plsh_alibi_attention_unfused", "plsh_alibi_attention_walk",
             "plsh_alibi_attention_backward", "plsh_exact_alibi_attention",
             "plsh_sample_params_device", "plsh_kernel_timer", "plsh_kernel_timer_read", "plsh_last_error"]
 
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         L.plsh_alibi_attention.argtypes = attn
         L.plsh_debug_attention_reference.argtypes = attn
         L.plsh_alibi_attention_unfused.argtypes = attn
+        L.plsh_alibi_attention_walk.argtypes = attn
         L.plsh_alibi_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                     ctypes.c_int, vp, i32, TP, i32, vp]
         L.plsh_debug_block_intervals.argtypes = [TP, vp, vp]
@@ -242,6 +243,13 @@ def attention_unfused(q, k, v, sigma, s, tables: DeviceTables, causal: bool = Fa
     """plsh_alibi_attention_unfused: s single-sample passes plus a
     log-sum-exp combine (ablation of the sample fusion)."""
     return _attention(lib().plsh_alibi_attention_unfused, q, k, v, sigma, s, tables, causal, out, stream)
+
+
+def attention_walk(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
+                   out: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
+    """plsh_alibi_attention_walk: the samples walked one by one with 0/1
+    masks inside one kernel (ablation of the sample fusion)."""
+    return _attention(lib().plsh_alibi_attention_walk, q, k, v, sigma, s, tables, causal, out, stream)
 
 
 def attention_backward(q, k, v, dout, sigma, s, tables: DeviceTables, causal: bool = False,

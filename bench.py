@@ -23,7 +23,8 @@ sequence lengths and prints one JSON line per length.
 The default run also times, outside the timed steps and on the same inputs,
 the exact-ALiBi kernel ("exact_alibi_comparator"), fixed blocks through the
 estimator ("fixed_blocks_baseline"), the unfused per-sample form
-("unfused_ablation") and the backward for fixed tables ("backward");
+("unfused_ablation"), the per-sample walk inside one kernel
+("walk_ablation") and the backward for fixed tables ("backward");
 --no-comparators skips them (profiling runs).
 """
 
@@ -308,6 +309,23 @@ def main():
         log(f"[bench] unfused: {uf_ms:.3f} ms ({uf_ms / ms:.1f}x the fused call), parity vs oracle {uf_parity:.3e}")
         del uf_out
 
+    # the literal walk (one MFMA pass per sample with 0/1 masks inside one
+    # kernel): the MFMA work the multiplicity fusion saves
+    walk_rec = None
+    if not args.no_comparators:
+        wk_out = torch.empty_like(qd)
+        wk_ms, wk_kernel_ms = time_calls(lambda: plsh.attention_walk(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal,
+                                                                    out=wk_out), 3)
+        wk_parity = float(np.abs(W.to_f64(wk_out[:, :, rows]) - est).max())
+        walk_rec = {"ms": wk_ms, "kernel_ms": wk_kernel_ms, "over_fused_call": wk_ms / ms,
+                    "over_fused_kernel": wk_kernel_ms / kernel_ms,
+                    "s_walk_tflops_in_kernel": f_alg / (wk_kernel_ms / 1e3) / 1e12,
+                    "mfma_work_over_fused": pairs_alg / pairs_distinct,
+                    "parity_sampled_rows_max_abs": wk_parity}
+        log(f"[bench] walk: {wk_ms:.3f} ms ({wk_ms / ms:.1f}x the fused call; kernel {wk_kernel_ms:.3f} ms, "
+            f"{walk_rec['s_walk_tflops_in_kernel']:.0f} TFLOP/s of s-walk work), parity vs oracle {wk_parity:.3e}")
+        del wk_out
+
     # the backward for fixed tables (a statistics pass of the estimator, the
     # D = dO.O pass, the dQ kernel, the dK/dV kernel): its call time, and dq
     # on the sampled rows against the oracle's row-local gradient
@@ -374,6 +392,7 @@ def main():
         "exact_alibi_comparator": exact_rec,
         "fixed_blocks_baseline": fixed_rec,
         "unfused_ablation": unfused_rec,
+        "walk_ablation": walk_rec,
         "backward": bwd_rec,
         "kernel_sha": kernel_sha(),
     }

@@ -213,6 +213,29 @@ plsh_status plsh_debug_block_intervals(const plsh_tables *boundaries, int32_t *l
                                        plsh_stream_t stream);
 
 /*
+ * plsh_alibi_attention_walk -- the same estimate as plsh_alibi_attention,
+ * computed the literal way of Methodology §3 (Theorem 2.2): for every
+ * sample k in turn, attention of each row i to its block B_k(i) alone (a
+ * 0/1 mask), all samples accumulated into one online softmax per row, so
+ * that out_i = sum_k sum_{j in B_k(i)} e^{q_i.k_j} v_j / sum_k sum_{j in
+ * B_k(i)} e^{q_i.k_j}: the ratio of sums of the fused kernel, with each
+ * in-block pair evaluated once per sample that holds it.  An ablation of the
+ * sample fusion (its MFMA work is the s-walk count of plsh_count_work).
+ * Arguments as plsh_alibi_attention; bf16 only, s <= 255.
+ * Kernels: the block-edge pre-pass over heads*s single-sample record sets,
+ * then the MFMA attention kernel looping over the samples.
+ * Device memory: heads*s*ceil(n/32)*1328 bytes of records from the
+ * stream-ordered allocator on `stream`, released within the call.
+ * Errors: as plsh_alibi_attention, and PLSH_ERR_UNSUPPORTED for fp32 or when
+ * heads*s*ceil(n/32) exceeds 2^31.
+ */
+plsh_status plsh_alibi_attention_walk(const void *q, const void *k, const void *v, void *out,
+                                      int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                      int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                      const plsh_tables *boundaries, int32_t causal,
+                                      plsh_stream_t stream);
+
+/*
  * plsh_alibi_attention_backward -- gradients of the estimate of
  * plsh_alibi_attention for fixed tables (the pages train with the method,
  * Experimental Validation).  With P_ij = c_ij e^{q_i.k_j} / sum_l c_il

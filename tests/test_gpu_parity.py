@@ -416,12 +416,12 @@ def test_fixed_blocks_repeated_samples_agree(dev):
     check_bf16(W.to_f64(o4), W.to_f64(o1), what="fixed blocks s=4 vs s=1")
 
 
-# ------------------------------------------- unfused reduction (ablation) ---
-def run_unfused(dev, w: W.Workload, rows=None):
+# ------------------------------- unfused reduction and sample walk (ablations) ---
+def run_ablation(dev, w: W.Workload, fn, rows=None):
     q, k, v = W.make_qkv(w)
     t = plsh.sample_tables(w.hash_seed, w.n, w.sigma, w.s)
-    say(w.name, "unfused", "B", w.batch, "H", w.heads, "n", w.n, "d", w.d, "s", w.s, "causal", w.causal)
-    out = plsh.attention_unfused(q.to(dev), k.to(dev), v.to(dev), w.sigma, w.s, t.to(dev), causal=w.causal)
+    say(w.name, fn.__name__, "B", w.batch, "H", w.heads, "n", w.n, "d", w.d, "s", w.s, "causal", w.causal)
+    out = fn(q.to(dev), k.to(dev), v.to(dev), w.sigma, w.s, t.to(dev), causal=w.causal)
     torch.cuda.synchronize()
     o = W.to_f64(out)
     off, st = orc.tables_from_params(w.n, t.params)
@@ -436,15 +436,41 @@ def test_unfused_matches_oracle(dev, d, causal):
     """s single-sample passes plus the log-sum-exp combine give the same
     estimate (Methodology §3 reduction, stated per sample)."""
     w = small("unfused", 2, 4, 2, 1000, d, "bf16", causal, [1.3, 9.0, 60.0, 700.0], 7)
-    o, ref = run_unfused(dev, w)
+    o, ref = run_ablation(dev, w, plsh.attention_unfused)
     check_bf16(o, ref, what=f"unfused d={d} causal={causal}")
 
 
 def test_unfused_full_size_sampled_rows(dev):
     w = W.get("mistral-7b-n16384-s20")
     rows = W.sample_rows(w.n, 32, seed=29)
-    o, ref = run_unfused(dev, w, rows=rows)
+    o, ref = run_ablation(dev, w, plsh.attention_unfused, rows=rows)
     check_bf16(o, ref, what="unfused mistral")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_walk_matches_oracle(dev, d, causal):
+    """The samples walked one by one with 0/1 masks inside one kernel
+    (Methodology §3 reduction, literal form) give the estimate."""
+    w = small("walk", 2, 4, 2, 1000, d, "bf16", causal, [1.3, 9.0, 60.0, 700.0], 7)
+    o, ref = run_ablation(dev, w, plsh.attention_walk)
+    check_bf16(o, ref, what=f"walk d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("n,s,causal", [(1, 3, True), (33, 5, False), (300, 200, True), (300, 255, False)])
+def test_walk_ragged_and_many_samples(dev, n, s, causal):
+    """Tiny and ragged n, and s beyond the fused MFMA kernel's 124 (the walk
+    keeps one sample's edges in LDS at a time)."""
+    w = small("walk-ragged", 1, 3, 1, n, 64, "bf16", causal, [0.9, 12.0, 150.0], s)
+    o, ref = run_ablation(dev, w, plsh.attention_walk)
+    check_bf16(o, ref, what=f"walk n={n} s={s} causal={causal}")
+
+
+def test_walk_full_size_sampled_rows(dev):
+    w = W.get("mistral-7b-n16384-s20")
+    rows = W.sample_rows(w.n, 32, seed=41)
+    o, ref = run_ablation(dev, w, plsh.attention_walk, rows=rows)
+    check_bf16(o, ref, what="walk mistral")
 
 
 # ------------------------------------------------------- device sampler ---

@@ -247,6 +247,24 @@ def test_exact_attention_rejects_bad_sigma_and_needs_a_device():
         assert st == plsh.PLSH_ERR_HIP, msg
 
 
+def test_walk_argument_errors_and_device():
+    """plsh_alibi_attention_walk validates as the estimator, bf16 only."""
+    import torch
+    L, a, keep = _attn_args(dtype=plsh.PLSH_F32)
+    args = [a[x] for x in ("q", "k", "v", "out", "batch", "n", "heads", "kv_heads", "d", "dtype", "sigma", "s",
+                           "tables", "causal", "stream")]
+    assert L.plsh_alibi_attention_walk(*args) == plsh.PLSH_ERR_UNSUPPORTED
+    args[9] = plsh.PLSH_BF16
+    args[0] = None
+    assert L.plsh_alibi_attention_walk(*args) == plsh.PLSH_ERR_ARG
+    args[0] = a["q"]
+    args[8] = 96
+    assert L.plsh_alibi_attention_walk(*args) == plsh.PLSH_ERR_UNSUPPORTED
+    args[8] = 64
+    if not torch.cuda.is_available():
+        assert L.plsh_alibi_attention_walk(*args) == plsh.PLSH_ERR_HIP, L.plsh_last_error()
+
+
 def _bwd_call(**over):
     L, a, keep = _attn_args(**over)
     b = dict(dout=0x50000, dq=0x60000, dk=0x70000, dv=0x80000)
