@@ -27,6 +27,7 @@
 // Row i = r0 + t then has lo_k(i) = r0 + (highest set bit <= t) or lead_k, and
 // hi_k(i) = r0 + (lowest set bit > t) or trail_k.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -2224,8 +2225,9 @@ void fill_args(dev::AttnArgs &a, const void *q, const void *k, const void *v, vo
 }
 
 // Per-thread timer of the attention kernel (measurement aid): while enabled,
-// every launch records a pair of events around the attention kernel on the
-// call's stream.  The events are created on first use and reused.
+// every attention kernel is launched with a pair of events that the dispatch
+// itself stamps at its start and end (no extra packets on the stream).  The
+// events are created on first use and reused.
 struct KernelTimer {
   bool on = false;
   size_t used = 0;
@@ -2248,20 +2250,26 @@ std::pair<hipEvent_t, hipEvent_t> *timer_slot() {
   return &g_timer.ev[g_timer.used++];
 }
 
+// kernel launch, stamping the timer's events when tm is set
+template <typename... Args, typename... P>
+void launch_k(void (*kern)(Args...), dim3 grid, dim3 block, size_t shm, hipStream_t st,
+              std::pair<hipEvent_t, hipEvent_t> *tm, P... p) {
+  if (tm) hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)shm, st, tm->first, tm->second, 0u, p...);
+  else hipLaunchKernelGGL(kern, grid, block, shm, st, p...);
+}
+
 plsh_status launch_valu(const dev::AttnArgs &a, int d, plsh_dtype dtype, int causal, hipStream_t st,
                         const char *who) {
   const size_t shm = 4 * dev::valu_wave_bytes(a.s, d);
   const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(256);
   auto *tm = timer_slot();
-  if (tm) (void)hipEventRecord(tm->first, st);
   if (dtype == PLSH_F32) {
-    if (d == 64) hipLaunchKernelGGL((dev::attn_valu_kernel<float, 64>), grid, block, shm, st, a, causal);
-    else hipLaunchKernelGGL((dev::attn_valu_kernel<float, 128>), grid, block, shm, st, a, causal);
+    if (d == 64) launch_k(dev::attn_valu_kernel<float, 64>, grid, block, shm, st, tm, a, causal);
+    else launch_k(dev::attn_valu_kernel<float, 128>, grid, block, shm, st, tm, a, causal);
   } else {
-    if (d == 64) hipLaunchKernelGGL((dev::attn_valu_kernel<uint16_t, 64>), grid, block, shm, st, a, causal);
-    else hipLaunchKernelGGL((dev::attn_valu_kernel<uint16_t, 128>), grid, block, shm, st, a, causal);
+    if (d == 64) launch_k(dev::attn_valu_kernel<uint16_t, 64>, grid, block, shm, st, tm, a, causal);
+    else launch_k(dev::attn_valu_kernel<uint16_t, 128>, grid, block, shm, st, tm, a, causal);
   }
-  if (tm) (void)hipEventRecord(tm->second, st);
   return launch_check(who);
 }
 
@@ -2308,40 +2316,38 @@ plsh_status launch_attn(const dev::AttnArgs &a, int d, int causal, hipStream_t s
   const uint8_t *w8 = (const uint8_t *)ws;
   const size_t shm = 4 * dev::ev_wave_bytes(mode == 3 ? 1 : a.s, causal != 0 && mode != 2);
   auto *tm = timer_slot();
-  if (tm) (void)hipEventRecord(tm->first, st);
   if (mode == 2) {
     uint16_t *k16 = (uint16_t *)dk, *v16 = (uint16_t *)dv;
     if (d == 64) {
-      if (causal) hipLaunchKernelGGL((dev::attn_dkv_kernel<64, true>), grid, block, shm, st, a, w8, k16, v16);
-      else hipLaunchKernelGGL((dev::attn_dkv_kernel<64, false>), grid, block, shm, st, a, w8, k16, v16);
+      if (causal) launch_k(dev::attn_dkv_kernel<64, true>, grid, block, shm, st, tm, a, w8, k16, v16);
+      else launch_k(dev::attn_dkv_kernel<64, false>, grid, block, shm, st, tm, a, w8, k16, v16);
     } else {
-      if (causal) hipLaunchKernelGGL((dev::attn_dkv_kernel<128, true>), grid, block, shm, st, a, w8, k16, v16);
-      else hipLaunchKernelGGL((dev::attn_dkv_kernel<128, false>), grid, block, shm, st, a, w8, k16, v16);
+      if (causal) launch_k(dev::attn_dkv_kernel<128, true>, grid, block, shm, st, tm, a, w8, k16, v16);
+      else launch_k(dev::attn_dkv_kernel<128, false>, grid, block, shm, st, tm, a, w8, k16, v16);
     }
   } else if (mode == 3) {
     if (d == 64) {
-      if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<64, true, true>), grid, block, shm, st, a, w8);
-      else hipLaunchKernelGGL((dev::attn_mfma_kernel<64, false, true>), grid, block, shm, st, a, w8);
+      if (causal) launch_k(dev::attn_mfma_kernel<64, true, true>, grid, block, shm, st, tm, a, w8);
+      else launch_k(dev::attn_mfma_kernel<64, false, true>, grid, block, shm, st, tm, a, w8);
     } else {
-      if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<128, true, true>), grid, block, shm, st, a, w8);
-      else hipLaunchKernelGGL((dev::attn_mfma_kernel<128, false, true>), grid, block, shm, st, a, w8);
+      if (causal) launch_k(dev::attn_mfma_kernel<128, true, true>, grid, block, shm, st, tm, a, w8);
+      else launch_k(dev::attn_mfma_kernel<128, false, true>, grid, block, shm, st, tm, a, w8);
     }
   } else if (mode == 1) {
     if (d == 64) {
-      if (causal) hipLaunchKernelGGL((dev::attn_dq_kernel<64, true>), grid, block, shm, st, a, w8);
-      else hipLaunchKernelGGL((dev::attn_dq_kernel<64, false>), grid, block, shm, st, a, w8);
+      if (causal) launch_k(dev::attn_dq_kernel<64, true>, grid, block, shm, st, tm, a, w8);
+      else launch_k(dev::attn_dq_kernel<64, false>, grid, block, shm, st, tm, a, w8);
     } else {
-      if (causal) hipLaunchKernelGGL((dev::attn_dq_kernel<128, true>), grid, block, shm, st, a, w8);
-      else hipLaunchKernelGGL((dev::attn_dq_kernel<128, false>), grid, block, shm, st, a, w8);
+      if (causal) launch_k(dev::attn_dq_kernel<128, true>, grid, block, shm, st, tm, a, w8);
+      else launch_k(dev::attn_dq_kernel<128, false>, grid, block, shm, st, tm, a, w8);
     }
   } else if (d == 64) {
-    if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<64, true>), grid, block, shm, st, a, w8);
-    else hipLaunchKernelGGL((dev::attn_mfma_kernel<64, false>), grid, block, shm, st, a, w8);
+    if (causal) launch_k(dev::attn_mfma_kernel<64, true>, grid, block, shm, st, tm, a, w8);
+    else launch_k(dev::attn_mfma_kernel<64, false>, grid, block, shm, st, tm, a, w8);
   } else {
-    if (causal) hipLaunchKernelGGL((dev::attn_mfma_kernel<128, true>), grid, block, shm, st, a, w8);
-    else hipLaunchKernelGGL((dev::attn_mfma_kernel<128, false>), grid, block, shm, st, a, w8);
+    if (causal) launch_k(dev::attn_mfma_kernel<128, true>, grid, block, shm, st, tm, a, w8);
+    else launch_k(dev::attn_mfma_kernel<128, false>, grid, block, shm, st, tm, a, w8);
   }
-  if (tm) (void)hipEventRecord(tm->second, st);
   return launch_check(who);
 }
 
@@ -2385,15 +2391,13 @@ plsh_status check_exact(const void *q, const void *k, const void *v, void *out, 
 plsh_status launch_exact(const dev::ExactArgs &a, int d, int causal, hipStream_t st, const char *who) {
   const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(64 * dev::kWaves);
   auto *tm = timer_slot();
-  if (tm) (void)hipEventRecord(tm->first, st);
   if (d == 64) {
-    if (causal) hipLaunchKernelGGL((dev::exact_mfma_kernel<64, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((dev::exact_mfma_kernel<64, false>), grid, block, 0, st, a);
+    if (causal) launch_k(dev::exact_mfma_kernel<64, true>, grid, block, 0, st, tm, a);
+    else launch_k(dev::exact_mfma_kernel<64, false>, grid, block, 0, st, tm, a);
   } else {
-    if (causal) hipLaunchKernelGGL((dev::exact_mfma_kernel<128, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((dev::exact_mfma_kernel<128, false>), grid, block, 0, st, a);
+    if (causal) launch_k(dev::exact_mfma_kernel<128, true>, grid, block, 0, st, tm, a);
+    else launch_k(dev::exact_mfma_kernel<128, false>, grid, block, 0, st, tm, a);
   }
-  if (tm) (void)hipEventRecord(tm->second, st);
   return launch_check(who);
 }
 

@@ -310,11 +310,13 @@ plsh_status plsh_exact_alibi_attention(const void *q, const void *k, const void 
 
 /*
  * plsh_kernel_timer -- measurement aid (no part of the method).  With
- * enable != 0, every later plsh_alibi_attention / plsh_debug_attention_reference
- * / plsh_exact_alibi_attention call of this thread records a pair of HIP
- * events on its stream immediately before and after its attention kernel
- * (the block-edge pre-pass is outside the pair); enable == 0 stops recording.  Either call discards pairs not yet
- * read.  The events are created on first use and kept for reuse by the thread.
+ * enable != 0, every later call of this thread launches each attention kernel
+ * (the estimator's, the walk's, the backward's dQ and dK/dV, the exact
+ * comparator's and the VALU reference's; not the block-edge pre-pass) with a
+ * pair of HIP events that the dispatch itself stamps at the kernel's start
+ * and end (hipExtLaunchKernelGGL: no extra packets on the stream); enable == 0
+ * stops recording.  Either call discards pairs not yet read.  The events are
+ * created on first use and kept for reuse by the thread.
  */
 plsh_status plsh_kernel_timer(int32_t enable);
 
