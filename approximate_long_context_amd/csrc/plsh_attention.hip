@@ -2273,11 +2273,25 @@ plsh_status launch_valu(const dev::AttnArgs &a, int d, plsh_dtype dtype, int cau
   return launch_check(who);
 }
 
-// The block-edge records of every (head, 32-row group), causal or not, into a
-// workspace from the stream-ordered allocator (released by free_records).
-plsh_status build_records(const dev::AttnArgs &a, bool causal, hipStream_t st, const char *who, void **ws) {
+// bytes of the block-edge records of every (head, 32-row group)
+size_t records_bytes(int n, int heads, int s) { return (size_t)heads * ((n + 31) / 32) * dev::rec_bytes(s); }
+
+// The block-edge records of every (head, 32-row group), causal or not, into
+// ws (records_bytes(a.n, a.heads, a.s) bytes, 16-byte aligned).
+plsh_status launch_edges(const dev::AttnArgs &a, bool causal, hipStream_t st, const char *who, void *ws) {
   const int g32 = (a.n + 31) / 32;
-  const size_t ws_bytes = (size_t)a.heads * g32 * dev::rec_bytes(a.s);
+  const int items = a.heads * g32;
+  const dim3 egrid((unsigned)((items + 3) / 4)), eblock(256);
+  const size_t eshm = 4 * (dev::wavetab_bytes(a.s) + 32 * 16 * 4);
+  if (causal) hipLaunchKernelGGL(dev::edges_kernel<true>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)ws);
+  else hipLaunchKernelGGL(dev::edges_kernel<false>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)ws);
+  return launch_check(who);
+}
+
+// The records into a workspace from the stream-ordered allocator (released by
+// free_records).
+plsh_status build_records(const dev::AttnArgs &a, bool causal, hipStream_t st, const char *who, void **ws) {
+  const size_t ws_bytes = records_bytes(a.n, a.heads, a.s);
   *ws = nullptr;
   hipError_t e = hipMallocAsync(ws, ws_bytes, st);
   if (e != hipSuccess) {
@@ -2286,12 +2300,7 @@ plsh_status build_records(const dev::AttnArgs &a, bool causal, hipStream_t st, c
     return fail(PLSH_ERR_HIP, "%s: workspace allocation of %zu bytes failed: %s", who, ws_bytes,
                 hipGetErrorString(e));
   }
-  const int items = a.heads * g32;
-  const dim3 egrid((unsigned)((items + 3) / 4)), eblock(256);
-  const size_t eshm = 4 * (dev::wavetab_bytes(a.s) + 32 * 16 * 4);
-  if (causal) hipLaunchKernelGGL(dev::edges_kernel<true>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)*ws);
-  else hipLaunchKernelGGL(dev::edges_kernel<false>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)*ws);
-  return launch_check(who);
+  return launch_edges(a, causal, st, who, *ws);
 }
 
 plsh_status free_records(void *ws, hipStream_t st, const char *who, plsh_status rc) {
@@ -2351,8 +2360,15 @@ plsh_status launch_attn(const dev::AttnArgs &a, int d, int causal, hipStream_t s
   return launch_check(who);
 }
 
-// The estimator: its records, then attn_mfma_kernel.
-plsh_status launch_mfma(const dev::AttnArgs &a, int d, int causal, hipStream_t st, const char *who) {
+// The estimator: its records, then attn_mfma_kernel.  The records go to the
+// caller's workspace when one is given, else to one from the stream-ordered
+// allocator.
+plsh_status launch_mfma(const dev::AttnArgs &a, int d, int causal, hipStream_t st, const char *who,
+                        void *caller_ws = nullptr) {
+  if (caller_ws) {
+    plsh_status rc = launch_edges(a, causal != 0, st, who, caller_ws);
+    return rc == PLSH_OK ? launch_attn(a, d, causal, st, who, 0, caller_ws) : rc;
+  }
   void *ws = nullptr;
   plsh_status rc = build_records(a, causal != 0, st, who, &ws);
   if (rc == PLSH_OK) rc = launch_attn(a, d, causal, st, who, 0, ws);
@@ -2419,6 +2435,49 @@ extern "C" plsh_status plsh_alibi_attention(const void *q, const void *k, const 
   dev::AttnArgs a;
   fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
   if (dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples) return launch_mfma(a, d, causal != 0, (hipStream_t)stream, who);
+  return launch_valu(a, d, dtype, causal != 0, (hipStream_t)stream, who);
+}
+
+// Bytes of workspace plsh_alibi_attention_ws takes for a call (0 on the
+// paths that need none).
+extern "C" plsh_status plsh_attention_workspace_size(int32_t n, int32_t heads, int32_t s, plsh_dtype dtype,
+                                                     int64_t *bytes) {
+  clear_error();
+  if (!bytes) return fail(PLSH_ERR_ARG, "plsh_attention_workspace_size: null pointer argument");
+  if (n < 1 || heads < 1 || s < 1) return fail(PLSH_ERR_ARG, "plsh_attention_workspace_size: need n, heads, s >= 1");
+  if (dtype != PLSH_BF16 && dtype != PLSH_F32) return fail(PLSH_ERR_UNSUPPORTED, "plsh_attention_workspace_size: unknown dtype");
+  *bytes = (dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples) ? (int64_t)records_bytes(n, heads, s) : 0;
+  return PLSH_OK;
+}
+
+// plsh_alibi_attention with the pre-pass records in a caller-owned workspace.
+extern "C" plsh_status plsh_alibi_attention_ws(const void *q, const void *k, const void *v, void *out,
+                                               int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                               int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                               const plsh_tables *boundaries, int32_t causal, void *workspace,
+                                               int64_t workspace_bytes, plsh_stream_t stream) {
+  static const char *who = "plsh_alibi_attention_ws";
+  clear_error();
+  plsh_status st = check_common(q, k, v, out, batch, n, heads, kv_heads, d, dtype, sigma, s, boundaries, who);
+  if (st != PLSH_OK) return st;
+  const bool mfma = dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples;
+  const size_t need = mfma ? records_bytes(n, heads, s) : 0;
+  if (workspace_bytes < 0 || (size_t)workspace_bytes < need)
+    return fail(PLSH_ERR_CAPACITY, "%s: workspace of %lld bytes, the call needs %zu", who,
+                (long long)workspace_bytes, need);
+  if (need && !workspace) return fail(PLSH_ERR_ARG, "%s: null workspace", who);
+  if ((uintptr_t)workspace & 15u) return fail(PLSH_ERR_ARG, "%s: workspace must be 16-byte aligned", who);
+  if (need) {
+    const size_t esz = dtype == PLSH_F32 ? 4 : 2;
+    const size_t qbytes = (size_t)batch * heads * n * d * esz, kbytes = (size_t)batch * kv_heads * n * d * esz;
+    if (overlaps(workspace, need, q, qbytes) || overlaps(workspace, need, k, kbytes) ||
+        overlaps(workspace, need, v, kbytes) || overlaps(workspace, need, out, qbytes))
+      return fail(PLSH_ERR_ARG, "%s: workspace overlaps q, k, v or out", who);
+  }
+  if ((st = have_device(who)) != PLSH_OK) return st;
+  dev::AttnArgs a;
+  fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
+  if (mfma) return launch_mfma(a, d, causal != 0, (hipStream_t)stream, who, workspace);
   return launch_valu(a, d, dtype, causal != 0, (hipStream_t)stream, who);
 }
 

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "PLSH_OK", 1: "PLSH_ERR_ARG", 2: "PLSH_ERR_TABLE", 3: "PLSH_E
                 4: "PLSH_ERR_CAPACITY", 5: "PLSH_ERR_HIP"}
 
 EXPORTED = ["plsh_sample_tables", "plsh_build_tables", "plsh_validate_tables", "plsh_count_work",
-            "plsh_alibi_attention", "plsh_debug_block_intervals",
+            "plsh_alibi_attention", "plsh_alibi_attention_ws", "plsh_attention_workspace_size",
+            "plsh_debug_block_intervals",
             "plsh_debug_attention_reference", "plsh_alibi_attention_unfused", "plsh_alibi_attention_walk",
             "plsh_alibi_attention_backward", "plsh_exact_alibi_attention",
             "plsh_sample_params_device", "plsh_kernel_timer", "plsh_kernel_timer_read", "plsh_last_error"]
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.plsh_debug_attention_reference.argtypes = attn
         L.plsh_alibi_attention_unfused.argtypes = attn
         L.plsh_alibi_attention_walk.argtypes = attn
+        L.plsh_alibi_attention_ws.argtypes = attn[:-1] + [vp, i64, vp]
+        L.plsh_attention_workspace_size.argtypes = [i32, i32, i32, ctypes.c_int, ctypes.POINTER(i64)]
         L.plsh_alibi_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                     ctypes.c_int, vp, i32, TP, i32, vp]
         L.plsh_debug_block_intervals.argtypes = [TP, vp, vp]
@@ -212,7 +215,7 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise PlshError(PLSH_ERR_UNSUPPORTED, f"dtype {t.dtype} not supported")
 
 
-def _attention(fn, q, k, v, sigma, s, tables: DeviceTables, causal, out, stream):
+def _attention(fn, q, k, v, sigma, s, tables: DeviceTables, causal, out, stream, ws=None):
     for name, x in (("q", q), ("k", k), ("v", v)):
         if not x.is_contiguous():
             raise PlshError(PLSH_ERR_ARG, f"{name} must be contiguous")
@@ -227,14 +230,46 @@ def _attention(fn, q, k, v, sigma, s, tables: DeviceTables, causal, out, stream)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = tables.c_struct()
-    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, n, H, k.shape[1], d,
-              _dtype_code(q), _ptr(sig), s, ctypes.byref(st), int(bool(causal)), stream))
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, n, H, k.shape[1], d,
+            _dtype_code(q), _ptr(sig), s, ctypes.byref(st), int(bool(causal))]
+    if ws is not None:
+        args += list(ws)
+    _check(fn(*args, stream))
     return out
 
 
+def workspace_size(n: int, heads: int, s: int, dtype: torch.dtype) -> int:
+    """plsh_attention_workspace_size: bytes of workspace attention() takes."""
+    nb = ctypes.c_int64(0)
+    code = PLSH_BF16 if dtype == torch.bfloat16 else PLSH_F32 if dtype == torch.float32 else -1
+    _check(lib().plsh_attention_workspace_size(n, heads, s, code, ctypes.byref(nb)))
+    return nb.value
+
+
 def attention(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
-              out: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
-    """plsh_alibi_attention on the current stream: q [B,H,n,d], k/v [B,Hkv,n,d]."""
+              out: Optional[torch.Tensor] = None, stream: Optional[int] = None,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The estimator, q [B,H,n,d], k/v [B,Hkv,n,d].  On torch's current
+    stream: plsh_alibi_attention_ws with `workspace` (a device uint8 tensor
+    of at least workspace_size() bytes) or one from torch's caching
+    allocator.  With an explicit `stream` and no workspace:
+    plsh_alibi_attention (the library's stream-ordered workspace)."""
+    if stream is not None and workspace is None:
+        return _attention(lib().plsh_alibi_attention, q, k, v, sigma, s, tables, causal, out, stream)
+    need = workspace_size(q.shape[2], q.shape[1], s, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != q.device:
+        raise PlshError(PLSH_ERR_ARG, "workspace must be a contiguous uint8 tensor on q's device")
+    ws = (workspace.data_ptr(), workspace.numel())
+    return _attention(lib().plsh_alibi_attention_ws, q, k, v, sigma, s, tables, causal, out, stream, ws)
+
+
+def attention_library_workspace(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
+                                out: Optional[torch.Tensor] = None,
+                                stream: Optional[int] = None) -> torch.Tensor:
+    """plsh_alibi_attention: the workspace from the library's stream-ordered
+    allocator, taken and released on the stream inside the call."""
     return _attention(lib().plsh_alibi_attention, q, k, v, sigma, s, tables, causal, out, stream)
 
 

@@ -27,8 +27,10 @@
  *   - Device memory: plsh_alibi_attention on the bf16 path takes a workspace
  *     of heads * ceil(n/32) * (1040 + 16 * E) bytes, E = s + 16 rounded up to
  *     even, from the stream-ordered allocator (hipMallocAsync on `stream`) and
- *     releases it on the same stream (hipFreeAsync) within the call; no other
- *     entry point allocates device memory.
+ *     releases it on the same stream (hipFreeAsync) within the call;
+ *     plsh_alibi_attention_ws takes the same workspace from the caller
+ *     instead.  The ablation and backward entry points allocate their own
+ *     workspaces the same way; the others allocate no device memory.
  *   - The library keeps no state besides a thread-local error string and the
  *     thread-local kernel timer below.
  */
@@ -179,6 +181,43 @@ plsh_status plsh_alibi_attention(const void *q, const void *k, const void *v, vo
                                  int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
                                  const plsh_tables *boundaries, int32_t causal,
                                  plsh_stream_t stream);
+
+/*
+ * plsh_attention_workspace_size -- bytes of device workspace that
+ * plsh_alibi_attention_ws needs for a call with these sizes: the block-edge
+ * records of the pre-pass, heads * ceil(n/32) * (1040 + 16 * E) bytes with
+ * E = s + 16 rounded up to even (bf16 with s <= 124), else 0 (the VALU
+ * kernel needs none).  Host only; needs no device.
+ *   bytes  HOST int64 output
+ * Errors: PLSH_ERR_ARG (null pointer, n, heads or s < 1),
+ * PLSH_ERR_UNSUPPORTED (unknown dtype).
+ */
+plsh_status plsh_attention_workspace_size(int32_t n, int32_t heads, int32_t s, plsh_dtype dtype,
+                                          int64_t *bytes);
+
+/*
+ * plsh_alibi_attention_ws -- plsh_alibi_attention (same estimator, same
+ * kernels, bitwise the same output) with the pre-pass records written to a
+ * caller-owned DEVICE workspace instead of one from the stream-ordered
+ * allocator, so that a caller with its own caching allocator adds no
+ * allocator operations to the stream.  Methodology §3 (Theorem 2.2), as for
+ * plsh_alibi_attention; every other argument is as there.
+ *   workspace        DEVICE, 16-byte aligned, at least
+ *                    plsh_attention_workspace_size bytes (may be NULL when
+ *                    that is 0); overwritten by the call's pre-pass and read
+ *                    by its attention kernel, so it must stay alive and
+ *                    untouched until the stream work completes; calls that
+ *                    share a workspace must be ordered (same stream).
+ *   workspace_bytes  its size in bytes
+ * Errors: those of plsh_alibi_attention, plus PLSH_ERR_CAPACITY (workspace
+ * smaller than needed) and PLSH_ERR_ARG (null or misaligned workspace, or one
+ * overlapping q, k, v or out).
+ */
+plsh_status plsh_alibi_attention_ws(const void *q, const void *k, const void *v, void *out,
+                                    int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                    int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                    const plsh_tables *boundaries, int32_t causal, void *workspace,
+                                    int64_t workspace_bytes, plsh_stream_t stream);
 
 /*
  * plsh_sample_params_device -- the hash parameters of plsh_sample_tables,

@@ -284,6 +284,42 @@ def test_full_size_repeats_bitwise(dev, wname, causal, d):
     assert bool(torch.isfinite(first).all())
 
 
+@pytest.mark.parametrize("wname,causal", [("mistral-7b-n16384-s20", True), ("slopes-n4096", False)])
+def test_caller_workspace_bitwise_equals_library_workspace(dev, wname, causal):
+    """plsh_alibi_attention_ws (records in a caller-owned workspace) gives the
+    bits of plsh_alibi_attention (records in the library's stream-ordered
+    workspace), also with a larger, garbage-filled workspace reused by two
+    calls of different sizes, the second smaller (every byte the attention
+    kernel reads is written by the call's own pre-pass)."""
+    import dataclasses
+    w = dataclasses.replace(W.get(wname), causal=causal)
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(w.hash_seed, w.n, w.sigma, w.s).to(dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    say(w.name, "caller workspace", "causal", causal)
+    lib_out = plsh.attention_library_workspace(qd, kd, vd, w.sigma, w.s, t, causal=causal)
+    need = plsh.workspace_size(w.n, w.heads, w.s, qd.dtype)
+    ws = torch.full((need + 4096,), 0xA5, dtype=torch.uint8, device=dev)
+    own = plsh.attention(qd, kd, vd, w.sigma, w.s, t, causal=causal)
+    given = plsh.attention(qd, kd, vd, w.sigma, w.s, t, causal=causal, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(lib_out, own)
+    assert torch.equal(lib_out, given)
+    # a smaller call (fewer rows, fewer heads) in the same, now dirty workspace
+    n2, h2 = w.n // 2 + 17, w.heads // 2
+    hk2 = max(1, h2 * w.kv_heads // w.heads)
+    q2 = qd[:, :h2, :n2].contiguous()
+    k2, v2 = kd[:, :hk2, :n2].contiguous(), vd[:, :hk2, :n2].contiguous()
+    t2 = plsh.sample_tables(3, n2, w.sigma[:h2], w.s).to(dev)
+    lib2 = plsh.attention_library_workspace(q2, k2, v2, w.sigma[:h2], w.s, t2, causal=causal)
+    given2 = plsh.attention(q2, k2, v2, w.sigma[:h2], w.s, t2, causal=causal, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(lib2, given2)
+    with pytest.raises(plsh.PlshError) as e:
+        plsh.attention(qd, kd, vd, w.sigma, w.s, t, causal=causal, workspace=ws[:need - 16])
+    assert e.value.status == plsh.PLSH_ERR_CAPACITY
+
+
 # ------------------------------------------------------------------- G7 ---
 @pytest.mark.parametrize("causal", [False, True])
 def test_g7_huge_sigma_is_softmax_attention(dev, causal):

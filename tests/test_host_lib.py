@@ -195,6 +195,58 @@ def test_attention_without_device_reports_hip_error():
     assert st == plsh.PLSH_ERR_HIP, msg
 
 
+def test_workspace_size_formula():
+    """Records of the pre-pass: heads * ceil(n/32) records of 16 + 16 E + 1024
+    bytes, E = s + 16 rounded up to even; none for fp32 or s > 124."""
+    for n, heads, s in ((1, 1, 1), (512, 1, 8), (16384, 32, 20), (8193, 16, 124), (100, 3, 7)):
+        e = (s + 16 + 1) & ~1
+        want = heads * ((n + 31) // 32) * (16 + 16 * e + 1024)
+        assert plsh.workspace_size(n, heads, s, torch_dtype("bf16")) == want
+        assert plsh.workspace_size(n, heads, s, torch_dtype("f32")) == 0
+    assert plsh.workspace_size(100, 2, 125, torch_dtype("bf16")) == 0
+    nb = ctypes.c_int64(-1)
+    L = plsh.lib()
+    assert L.plsh_attention_workspace_size(0, 1, 1, plsh.PLSH_BF16, ctypes.byref(nb)) == plsh.PLSH_ERR_ARG
+    assert L.plsh_attention_workspace_size(4, 1, 1, 9, ctypes.byref(nb)) == plsh.PLSH_ERR_UNSUPPORTED
+    assert L.plsh_attention_workspace_size(4, 1, 1, plsh.PLSH_BF16, None) == plsh.PLSH_ERR_ARG
+
+
+def torch_dtype(name):
+    import torch
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def _call_ws(ws, ws_bytes, **over):
+    L, a, keep = _attn_args(**over)
+    st = L.plsh_alibi_attention_ws(a["q"], a["k"], a["v"], a["out"], a["batch"], a["n"], a["heads"],
+                                   a["kv_heads"], a["d"], a["dtype"], a["sigma"], a["s"], a["tables"],
+                                   a["causal"], ws, ws_bytes, a["stream"])
+    return st, L.plsh_last_error().decode()
+
+
+def test_attention_ws_argument_errors():
+    """The caller-workspace entry point checks its workspace before any device
+    work: too small, null, misaligned, overlapping an operand; then the common
+    argument checks as plsh_alibi_attention."""
+    need = plsh.workspace_size(64, 4, 3, torch_dtype("bf16"))
+    big = 0x4000000
+    assert _call_ws(big, need - 1)[0] == plsh.PLSH_ERR_CAPACITY
+    assert _call_ws(big, -1)[0] == plsh.PLSH_ERR_CAPACITY
+    assert _call_ws(None, need)[0] == plsh.PLSH_ERR_ARG
+    assert _call_ws(big + 8, need)[0] == plsh.PLSH_ERR_ARG
+    L, a, keep = _attn_args()
+    assert _call_ws(a["v"], need)[0] == plsh.PLSH_ERR_ARG   # overlaps v
+    assert _call_ws(big, need, d=96)[0] == plsh.PLSH_ERR_UNSUPPORTED
+    assert _call_ws(big, need, n=0)[0] == plsh.PLSH_ERR_ARG
+    # fp32 needs no workspace: a null one of size 0 passes the checks
+    import torch
+    if not torch.cuda.is_available():
+        st, msg = _call_ws(None, 0, dtype=plsh.PLSH_F32)
+        assert st == plsh.PLSH_ERR_HIP, msg
+        st, msg = _call_ws(big, need)
+        assert st == plsh.PLSH_ERR_HIP, msg
+
+
 def test_kernel_timer_without_launches():
     plsh.kernel_timer(True)
     assert plsh.kernel_timer_read() == (0, 0.0)
