@@ -128,6 +128,11 @@ __device__ __forceinline__ uint32_t other_half(uint32_t x, int lane) {
 __device__ __forceinline__ float other_half_f(float x, int lane) {
   return __uint_as_float(other_half(__float_as_uint(x), lane));
 }
+__device__ __forceinline__ double other_half_d(double x, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t lo = other_half((uint32_t)b, lane), hi = other_half((uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(lo | (hi << 32)));
+}
 
 // bits 1..t of a 32-bit mask (t in [0, 31])
 __device__ __forceinline__ uint32_t bits_1_to(int t) {
@@ -157,26 +162,37 @@ __device__ __forceinline__ WaveTab carve_wavetab(uint8_t *base, int s) {
   return w;
 }
 
-// Step 1: lanes take samples k = lane, lane + 64, ...: stage (delta, u) in
-// LDS, find the block of row r0 (lead) and of the wave's last row (trail),
-// and list the samples whose bins differ between those rows.  Returns the
-// number of listed samples (the same in every lane).
+// Step 1: the two half-waves take samples k = k0 + t, t = lane % 32, and run
+// the same instruction stream: the lower half finds the block of row r0 (its
+// first position, the lead), the upper half the block of the wave's last row
+// (one past its end, the trail), each as the first position whose bin reaches
+// a target (bin, or bin + 1).  The lower half stages (delta, u) in LDS and
+// lists the samples whose bins differ between those rows.  Returns the number
+// of listed samples (the same in every lane).
 __device__ int wave_ends(const double *prm, int s, int n, int r0, int lane, const WaveTab &w) {
   const int last = min(r0 + 31, n - 1);
+  const int t = lane & 31, hh = lane >> 5;
+  const int x = hh ? last : r0;
+  const int lo = hh ? last + 1 : 0, hi = hh ? n : r0;
+  int32_t *ends = hh ? w.trail : w.lead;
   int nact = 0;
-  for (int k0 = 0; k0 < s; k0 += 64) {
-    const int k = k0 + lane;
-    bool cross = false;
+  for (int k0 = 0; k0 < s; k0 += 32) {
+    const int k = k0 + t;
+    double b = 0.0;
     if (k < s) {
       const double dl = prm[2 * k], u = prm[2 * k + 1];
-      w.prm[2 * k] = dl;
-      w.prm[2 * k + 1] = u;
-      const double b0 = bin_of(r0, dl, u), b1 = bin_of(last, dl, u);
-      w.lead[k] = block_lo(r0, dl, u, b0);
-      w.trail[k] = block_hi(last, n, dl, u, b1);
-      w.mask[k] = 0u;
-      cross = b0 != b1;
+      if (hh == 0) {
+        w.prm[2 * k] = dl;
+        w.prm[2 * k + 1] = u;
+        w.mask[k] = 0u;
+      }
+      const double ri = 1.0 / dl;
+      b = bin_of_r(x, dl, u, ri);
+      ends[k] = first_at_least(hh ? b + 1.0 : b, lo, hi, dl, u, ri);
     }
+    // (the lane swap runs with every lane active, outside the condition)
+    const double bo = other_half_d(b, lane);
+    const bool cross = hh == 0 && k < s && b != bo;
     const uint64_t bal = __ballot(cross);
     if (cross) w.act[nact + __popcll(bal & ((1ull << lane) - 1ull))] = k;
     nact += __popcll(bal);
@@ -196,17 +212,18 @@ __device__ void wave_masks(int n, int r0, int lane, int nact, const WaveTab &w) 
     // its operands from registers instead of dependent LDS reads
     const int kc = c0 + lane < nact ? w.act[c0 + lane] : 0;
     const double dlc = w.prm[2 * kc], uc = w.prm[2 * kc + 1];
+    const double ric = 1.0 / dlc;
     const int m = min(64, nact - c0);
 #pragma unroll 2
     for (int a0 = 0; a0 < m; a0 += 2) {
       // half-wave hh takes listed sample c0 + a0 + hh
       const int src = min(a0 + hh, m - 1);
       const int k = __shfl(kc, src);
-      const double dl = __shfl(dlc, src), u = __shfl(uc, src);
+      const double dl = __shfl(dlc, src), u = __shfl(uc, src), ri = __shfl(ric, src);
       const bool have = a0 + hh < m;
       const bool valid = have && x <= last;
       double b = 0.0;
-      if (valid) b = bin_of(x, dl, u);
+      if (valid) b = bin_of_r(x, dl, u, ri);
       const double bp = __shfl_up(b, 1, 32);
       const uint64_t bal = __ballot(valid && t > 0 && b != bp);
       if (t == 0 && have) w.mask[k] = (uint32_t)(bal >> (32 * hh));

@@ -28,47 +28,59 @@ PLSH_HD double bin_of(int32_t x, double delta, double u) {
   return floor(((double)x + u) / delta);
 }
 
-// First position of the block that holds x: the smallest y in [0, x] with
-// bin(y) == bin(x) == b.  The arithmetic guess is settled with the exact
-// predicate, so the answer never depends on how the guess was rounded; a
-// bisection (bin is non-decreasing) finishes any case the local steps do not.
-// Both probes of a step are independent, so their divisions overlap.
-PLSH_HD int32_t block_lo(int32_t x, double delta, double u, double b) {
-  double c = ceil(b * delta - u);
-  int32_t y = (c <= 0.0) ? 0 : (c >= (double)x ? x : (int32_t)c);
-  for (int it = 0; it < 4; ++it) {
-    const double bl = bin_of(y > 0 ? y - 1 : 0, delta, u);
-    const double by = bin_of(y, delta, u);
-    if (y > 0 && bl >= b) { --y; continue; }
-    if (by < b) { ++y; continue; }
-    return y;
-  }
-  int32_t lo = 0, hi = x;  // bin(x) == b, so the answer lies in [0, x]
-  while (lo < hi) {
-    int32_t mid = lo + ((hi - lo) >> 1);
-    if (bin_of(mid, delta, u) >= b) hi = mid; else lo = mid + 1;
-  }
-  return lo;
+// The same bin without the division wherever that is provably safe.  With
+// a = fl(x + u), Q = a / delta exact, D = fl(Q) the correctly rounded
+// quotient and q = fl(a * rinv), rinv = fl(1 / delta): each of the three
+// roundings errs by at most 2^-53 relative, so |q - D| <= 3.02 * 2^-53 |q|.
+// If no integer lies within 2^-50 |q| of q, then D and q have the same floor.
+// (q - f and (f + 1) - q are exact by Sterbenz's lemma below 2^52; from 2^52
+// on every double is an integer, q - f == 0 and the division is taken; a
+// fused multiply-add in either difference only makes it more accurate.)
+// Otherwise, and for q == 0, inf or NaN, the defining division decides.
+PLSH_HD double bin_of_r(int32_t x, double delta, double u, double rinv) {
+  const double a = (double)x + u;
+  const double q = a * rinv;
+  const double f = floor(q);
+  const double tol = fabs(q) * 0x1p-50;
+  if (q - f > tol && (f + 1.0) - q > tol) return f;
+  return floor(a / delta);
 }
 
-// One past the last position of the block that holds x: the smallest y in
-// (x, n] with y == n or bin(y) > b, b = bin(x).
-PLSH_HD int32_t block_hi(int32_t x, int32_t n, double delta, double u, double b) {
-  double c = ceil((b + 1.0) * delta - u);
-  int32_t y = (c <= (double)(x + 1)) ? x + 1 : (c >= (double)n ? n : (int32_t)c);
+// The first position y in [lo, hi] with y == hi or bin(y) >= m, given that
+// bin(lo - 1) < m when lo > 0 (bins never decrease, so every y' in [lo, y)
+// has bin(y') < m).  The block of x starts at first_at_least(bin(x), 0, x)
+// and ends before first_at_least(bin(x) + 1, x + 1, n).  The arithmetic guess
+// ceil(m delta - u) is settled with the exact predicate, so the answer never
+// depends on how the guess was rounded; a bisection finishes any case the
+// local steps do not.  The two probes of a step are independent, so their
+// arithmetic overlaps.
+PLSH_HD int32_t first_at_least(double m, int32_t lo, int32_t hi, double delta, double u, double rinv) {
+  const double c = ceil(m * delta - u);
+  int32_t y = (c <= (double)lo) ? lo : (c >= (double)hi ? hi : (int32_t)c);
   for (int it = 0; it < 4; ++it) {
-    const double bl = bin_of(y - 1, delta, u);
-    const double by = bin_of(y, delta, u);
-    if (y > x + 1 && bl > b) { --y; continue; }
-    if (y < n && by <= b) { ++y; continue; }
+    const double bl = bin_of_r(y > lo ? y - 1 : lo, delta, u, rinv);
+    const double by = bin_of_r(y < hi ? y : lo, delta, u, rinv);
+    if (y > lo && bl >= m) { --y; continue; }
+    if (y < hi && by < m) { ++y; continue; }
     return y;
   }
-  int32_t lo = x + 1, hi = n;
-  while (lo < hi) {
-    int32_t mid = lo + ((hi - lo) >> 1);
-    if (bin_of(mid, delta, u) > b) hi = mid; else lo = mid + 1;
+  int32_t a = lo, b = hi;  // answer in [a, b]: bin(a - 1) < m, and b == hi or bin(b) >= m
+  while (a < b) {
+    const int32_t mid = a + ((b - a) >> 1);
+    if (bin_of_r(mid, delta, u, rinv) >= m) b = mid; else a = mid + 1;
   }
-  return lo;
+  return a;
+}
+
+// First position of the block that holds x (b = bin(x)).
+PLSH_HD int32_t block_lo(int32_t x, double delta, double u, double b, double rinv) {
+  return first_at_least(b, 0, x, delta, u, rinv);
+}
+
+// One past the last position of the block that holds x (b = bin(x)): the
+// first y in (x, n] with y == n or bin(y) > b.
+PLSH_HD int32_t block_hi(int32_t x, int32_t n, double delta, double u, double b, double rinv) {
+  return first_at_least(b + 1.0, x + 1, n, delta, u, rinv);
 }
 
 }  // namespace plsh

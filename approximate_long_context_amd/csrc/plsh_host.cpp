@@ -42,9 +42,10 @@ namespace {
 // Block starts of one hash: 0, each bin change, n.  Walks block by block.
 void hash_starts(int32_t n, double delta, double u, std::vector<int32_t> &out) {
   out.push_back(0);
+  const double rinv = 1.0 / delta;
   int32_t x = 0;
   while (x < n) {
-    int32_t y = block_hi(x, n, delta, u, bin_of(x, delta, u));
+    int32_t y = block_hi(x, n, delta, u, bin_of_r(x, delta, u, rinv), rinv);
     out.push_back(y);
     x = y;
   }

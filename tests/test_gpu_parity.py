@@ -122,9 +122,12 @@ def test_g1_block_intervals_integer_quotients(dev):
     exact-division fallback reproduces the oracle's scan bit for bit."""
     n = 4000
     rows = []
-    for dl in (3.0, 5.0, 6.0, 7.0, 10.0, 49.0, 96.0, 2.5, 12.75, 0.1, 1.0 / 3.0, 1e-3):
-        for u in (0.0, dl / 2.0, dl * (1.0 - 2.0 ** -40), dl * 2.0 ** -45):
-            rows.append((dl, u))
+    for d0 in (3.0, 5.0, 6.0, 7.0, 10.0, 49.0, 96.0, 2.5, 12.75, 0.1, 1.0 / 3.0, 1e-3):
+        # the pitch itself and its two neighbouring doubles
+        for dl in (d0, float(np.nextafter(d0, 0.0)), float(np.nextafter(d0, np.inf))):
+            for u in (0.0, dl / 2.0, dl * (1.0 - 2.0 ** -40), dl * 2.0 ** -45,
+                      float(np.nextafter(dl, 0.0))):
+                rows.append((dl, u))
     params = np.array(rows, dtype=np.float64)
     off, st = orc.tables_from_params(n, params)
     t = plsh.Tables(n, 1, len(rows), params, off.astype(np.int32), st.astype(np.int32))

@@ -411,6 +411,33 @@ def test_fixed_block_tables_match_oracle_scan(width):
         assert np.array_equal(r0, want)
 
 
+def _near_integer_rows():
+    """(delta, u) rows whose quotients (x + u) / delta hit integers exactly or
+    land within a few ulp of one: integer and dyadic pitches with offsets 0
+    and exact fractions, pitches one ulp off an integer or a third, and
+    offsets one ulp below delta."""
+    rows = []
+    for d in (1.0, 2.0, 3.0, 5.0, 0.5, 0.25, 1.5, 2.5, 7.0, 64.0, 0.125, 1.0 / 3.0, 0.1, 6.0,
+              10.0 / 3.0):
+        for dd in (d, np.nextafter(d, 0.0), np.nextafter(d, np.inf)):
+            for u in (0.0, dd / 2.0, dd / 3.0, np.nextafter(dd, 0.0), 2.0 ** -40, dd * 0.75):
+                if 0.0 <= u < dd:
+                    rows.append((dd, u))
+    return np.array(rows, dtype=np.float64)
+
+
+def test_build_tables_exact_near_integer_quotients():
+    """The host scan's bins (a product with the pitch's reciprocal, the
+    division taken wherever the product lies within its error bound of an
+    integer) equal the oracle's plain floor((x + u) / delta) scan, start for
+    start, where the quotient is an exact integer or within ulps of one."""
+    params = _near_integer_rows()
+    n = 2000
+    t = plsh.build_tables(n, 1, len(params), params)
+    off, st = orc.tables_from_params(n, t.params)
+    assert np.array_equal(t.offsets, off) and np.array_equal(t.starts, st)
+
+
 def test_build_tables_reproduces_the_sampler():
     t = plsh.sample_tables(11, 3000, [1.19, 16.0, 256.0], 7)
     b = plsh.build_tables(3000, 3, 7, t.params)
