@@ -39,6 +39,7 @@ Parity status per function:
   lsh_estimate             pinned (brute force n <= 64, sigma limits, s = 1,
                            error-bound inequality, convex hull)
   lsh_estimate_multiplicity pinned (brute force)
+  lsh_row_log_normaliser   pinned (brute-force row sums of A o (sum_k M) o C)
   mask_mean / matrix_errors pinned (variance identity, 1/sqrt(s) slope)
   work_counts              pinned (brute-force pair enumeration)
   lsh_estimate_grad /      pinned (central finite differences of the
@@ -67,6 +68,7 @@ __all__ = [
     "exact_alibi",
     "lsh_estimate",
     "lsh_estimate_multiplicity",
+    "lsh_row_log_normaliser",
     "multiplicity_dense",
     "alibi_matrix",
     "mask_dense",
@@ -324,6 +326,36 @@ def lsh_estimate(q: np.ndarray, k: np.ndarray, v: np.ndarray,
             m = mus.max(axis=0)
             wgt = np.exp(mus - m[None, :])
             out[b, h] = (wgt[:, :, None] * Ns).sum(axis=0) / (wgt * Zs).sum(axis=0)[:, None]
+    return out
+
+
+def lsh_row_log_normaliser(q: np.ndarray, k: np.ndarray, tables: List[List[np.ndarray]],
+                           causal: bool, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """ln of each row's normaliser, ln sum_k sum_{j in B_k(i), j in J(i)}
+    e^{q_i.k_j}: the diagonal of s D~ with D~ = diag((A o M~ o C) 1)
+    (Methodology §3, Theorem 2.2), as [B, H, rows].  Per hash, the block
+    maximum mu_k and sum Z_k of the block-walk statistics; over hashes,
+    ln sum_k e^{mu_k} Z_k taken as max + ln sum e^{mu_k - max} Z_k."""
+    B, H, n, d = q.shape
+    Hkv = k.shape[1]
+    s = len(tables[0])
+    R = n if rows is None else len(rows)
+    out = np.empty((B, H, R))
+    zero_v = np.zeros((n, d))  # (the value sums are not needed)
+    for b in range(B):
+        for h in range(H):
+            g = _kv_head(h, H, Hkv)
+            qh, kh = q[b, h], k[b, g]
+            mus = np.empty((s, R))
+            Zs = np.empty((s, R))
+            for kk in range(s):
+                st = np.asarray(tables[h][kk], dtype=np.int64)
+                if rows is None:
+                    mus[kk], Zs[kk], _ = _block_stats_full(qh, kh, zero_v, st, causal)
+                else:
+                    mus[kk], Zs[kk], _ = _block_stats_rows(qh, kh, zero_v, st, causal, np.asarray(rows))
+            m = mus.max(axis=0)
+            out[b, h] = m + np.log((np.exp(mus - m[None, :]) * Zs).sum(axis=0))
     return out
 
 

@@ -245,6 +245,39 @@ def test_p7_brute_force_small_n(causal, n, s, sigma):
         np.testing.assert_allclose(got[0, h], ref, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,s,sigma", [(9, 3, 2.0), (48, 6, 7.0)])
+def test_row_log_normaliser_brute_force(causal, n, s, sigma):
+    """The row normaliser ln sum_j c_ij e^{q_i.k_j} (Methodology §3: the
+    diagonal of s D~, D~ = diag((A o M~ o C) 1)) against the plain sum over
+    pairs, c_ij counted pair by pair from the floor formula (no table), with
+    logits large enough (|q.k| up to ~40) that a dropped maximum would
+    overflow nothing but a wrong one would show; also on a row subset."""
+    rng = np.random.default_rng(n * 7 + s)
+    q, k, _ = _rand_qkv(rng, 1, 2, 1, n, 6, scale=2.0)
+    params = orc.sample_params(11, [sigma, sigma * 3.0], s)
+    tables = [[orc.block_starts(n, *params[h * s + kk]) for kk in range(s)] for h in range(2)]
+    got = orc.lsh_row_log_normaliser(q, k, tables, causal)
+    rows = np.array([0, n // 2, n - 1])
+    sub = orc.lsh_row_log_normaliser(q, k, tables, causal, rows=rows)
+    for h in range(2):
+        want = np.empty(n)
+        for i in range(n):
+            tot = Fraction(0)
+            for j in range(n):
+                if causal and j > i:
+                    continue
+                c = 0
+                for kk in range(s):
+                    dl, u = params[h * s + kk]
+                    c += math.floor((i + u) / dl) == math.floor((j + u) / dl)
+                if c:
+                    tot += c * Fraction(math.exp(float(q[0, h, i] @ k[0, 0, j])))
+            want[i] = math.log(tot)
+        np.testing.assert_allclose(got[0, h], want, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sub[0, h], want[rows], rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------------------- P8 ---
 @pytest.mark.parametrize("causal", [False, True])
 def test_p8_large_sigma_is_plain_softmax_attention(causal):
