@@ -80,6 +80,9 @@ struct AttnArgs {
   const float *dvec;
   float *stat_lse2;
   float *stat_dvec;
+  // when set, the MFMA kernel writes lse2 ([batch, heads, ns], rows n .. ns - 1
+  // hold 0) beside out: the statistic a later backward reads
+  float *save_lse2;
   int32_t order[kMaxHeadsArg];  // head processed in slot i, heaviest sigma first
 };
 
@@ -1047,6 +1050,7 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   const int64_t srow = ((int64_t)b * a.heads + h) * ns + r0 + qc;
   if (!active) {
     if (a.stat_lse2 && r0 < ns && gq == 0) a.stat_lse2[srow] = a.stat_dvec[srow] = 0.f;
+    if (a.save_lse2 && r0 < ns && gq == 0) a.save_lse2[srow] = 0.f;
     return;
   }
   float ltot = lsum + xor16_f(lsum);
@@ -1087,6 +1091,7 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     }
     return;
   }
+  if (a.save_lse2 && gq == 0) a.save_lse2[srow] = r0 + qc < n ? m2 + __log2f(ltot) : 0.f;
   const int free_slot = (((nst - 1) >> 1) & 1) ? 0 : 2;
   char *ob = (char *)lds.kv[free_slot][0] + wave * 32 * D;
 #pragma unroll
@@ -2165,6 +2170,38 @@ void attn_dkv_kernel(AttnArgs a, const uint8_t *ws, uint16_t *dk_out, uint16_t *
   }
 }
 
+// ---------------------------------------------------------------------------
+// D_i = dO_i . O_i (fp32 sums of bf16 products) for the backward from a saved
+// forward; rows n .. ns - 1 of each (batch, head) get 0.  Sixteen lanes per
+// row, 16 bytes per lane and pass; rows are [batch * heads][ns].
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void dvec_kernel(const uint16_t *o, const uint16_t *dout, int n, int ns,
+                                                   int64_t rows, float *dvec) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const int64_t slab = row / ns;
+    const int i = (int)(row - slab * ns);
+    if (i < n) {
+      const uint16_t *orow = o + (slab * n + i) * D, *drow = dout + (slab * n + i) * D;
+#pragma unroll
+      for (int c = 8 * l; c < D; c += 128) {
+        const u32x4 ov = *(const u32x4 *)(orow + c), dv = *(const u32x4 *)(drow + c);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          acc = fmaf(__uint_as_float(ov[w] << 16), __uint_as_float(dv[w] << 16), acc);
+          acc = fmaf(__uint_as_float(ov[w] & 0xFFFF0000u), __uint_as_float(dv[w] & 0xFFFF0000u), acc);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && l == 0) dvec[row] = acc;
+}
+
 }  // namespace dev
 
 // ---------------------------------------------------------------------------
@@ -2234,6 +2271,7 @@ void fill_args(dev::AttnArgs &a, const void *q, const void *k, const void *v, vo
   a.dvec = nullptr;
   a.stat_lse2 = nullptr;
   a.stat_dvec = nullptr;
+  a.save_lse2 = nullptr;
   // heavy heads first: per-row work grows with sigma
   int idx[dev::kMaxHeadsArg];
   std::iota(idx, idx + heads, 0);
@@ -2633,28 +2671,33 @@ extern "C" plsh_status plsh_alibi_attention_walk(const void *q, const void *k, c
 }
 
 // Gradients of the estimate for fixed tables (see include/plsh.h).
-extern "C" plsh_status plsh_alibi_attention_backward(const void *q, const void *k, const void *v,
-                                                     const void *dout, void *dq, void *dk, void *dv,
-                                                     int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
-                                                     int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
-                                                     const plsh_tables *boundaries, int32_t causal,
-                                                     plsh_stream_t stream) {
-  static const char *who = "plsh_alibi_attention_backward";
+// The backward of the estimate for fixed tables.  With saved_out and
+// saved_lse2 (the output and row statistics of plsh_alibi_attention_lse) the
+// statistics pass is replaced by D = dO . O from the saved output.
+static plsh_status backward_common(const char *who, const void *q, const void *k, const void *v,
+                                   const void *dout, void *dq, void *dk, void *dv, int32_t batch, int32_t n,
+                                   int32_t heads, int32_t kv_heads, int32_t d, plsh_dtype dtype,
+                                   const double *sigma, int32_t s, const plsh_tables *boundaries,
+                                   int32_t causal, plsh_stream_t stream, bool saved, const void *saved_out,
+                                   const float *saved_lse2) {
   clear_error();
   plsh_status st = check_common(q, k, v, dq, batch, n, heads, kv_heads, d, dtype, sigma, s, boundaries, who);
   if (st != PLSH_OK) return st;
-  if (!dout || !dk || !dv) return fail(PLSH_ERR_ARG, "%s: null pointer argument", who);
-  if (((uintptr_t)dout | (uintptr_t)dk | (uintptr_t)dv) & 15u)
+  if (!dout || !dk || !dv || (saved && (!saved_out || !saved_lse2)))
+    return fail(PLSH_ERR_ARG, "%s: null pointer argument", who);
+  if (((uintptr_t)dout | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)saved_out | (uintptr_t)saved_lse2) & 15u)
     return fail(PLSH_ERR_ARG, "%s: buffers must be 16-byte aligned", who);
+  const int ns = (n + 31) & ~31;
   {
     const size_t qb = (size_t)batch * heads * n * d * 2, kb = (size_t)batch * kv_heads * n * d * 2;
-    const void *ins[4] = {q, k, v, dout};
-    const size_t insz[4] = {qb, kb, kb, qb};
+    const size_t lb = (size_t)batch * heads * ns * sizeof(float);
+    const void *ins[6] = {q, k, v, dout, saved_out, saved_lse2};
+    const size_t insz[6] = {qb, kb, kb, qb, saved ? qb : 0, saved ? lb : 0};
     void *outs[3] = {dq, dk, dv};
     const size_t outsz[3] = {qb, kb, kb};
     for (int o = 0; o < 3; ++o) {
-      for (int i = 0; i < 4; ++i)
-        if (overlaps(outs[o], outsz[o], ins[i], insz[i]))
+      for (int i = 0; i < 6; ++i)
+        if (insz[i] && overlaps(outs[o], outsz[o], ins[i], insz[i]))
           return fail(PLSH_ERR_ARG, "%s: dq, dk or dv overlaps an input", who);
       for (int o2 = o + 1; o2 < 3; ++o2)
         if (overlaps(outs[o], outsz[o], outs[o2], outsz[o2]))
@@ -2665,27 +2708,38 @@ extern "C" plsh_status plsh_alibi_attention_backward(const void *q, const void *
     return fail(PLSH_ERR_UNSUPPORTED, "%s: bf16 with s <= %d only", who, dev::kMaxMfmaSamples);
   if ((st = have_device(who)) != PLSH_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
-  const int ns = (n + 31) & ~31;
   const int64_t prows = (int64_t)batch * heads * ns;
-  const size_t bytes = 2 * (size_t)prows * sizeof(float);
+  const size_t bytes = (saved ? 1 : 2) * (size_t)prows * sizeof(float);
   void *stats = nullptr;
   hipError_t e = hipMallocAsync(&stats, bytes, hs);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(PLSH_ERR_HIP, "%s: statistics allocation of %zu bytes failed: %s", who, bytes, hipGetErrorString(e));
   }
-  float *lse2 = (float *)stats;
-  float *dvec = lse2 + prows;
+  const float *lse2 = saved ? saved_lse2 : (const float *)stats;
+  float *dvec = saved ? (float *)stats : (float *)stats + prows;
   dev::AttnArgs a;
   fill_args(a, q, k, v, dq, batch, n, heads, kv_heads, sigma, s, boundaries);
   a.dout = dout;
+  plsh_status rc = PLSH_OK;
+  if (saved) {
+    // D = dO . O from the saved output
+    const dim3 grid((unsigned)((prows + 15) / 16)), block(256);
+    if (d == 64)
+      hipLaunchKernelGGL(dev::dvec_kernel<64>, grid, block, 0, hs, (const uint16_t *)saved_out,
+                         (const uint16_t *)dout, n, ns, prows, dvec);
+    else
+      hipLaunchKernelGGL(dev::dvec_kernel<128>, grid, block, 0, hs, (const uint16_t *)saved_out,
+                         (const uint16_t *)dout, n, ns, prows, dvec);
+    rc = launch_check(who);
+  }
   // the records of the estimator serve its statistics pass and dQ; dK/dV
   // takes non-causal ones (the same records when the call is not causal)
   void *rec = nullptr, *rec_nc = nullptr;
-  plsh_status rc = build_records(a, causal != 0, hs, who, &rec);
-  if (rc == PLSH_OK) {
+  if (rc == PLSH_OK) rc = build_records(a, causal != 0, hs, who, &rec);
+  if (rc == PLSH_OK && !saved) {
     // statistics: each row's normaliser and D = dO . O
-    a.stat_lse2 = lse2;
+    a.stat_lse2 = (float *)stats;
     a.stat_dvec = dvec;
     rc = launch_attn(a, d, causal != 0, hs, who, 0, rec);
   }
@@ -2717,6 +2771,66 @@ extern "C" plsh_status plsh_alibi_attention_backward(const void *q, const void *
     return fail(PLSH_ERR_HIP, "%s: statistics release failed: %s", who, hipGetErrorString(e));
   }
   return rc;
+}
+
+extern "C" plsh_status plsh_alibi_attention_backward(const void *q, const void *k, const void *v,
+                                                     const void *dout, void *dq, void *dk, void *dv,
+                                                     int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                                     int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                                     const plsh_tables *boundaries, int32_t causal,
+                                                     plsh_stream_t stream) {
+  return backward_common("plsh_alibi_attention_backward", q, k, v, dout, dq, dk, dv, batch, n, heads, kv_heads,
+                         d, dtype, sigma, s, boundaries, causal, stream, false, nullptr, nullptr);
+}
+
+extern "C" plsh_status plsh_alibi_attention_backward_saved(const void *q, const void *k, const void *v,
+                                                           const void *out, const float *lse2,
+                                                           const void *dout, void *dq, void *dk, void *dv,
+                                                           int32_t batch, int32_t n, int32_t heads,
+                                                           int32_t kv_heads, int32_t d, plsh_dtype dtype,
+                                                           const double *sigma, int32_t s,
+                                                           const plsh_tables *boundaries, int32_t causal,
+                                                           plsh_stream_t stream) {
+  return backward_common("plsh_alibi_attention_backward_saved", q, k, v, dout, dq, dk, dv, batch, n, heads,
+                         kv_heads, d, dtype, sigma, s, boundaries, causal, stream, true, out, lse2);
+}
+
+// The estimator, writing each row's log2 normaliser beside the output.
+extern "C" plsh_status plsh_alibi_attention_lse(const void *q, const void *k, const void *v, void *out,
+                                                int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                                int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                                const plsh_tables *boundaries, int32_t causal, float *lse2,
+                                                void *workspace, int64_t workspace_bytes,
+                                                plsh_stream_t stream) {
+  static const char *who = "plsh_alibi_attention_lse";
+  clear_error();
+  plsh_status st = check_common(q, k, v, out, batch, n, heads, kv_heads, d, dtype, sigma, s, boundaries, who);
+  if (st != PLSH_OK) return st;
+  if (!lse2) return fail(PLSH_ERR_ARG, "%s: null pointer argument", who);
+  if ((uintptr_t)lse2 & 15u) return fail(PLSH_ERR_ARG, "%s: lse2 must be 16-byte aligned", who);
+  const size_t ns = (size_t)((n + 31) & ~31);
+  const size_t lb = (size_t)batch * heads * ns * sizeof(float), esz = dtype == PLSH_F32 ? 4 : 2;
+  const size_t qb = (size_t)batch * heads * n * d * esz, kb = (size_t)batch * kv_heads * n * d * esz;
+  if (overlaps(lse2, lb, q, qb) || overlaps(lse2, lb, k, kb) || overlaps(lse2, lb, v, kb) ||
+      overlaps(lse2, lb, out, qb))
+    return fail(PLSH_ERR_ARG, "%s: lse2 overlaps q, k, v or out", who);
+  if (dtype != PLSH_BF16 || s > dev::kMaxMfmaSamples)
+    return fail(PLSH_ERR_UNSUPPORTED, "%s: bf16 with s <= %d only", who, dev::kMaxMfmaSamples);
+  if (workspace) {
+    const size_t need = records_bytes(n, heads, s);
+    if (workspace_bytes < 0 || (size_t)workspace_bytes < need)
+      return fail(PLSH_ERR_CAPACITY, "%s: workspace of %lld bytes, the call needs %zu", who,
+                  (long long)workspace_bytes, need);
+    if ((uintptr_t)workspace & 15u) return fail(PLSH_ERR_ARG, "%s: workspace must be 16-byte aligned", who);
+    if (overlaps(workspace, need, q, qb) || overlaps(workspace, need, k, kb) || overlaps(workspace, need, v, kb) ||
+        overlaps(workspace, need, out, qb) || overlaps(workspace, need, lse2, lb))
+      return fail(PLSH_ERR_ARG, "%s: workspace overlaps q, k, v, out or lse2", who);
+  }
+  if ((st = have_device(who)) != PLSH_OK) return st;
+  dev::AttnArgs a;
+  fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
+  a.save_lse2 = lse2;
+  return launch_mfma(a, d, causal != 0, (hipStream_t)stream, who, workspace);
 }
 
 extern "C" plsh_status plsh_kernel_timer(int32_t enable) {

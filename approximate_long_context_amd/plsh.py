@@ -27,7 +27,8 @@ EXPORTED = ["plsh_sample_tables", "plsh_build_tables", "plsh_validate_tables", "
             "plsh_alibi_attention", "plsh_alibi_attention_ws", "plsh_attention_workspace_size",
             "plsh_debug_block_intervals",
             "plsh_debug_attention_reference", "plsh_alibi_attention_unfused", "plsh_alibi_attention_walk",
-            "plsh_alibi_attention_backward", "plsh_exact_alibi_attention",
+            "plsh_alibi_attention_backward", "plsh_alibi_attention_backward_saved",
+            "plsh_alibi_attention_lse", "plsh_exact_alibi_attention",
             "plsh_sample_params_device", "plsh_kernel_timer", "plsh_kernel_timer_read", "plsh_last_error"]
 
 
@@ -69,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.plsh_attention_workspace_size.argtypes = [i32, i32, i32, ctypes.c_int, ctypes.POINTER(i64)]
         L.plsh_alibi_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                     ctypes.c_int, vp, i32, TP, i32, vp]
+        L.plsh_alibi_attention_backward_saved.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                                          i32, i32, ctypes.c_int, vp, i32, TP, i32, vp]
+        L.plsh_alibi_attention_lse.argtypes = attn[:-1] + [vp, vp, i64, vp]
         L.plsh_debug_block_intervals.argtypes = [TP, vp, vp]
         L.plsh_exact_alibi_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                                                  vp, i32, vp]
@@ -287,11 +291,41 @@ def attention_walk(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False
     return _attention(lib().plsh_alibi_attention_walk, q, k, v, sigma, s, tables, causal, out, stream)
 
 
+def attention_with_lse(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
+                       out: Optional[torch.Tensor] = None, stream: Optional[int] = None,
+                       lse2: Optional[torch.Tensor] = None):
+    """plsh_alibi_attention_lse: (out, lse2), lse2 float32 [B, H, ceil32(n)]
+    = log2 of each row's normaliser (rows past n hold 0), for
+    attention_backward(..., out=out, lse2=lse2)."""
+    B, H, n, d = q.shape
+    shape = (B, H, (n + 31) // 32 * 32)
+    if lse2 is None:
+        lse2 = torch.empty(shape, dtype=torch.float32, device=q.device)
+    elif lse2.dtype != torch.float32 or tuple(lse2.shape) != shape or not lse2.is_contiguous():
+        raise PlshError(PLSH_ERR_ARG, "lse2 must be a contiguous float32 [B, H, ceil32(n)] tensor")
+    if stream is None:
+        need = workspace_size(n, H, s, q.dtype)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        ws_args = (ws.data_ptr(), ws.numel())
+    else:   # an explicit stream: the library's stream-ordered workspace
+        ws_args = (None, 0)
+
+    def fn(*args):
+        return lib().plsh_alibi_attention_lse(*args[:-1], lse2.data_ptr(), *ws_args, args[-1])
+    out = _attention(fn, q, k, v, sigma, s, tables, causal, out, stream)
+    return out, lse2
+
+
 def attention_backward(q, k, v, dout, sigma, s, tables: DeviceTables, causal: bool = False,
-                       stream: Optional[int] = None):
-    """plsh_alibi_attention_backward: (dq, dk, dv) for the upstream gradient
-    dout of plsh_alibi_attention's output (fixed tables)."""
-    for name, x in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+                       stream: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                       lse2: Optional[torch.Tensor] = None):
+    """(dq, dk, dv) for the upstream gradient dout of the estimate (fixed
+    tables): plsh_alibi_attention_backward, or, given the forward's out and
+    lse2 (attention_with_lse), plsh_alibi_attention_backward_saved."""
+    if (out is None) != (lse2 is None):
+        raise PlshError(PLSH_ERR_ARG, "out and lse2 go together")
+    for name, x in (("q", q), ("k", k), ("v", v), ("dout", dout)) + \
+            ((("out", out), ("lse2", lse2)) if out is not None else ()):
         if not x.is_contiguous():
             raise PlshError(PLSH_ERR_ARG, f"{name} must be contiguous")
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or dout.shape != q.shape or \
@@ -305,10 +339,20 @@ def attention_backward(q, k, v, dout, sigma, s, tables: DeviceTables, causal: bo
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = tables.c_struct()
-    _check(lib().plsh_alibi_attention_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                                               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, n, H,
-                                               k.shape[1], d, _dtype_code(q), _ptr(sig), s,
-                                               ctypes.byref(st), int(bool(causal)), stream))
+    if out is None:
+        _check(lib().plsh_alibi_attention_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, n, H,
+                                                   k.shape[1], d, _dtype_code(q), _ptr(sig), s,
+                                                   ctypes.byref(st), int(bool(causal)), stream))
+        return dq, dk, dv
+    if out.shape != q.shape or out.dtype != q.dtype or lse2.dtype != torch.float32 or \
+            tuple(lse2.shape) != (B, H, (n + 31) // 32 * 32):
+        raise PlshError(PLSH_ERR_ARG, "out [B,H,n,d] of q's dtype and lse2 float32 [B,H,ceil32(n)] expected")
+    _check(lib().plsh_alibi_attention_backward_saved(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                     lse2.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                                     dk.data_ptr(), dv.data_ptr(), B, n, H, k.shape[1], d,
+                                                     _dtype_code(q), _ptr(sig), s, ctypes.byref(st),
+                                                     int(bool(causal)), stream))
     return dq, dk, dv
 
 

@@ -27,7 +27,8 @@ The default run also times, outside the timed steps and on the same inputs,
 the exact-ALiBi kernel ("exact_alibi_comparator"), fixed blocks through the
 estimator ("fixed_blocks_baseline"), the unfused per-sample form
 ("unfused_ablation"), the per-sample walk inside one kernel
-("walk_ablation") and the backward for fixed tables ("backward");
+("walk_ablation") and the backward for fixed tables ("backward", with the
+variant that starts from a saved forward's output and row statistics);
 --no-comparators skips them (profiling runs).
 """
 
@@ -363,7 +364,27 @@ def main():
                    "dq_sampled_rows_rel_err": bw_err}
         log(f"[bench] backward: {bw_ms:.3f} ms ({bw_ms / ms:.1f}x the forward call, {bw_tflops:.0f} useful "
             f"TFLOP/s); dq sampled rows rel. err {bw_err:.2e}")
-        del dod, res
+        # the same backward from a saved forward (output and row statistics of
+        # plsh_alibi_attention_lse): D = dO.O replaces the statistics pass
+        o_s = torch.empty_like(qd)
+        l_s = torch.empty((B, H, (n + 31) // 32 * 32), dtype=torch.float32, device=dev)
+        fl_ms, fl_kernel_ms = time_calls(lambda: plsh.attention_with_lse(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal,
+                                                              out=o_s, lse2=l_s), 50)
+
+        def bwd_saved():
+            res["g"] = plsh.attention_backward(qd, kd, vd, dod, w.sigma, w.s, dt, causal=w.causal,
+                                               out=o_s, lse2=l_s)
+
+        bs_ms, _ = time_calls(bwd_saved, 10, 2)
+        gq = W.to_f64(res["g"][0][:, :, rows])
+        bs_err = float(np.abs(gq - rq).max() / np.abs(rq).max())
+        bwd_rec["saved_forward"] = {"forward_with_lse_ms": fl_ms, "forward_with_lse_kernel_ms": fl_kernel_ms,
+                                    "backward_ms": bs_ms,
+                                    "backward_over_recomputing": bs_ms / bw_ms,
+                                    "dq_sampled_rows_rel_err": bs_err}
+        log(f"[bench] saved forward: forward+lse {fl_ms:.3f} ms, backward {bs_ms:.3f} ms "
+            f"({bs_ms / bw_ms:.2f}x the recomputing backward); dq sampled rows rel. err {bs_err:.2e}")
+        del dod, res, o_s, l_s
 
     cpu = None
     if not args.no_cpu_baseline:

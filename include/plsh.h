@@ -308,6 +308,58 @@ plsh_status plsh_alibi_attention_backward(const void *q, const void *k, const vo
                                           plsh_stream_t stream);
 
 /*
+ * plsh_alibi_attention_lse -- plsh_alibi_attention (the same kernels, bitwise
+ * the same out) that also writes each row's normaliser, the statistic a
+ * later backward needs (Methodology §3, Theorem 2.2: the diagonal of
+ * s D~, D~ = diag((A o M~ o C) 1)):
+ *   lse2[b][h][i] = log2 sum_j c_ij e^{q_i.k_j}   (base 2; fp32)
+ *   lse2        DEVICE float [batch][heads][ceil32(n)] output, 16-byte
+ *               aligned; rows n .. ceil32(n)-1 of each (batch, head) get 0
+ *   workspace, workspace_bytes
+ *               the pre-pass workspace as for plsh_alibi_attention_ws, or
+ *               NULL: then the call takes it from the stream-ordered
+ *               allocator as plsh_alibi_attention does
+ *   the other arguments as for plsh_alibi_attention; bf16, s <= 124.
+ * Errors: as plsh_alibi_attention, plus PLSH_ERR_ARG (null, misaligned or
+ * overlapping lse2; misaligned or overlapping workspace), PLSH_ERR_CAPACITY
+ * (workspace too small) and PLSH_ERR_UNSUPPORTED (fp32 or s > 124).
+ */
+plsh_status plsh_alibi_attention_lse(const void *q, const void *k, const void *v, void *out,
+                                     int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                     int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                     const plsh_tables *boundaries, int32_t causal, float *lse2,
+                                     void *workspace, int64_t workspace_bytes, plsh_stream_t stream);
+
+/*
+ * plsh_alibi_attention_backward_saved -- plsh_alibi_attention_backward from a
+ * saved forward: `out` and `lse2` as written by plsh_alibi_attention_lse for
+ * the same q, k, v, tables and causal flag (Experimental Validation: training
+ * with the method).  The statistics pass is replaced by one streaming kernel
+ * for D_i = dO_i . out_i (fp32 sums of the bf16 products); every other
+ * launch is plsh_alibi_attention_backward's.  Because D is taken from the
+ * bf16 output rather than the fp32 estimate, the gradients differ from
+ * plsh_alibi_attention_backward's by the output's rounding (relative 2^-9
+ * per element of D).
+ *   out    DEVICE [batch, heads, n, d] bf16, 16-byte aligned
+ *   lse2   DEVICE float [batch][heads][ceil32(n)], 16-byte aligned
+ *   the other arguments as for plsh_alibi_attention_backward.
+ * Device memory: 4 * batch*heads*ceil32(n) bytes for D from the
+ * stream-ordered allocator on `stream`, released within the call, plus the
+ * pre-pass workspaces.  dq, dk, dv must not overlap any input (out and lse2
+ * included).
+ * Errors: as plsh_alibi_attention_backward, plus PLSH_ERR_ARG for a null or
+ * misaligned out or lse2.
+ */
+plsh_status plsh_alibi_attention_backward_saved(const void *q, const void *k, const void *v,
+                                                const void *out, const float *lse2,
+                                                const void *dout, void *dq, void *dk, void *dv,
+                                                int32_t batch, int32_t n, int32_t heads,
+                                                int32_t kv_heads, int32_t d, plsh_dtype dtype,
+                                                const double *sigma, int32_t s,
+                                                const plsh_tables *boundaries, int32_t causal,
+                                                plsh_stream_t stream);
+
+/*
  * plsh_alibi_attention_unfused -- the same estimate computed the way the
  * pages state the reduction (Methodology §3, Theorem 2.2: s short-context
  * attentions without positional bias): for each sample k a pass over every

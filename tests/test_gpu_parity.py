@@ -641,3 +641,102 @@ def test_backward_full_size_sampled(dev):
         rk, rv = orc.lsh_grad_keys(qf[:, hs], kf[:, g:g + 1], vf[:, g:g + 1], dof[:, hs], tabs[hs], w.causal, keys)
         check_grad(gk[:, g:g + 1][:, :, keys], rk, f"dk mistral kv head {g}")
         check_grad(gv[:, g:g + 1][:, :, keys], rv, f"dv mistral kv head {g}")
+
+
+# ------------------------------------------- saved forward statistics ---
+LSE2_TOL = 6e-3  # log2(1 + 2^-8) for the bf16 weights, plus fp32 slack
+def run_saved(dev, w, causal):
+    """Forward with its row statistics (plsh_alibi_attention_lse), then the
+    backward from them (plsh_alibi_attention_backward_saved)."""
+    q, k, v, do, t, tabs = grad_inputs(w)
+    say(w.name, "saved backward", "n", w.n, "d", w.d, "heads", w.heads, w.kv_heads, "s", w.s, "causal", causal)
+    qd, kd, vd, dt = q.to(dev), k.to(dev), v.to(dev), t.to(dev)
+    out, lse2 = plsh.attention_with_lse(qd, kd, vd, w.sigma, w.s, dt, causal=causal)
+    dq, dk, dv = plsh.attention_backward(qd, kd, vd, do.to(dev), w.sigma, w.s, dt, causal=causal,
+                                         out=out, lse2=lse2)
+    plain = plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=causal)
+    torch.cuda.synchronize()
+    return (q, k, v, do, tabs), (out, lse2, plain), (W.to_f64(dq), W.to_f64(dk), W.to_f64(dv))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_saved_forward_and_backward_match_oracle(dev, d, causal):
+    """plsh_alibi_attention_lse writes the estimator's output bit for bit and
+    each row's log2 normaliser (Methodology §3: the diagonal of s D~) within
+    the bf16 rounding of the weights it sums: bf16 has 8 significant bits, so
+    each weight errs by at most 2^-8 relative, the sum too, and log2 of the
+    sum by log2(1 + 2^-8) = 5.6e-3, plus fp32 sums and exp2/log2 far below
+    that: 6e-3.  Rows past n hold 0.  The backward from them matches the
+    oracle's gradients to the backward's own tolerance (GQA, n = 700, several
+    tiles, ragged tail)."""
+    w = small("saved", 2, 4, 2, 700, d, "bf16", causal, [1.3, 9.0, 60.0, 700.0], 7)
+    (q, k, v, do, tabs), (out, lse2, plain), (gq, gk, gv) = run_saved(dev, w, causal)
+    assert torch.equal(out, plain)
+    qf, kf, vf = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    ref = orc.lsh_row_log_normaliser(qf, kf, tabs, causal) / math.log(2.0)
+    got = lse2.cpu().double().numpy()
+    err = float(np.abs(got[:, :, :w.n] - ref).max())
+    say("lse2", f"max|lse2 - oracle| = {err:.3e}")
+    assert err <= LSE2_TOL, err
+    assert not got[:, :, w.n:].any()
+    rq, rk, rv = orc.lsh_estimate_grad(qf, kf, vf, W.to_f64(do), tabs, causal)
+    check_grad(gq, rq, f"saved dq d={d} causal={causal}")
+    check_grad(gk, rk, f"saved dk d={d} causal={causal}")
+    check_grad(gv, rv, f"saved dv d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("n,causal", [(1, True), (33, False), (333, True)])
+def test_saved_backward_ragged(dev, n, causal):
+    """Odd lengths, three query heads per KV head, n = 1; the saved path also
+    agrees with the recomputing backward to the same tolerance (D from the
+    bf16 output instead of the fp32 estimate)."""
+    w = small("saved-ragged", 1, 6, 2, n, 64, "bf16", causal, [0.7, 3.0, 17.0, 90.0, 400.0, 5000.0], 5)
+    (q, k, v, do, tabs), (out, lse2, plain), (gq, gk, gv) = run_saved(dev, w, causal)
+    assert torch.equal(out, plain)
+    rq, rk, rv = orc.lsh_estimate_grad(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do), tabs, causal)
+    fl = cancel_floor(q, k, v, do)
+    check_grad(gq, rq, f"saved dq n={n}", floor=fl)
+    check_grad(gk, rk, f"saved dk n={n}", floor=fl)
+    check_grad(gv, rv, f"saved dv n={n}")
+    _, (hq, hk, hv) = run_backward(dev, w, causal)
+    check_grad(gq, hq, f"saved vs recomputed dq n={n}", floor=fl)
+    check_grad(gv, hv, f"saved vs recomputed dv n={n}")
+
+
+def test_saved_backward_full_size_sampled(dev):
+    """The 32-head, n = 16384, s = 20 causal workload from a saved forward:
+    lse2 at sampled rows of every head, dq at the same rows and dk, dv at
+    sampled keys of the heaviest KV head against the oracle."""
+    w = W.get("mistral-7b-n16384-s20")
+    (q, k, v, do, tabs), (out, lse2, plain), (gq, gk, gv) = run_saved(dev, w, w.causal)
+    assert torch.equal(out, plain)
+    qf, kf, vf, dof = W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do)
+    rows = W.sample_rows(w.n, 16, seed=41)
+    ref = orc.lsh_row_log_normaliser(qf, kf, tabs, w.causal, rows=rows) / math.log(2.0)
+    err = float(np.abs(lse2.cpu().double().numpy()[:, :, rows] - ref).max())
+    say("lse2 mistral", f"max|lse2 - oracle| = {err:.3e}")
+    assert err <= LSE2_TOL, err
+    rq = orc.lsh_grad_rows(qf, kf, vf, dof, tabs, w.causal, rows)
+    check_grad(gq[:, :, rows], rq, "saved dq mistral sampled rows")
+    keys = W.sample_rows(w.n, 6, seed=43)
+    grp = w.heads // w.kv_heads
+    g = w.kv_heads - 1
+    hs = slice(g * grp, (g + 1) * grp)
+    rk, rv = orc.lsh_grad_keys(qf[:, hs], kf[:, g:g + 1], vf[:, g:g + 1], dof[:, hs], tabs[hs], w.causal, keys)
+    check_grad(gk[:, g:g + 1][:, :, keys], rk, "saved dk mistral heaviest kv head")
+    check_grad(gv[:, g:g + 1][:, :, keys], rv, "saved dv mistral heaviest kv head")
+
+
+def test_lse_forward_workspace_paths_bitwise(dev):
+    """plsh_alibi_attention_lse with a caller workspace (the binding's default)
+    and with the library's stream-ordered one give the same bits."""
+    w = small("lse-ws", 1, 4, 2, 500, 128, "bf16", True, [1.5, 8.0, 40.0, 300.0], 6)
+    q, k, v = W.make_qkv(w)
+    t = plsh.sample_tables(1, w.n, w.sigma, w.s).to(dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o1, l1 = plsh.attention_with_lse(qd, kd, vd, w.sigma, w.s, t, causal=True)
+    o2, l2 = plsh.attention_with_lse(qd, kd, vd, w.sigma, w.s, t, causal=True,
+                                     stream=torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

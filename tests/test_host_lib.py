@@ -247,6 +247,46 @@ def test_attention_ws_argument_errors():
         assert st == plsh.PLSH_ERR_HIP, msg
 
 
+def test_lse_and_saved_backward_argument_errors():
+    """plsh_alibi_attention_lse and plsh_alibi_attention_backward_saved check
+    their extra operands before any device work: null or misaligned lse2 /
+    out, fp32 (the MFMA path only); without a device the checks pass and the
+    call reports PLSH_ERR_HIP."""
+    import torch
+    L, a, keep = _attn_args()
+    big = 0x4000000
+
+    def lse(lse2, ws=None, ws_bytes=0, **over):
+        b = dict(a, **over)
+        return L.plsh_alibi_attention_lse(b["q"], b["k"], b["v"], b["out"], b["batch"], b["n"], b["heads"],
+                                          b["kv_heads"], b["d"], b["dtype"], b["sigma"], b["s"], b["tables"],
+                                          b["causal"], lse2, ws, ws_bytes, b["stream"])
+
+    def saved(out, lse2, **over):
+        b = dict(a, **over)
+        return L.plsh_alibi_attention_backward_saved(b["q"], b["k"], b["v"], out, lse2, 0x50000, 0x60000,
+                                                     0x70000, 0x80000, b["batch"], b["n"], b["heads"],
+                                                     b["kv_heads"], b["d"], b["dtype"], b["sigma"], b["s"],
+                                                     b["tables"], b["causal"], b["stream"])
+    assert lse(None) == plsh.PLSH_ERR_ARG
+    assert lse(big + 4) == plsh.PLSH_ERR_ARG
+    assert lse(a["q"]) == plsh.PLSH_ERR_ARG             # overlaps q
+    assert lse(big, dtype=plsh.PLSH_F32) == plsh.PLSH_ERR_UNSUPPORTED
+    need = plsh.workspace_size(64, 4, 3, torch.bfloat16)
+    assert lse(big, big + 0x100000, need - 1) == plsh.PLSH_ERR_CAPACITY
+    assert lse(big, big + 0x100008, need) == plsh.PLSH_ERR_ARG     # misaligned
+    assert lse(big, a["v"], need) == plsh.PLSH_ERR_ARG            # overlaps v
+    assert saved(None, big) == plsh.PLSH_ERR_ARG
+    assert saved(big, None) == plsh.PLSH_ERR_ARG
+    assert saved(big + 8, big + 0x100000) == plsh.PLSH_ERR_ARG
+    assert saved(0x60000, big) == plsh.PLSH_ERR_ARG     # dq overlaps out
+    assert saved(big, big + 0x100000, dtype=plsh.PLSH_F32) == plsh.PLSH_ERR_UNSUPPORTED
+    if not torch.cuda.is_available():
+        assert lse(big) == plsh.PLSH_ERR_HIP
+        assert lse(big, big + 0x100000, need) == plsh.PLSH_ERR_HIP
+        assert saved(big, big + 0x100000) == plsh.PLSH_ERR_HIP
+
+
 def test_kernel_timer_without_launches():
     plsh.kernel_timer(True)
     assert plsh.kernel_timer_read() == (0, 0.0)
