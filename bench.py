@@ -17,6 +17,11 @@ runs a plain device-to-device copy of MIB MiB a few times instead (the known
 byte count against which the HBM byte counters are scaled) and prints one
 JSON line describing it.
 
+    python bench.py --sweep
+
+times every workload (tiny fp32 through n = 524288) and prints one JSON line
+per workload, with the estimate's error against exact ALiBi.
+
     python bench.py --crossover
 
 times the estimator (one library call) against the dense exact-ALiBi kernel
@@ -128,6 +133,64 @@ def crossover() -> None:
         torch.cuda.empty_cache()
 
 
+SWEEP = ["tiny-f32-n512", "slopes-n4096", "qwen3-0.6b-n8192-s10", "qwen3-0.6b-n8192-s20",
+         "mistral-7b-n16384-s10", "mistral-7b-n16384-s20", "mistral-7b-n16384-s40",
+         "long-n65536", "long-n131072", "long-n524288"]
+
+
+def sweep(settle_s: float) -> None:
+    """Every workload: the call's time and throughput, the attention kernel's
+    time and HBM roofline fraction, and (informational) the estimate's error
+    against exact ALiBi and its parity with the oracle's estimate, on the full
+    output for n <= 4096 and on sampled rows (32 per head, shared by the
+    heads) beyond.  One JSON line per workload."""
+    import oracle as orc
+    dev = torch.device("cuda:0")
+    for name in SWEEP:
+        w = W.get(name)
+        q, k, v = W.make_qkv(w)
+        tables = plsh.sample_tables(w.hash_seed, w.n, w.sigma, w.s)
+        pairs_alg, pairs_distinct = plsh.count_work(tables, w.causal)
+        dt = tables.to(dev)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        out = torch.empty_like(qd)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(10):
+                plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out)
+            torch.cuda.synchronize()
+        reps = 50 if w.n <= 16384 else 10
+        ms, kernel_ms = time_calls(lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal,
+                                                          out=out), reps)
+        B, H, Hkv, n, d, s = w.batch, w.heads, w.kv_heads, w.n, w.d, w.s
+        bytes_min = w.esz * B * n * d * (2 * H + 2 * Hkv)
+        full = n <= 4096
+        rows = np.arange(n) if full else W.sample_rows(n, 32, seed=5)
+        o = W.to_f64(out[:, :, rows])
+        del qd, kd, vd, out
+        torch.cuda.empty_cache()
+        qf, kf, vf = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+        off, st = orc.tables_from_params(n, tables.params)
+        tabs = orc.starts_per_head(off, st, H, s)
+        exact = orc.exact_alibi(qf, kf, vf, w.sigma, w.causal, rows=None if full else rows)
+        est = orc.lsh_estimate(qf, kf, vf, tabs, w.causal, rows=None if full else rows)
+        rec = {"sweep": True, "workload": name, "batch": B, "heads": H, "kv_heads": Hkv, "n": n, "d": d,
+               "s": s, "causal": w.causal, "dtype": w.dtype, "ms_per_call": ms, "kernel": kernel_name(w),
+               "kernel_ms": kernel_ms, "rows_samples_per_s": B * H * n * s / (ms / 1e3),
+               "useful_tflops": 4.0 * d * B * pairs_distinct / (ms / 1e3) / 1e12,
+               "s_walk_equivalent_tflops": 4.0 * d * B * pairs_alg / (ms / 1e3) / 1e12,
+               "hbm_frac_kernel": bytes_min / (kernel_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+               "error_rows": "all" if full else f"{len(rows)} sampled per head",
+               "parity_max_abs": float(np.abs(o - est).max()),
+               "error_vs_exact_alibi": {"max_abs": float(np.abs(o - exact).max()),
+                                        "rel_fro": float(np.linalg.norm(o - exact) / np.linalg.norm(exact))}}
+        log(f"[sweep] {name}: {ms:.4f} ms/call, kernel {kernel_ms:.4f} ms, "
+            f"{rec['rows_samples_per_s']:.3g} rows*samples/s, HBM frac {rec['hbm_frac_kernel']:.2f}, "
+            f"parity {rec['parity_max_abs']:.2e}, rel. error vs exact {rec['error_vs_exact_alibi']['rel_fro']:.3f}")
+        print(json.dumps(rec), flush=True)
+        del q, k, v, qf, kf, vf, exact, est, o
+
+
 def kernel_sha() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
@@ -194,6 +257,8 @@ def main():
     ap.add_argument("--error-rows", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--crossover", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="every workload: time, throughput, roofline fraction, error (one line each)")
     ap.add_argument("--no-comparators", action="store_true",
                     help="skip the exact-ALiBi, fixed-blocks and unfused comparisons (profiling runs)")
     args = ap.parse_args()
@@ -208,6 +273,9 @@ def main():
         return
     if args.crossover:
         crossover()
+        return
+    if args.sweep:
+        sweep(min(args.settle_s, 0.5))
         return
     dev = torch.device("cuda:0")
     w = W.get(args.workload)
