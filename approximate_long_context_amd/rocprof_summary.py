@@ -16,6 +16,16 @@ turns two counter runs of the benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per
 dispatch) into HBM bytes per launch of the named kernel.  Each counter is
 scaled by what it reads for a plain copy of known size (`bench.py
 --copy-calibration`), which reads and writes exactly N bytes.
+
+    python -m approximate_long_context_amd.rocprof_summary mfma \
+        --run DIR --kernel attn_mfma_kernel --workload NAME --kernel-sha SHA \
+        --issued-pairs P --flops-per-pair F --command "..." \
+        --out-md profiles/NAME.md --out-json profiles/mfma.json
+
+turns a counter run with SQ_INSTS_VALU_MFMA_MOPS_BF16 and
+SQ_VALU_MFMA_BUSY_CYCLES into the bf16 matrix-core work per launch.  The
+counter counts units of 512 flops; the run is checked against the pairs the
+kernel issues by construction (P pairs of F flops each, from the tables).
 """
 
 from __future__ import annotations
@@ -88,7 +98,44 @@ def main(argv=None) -> None:
     t.add_argument("--commands", required=True, help="text file with the commands of the four runs")
     t.add_argument("--out-md", required=True)
     t.add_argument("--out-json", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--run", required=True)
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--kernel-sha", required=True)
+    m.add_argument("--issued-pairs", type=float, required=True)
+    m.add_argument("--flops-per-pair", type=float, required=True)
+    m.add_argument("--command", required=True)
+    m.add_argument("--out-md", required=True)
+    m.add_argument("--out-json", required=True)
     args = ap.parse_args(argv)
+
+    if args.cmd == "mfma":
+        mops, nd = counter_per_dispatch(args.run, "SQ_INSTS_VALU_MFMA_MOPS_BF16", args.kernel)
+        busy, _ = counter_per_dispatch(args.run, "SQ_VALU_MFMA_BUSY_CYCLES", args.kernel)
+        flops = mops * 512.0
+        want = args.issued_pairs * args.flops_per_pair
+        rec = {"kernel": args.kernel, "kernel_sha": args.kernel_sha, "dispatches": nd,
+               "mops_bf16_per_dispatch": mops, "flops_per_mop": 512,
+               "bf16_flops_per_launch": flops, "issued_pair_flops_per_launch": want,
+               "mfma_busy_cycles_per_dispatch": busy}
+        try:
+            allrec = json.load(open(args.out_json))
+        except (OSError, ValueError):
+            allrec = {}
+        allrec[args.workload] = rec
+        json.dump(allrec, open(args.out_json, "w"), indent=1, sort_keys=True)
+        md = (f"# bf16 matrix-core work of `{args.kernel}` on {args.workload}\n\n"
+              f"Command:\n\n```\n{args.command}\n```\n\n"
+              f"| quantity | value |\n|---|---|\n"
+              f"| SQ_INSTS_VALU_MFMA_MOPS_BF16 per dispatch | {mops:.0f} ({nd} dispatches) |\n"
+              f"| bf16 MFMA flops per launch (512 per MOP) | {flops / 1e9:.3f} GFLOP |\n"
+              f"| pairs issued by construction x {args.flops_per_pair:.0f} flops | {want / 1e9:.3f} GFLOP |\n"
+              f"| SQ_VALU_MFMA_BUSY_CYCLES per dispatch | {busy:.0f} |\n"
+              f"| kernel source sha256[:16] | `{args.kernel_sha}` |\n")
+        open(args.out_md, "w").write(md)
+        print(md)
+        return
 
     if args.cmd == "stats":
         path = _one(args.csv)

@@ -57,6 +57,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 KERNEL_SRC = os.path.join(HERE, "approximate_long_context_amd", "csrc", "plsh_attention.hip")
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
+MFMA_FILE = os.path.join(HERE, "profiles", "mfma.json")
 
 
 def log(*a):
@@ -189,6 +190,41 @@ def sweep(settle_s: float) -> None:
             f"parity {rec['parity_max_abs']:.2e}, rel. error vs exact {rec['error_vs_exact_alibi']['rel_fro']:.3f}")
         print(json.dumps(rec), flush=True)
         del q, k, v, qf, kf, vf, exact, est, o
+
+
+def issued_pairs(t: plsh.Tables, causal: bool) -> int:
+    """(row, key) pairs the MFMA kernel evaluates per batch element: each 16-row
+    wave computes the 32-key tiles of its 32-row group's key range, from the
+    smallest block start of the group's rows (rounded down to 32) to the
+    group's end (causal) or its largest block end (rounded up to 32)."""
+    n, total = t.n, 0
+    x = np.arange(n)
+    for h in range(t.heads):
+        lo = np.full(n, n)
+        hi = np.zeros(n, dtype=np.int64)
+        for k in range(t.s):
+            st = t.starts_of(h, k).astype(np.int64)
+            idx = np.searchsorted(st, x, side="right") - 1
+            lo = np.minimum(lo, st[idx])
+            hi = np.maximum(hi, st[idx + 1])
+        for r0 in range(0, n, 32):
+            u0 = (int(lo[r0:r0 + 32].min()) // 32) * 32
+            u1 = r0 + 32 if causal else ((int(hi[r0:r0 + 32].max()) + 31) // 32) * 32
+            total += (u1 - u0) * 32
+    return total
+
+
+def measured_mfma(workload: str):
+    """bf16 MFMA flops per launch from the committed counter run
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16, 512 flops per unit), if taken on the
+    current kernel source; else None."""
+    try:
+        ent = json.load(open(MFMA_FILE)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not ent or ent.get("kernel_sha") != kernel_sha():
+        return None
+    return ent.get("bf16_flops_per_launch")
 
 
 def kernel_sha() -> str:
@@ -328,6 +364,8 @@ def main():
     ach_gbs = bytes_min / (kernel_ms / 1e3) / 1e9  # the attention kernel alone
     useful_tflops = f_distinct / sec / 1e12
     traffic = measured_traffic(w.name)
+    issued = B * issued_pairs(tables, w.causal)
+    mfma_flops = measured_mfma(w.name)
 
     # error of the estimate against exact ALiBi on sampled rows (informational)
     import oracle as orc
@@ -487,7 +525,14 @@ def main():
                      "kernel_ms": kernel_ms,
                      "algorithmic_bytes_per_launch": bytes_min,
                      "arith_intensity_flop_per_byte": f_distinct / bytes_min,
-                     "useful_tflops_in_kernel": f_distinct / (kernel_ms / 1e3) / 1e12},
+                     "useful_tflops_in_kernel": f_distinct / (kernel_ms / 1e3) / 1e12,
+                     "issued_pairs": issued,
+                     "issued_tflops_in_kernel": 4.0 * d * issued / (kernel_ms / 1e3) / 1e12,
+                     "mfma_counters": None if mfma_flops is None else {
+                         "bf16_tflop_per_launch": mfma_flops / 1e12,
+                         "tflops": mfma_flops / (kernel_ms / 1e3) / 1e12,
+                         "pct_bf16_peak": 100.0 * mfma_flops / (kernel_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "source": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, profiles/mfma.json"}},
         "cpu_baseline": cpu,
         "host_sample_ms": host_sample_ms,
         "parity_sampled_rows_max_abs": parity,
