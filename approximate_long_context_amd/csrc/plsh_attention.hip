@@ -278,7 +278,9 @@ __global__ __launch_bounds__(64) void debug_intervals_kernel(const double *param
 // ---------------------------------------------------------------------------
 // Reference kernel (VALU, fp32 arithmetic): one wave per query row at a time.
 // Used for fp32 inputs and as an independent GPU formulation for bf16.
-// Grid: one 256-thread workgroup per (head slot, batch, 128-row tile).
+// Grid: one 256-thread workgroup per (head slot, batch, 32-row group); each
+// of its four waves sets up the group's block intervals in its own scratch
+// and takes eight of the rows.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ float load_elem(const T *p, int64_t i);
@@ -316,13 +318,15 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
   float *qrow = (float *)(rhi + s);
   float *pj = qrow + D;
 
-  const int unit = blockIdx.x / a.groups;
-  const int g = blockIdx.x % a.groups;
+  const int g32 = (n + 31) / 32;
+  const int unit = blockIdx.x / g32;
+  const int g = blockIdx.x % g32;
   const int h = a.order[unit / a.batch];
   const int b = unit % a.batch;
   const int kvh = h / (a.heads / a.kv_heads);
-  const int r0 = g * 128 + wave * 32;
-  if (r0 >= n) return;
+  const int r0 = g * 32;             // the group's first row
+  const int t_lo = 8 * wave;         // this wave's rows r0 + t_lo .. + 7
+  if (r0 + t_lo >= n) return;
 
   const T *Q = (const T *)a.q + ((int64_t)b * a.heads + h) * n * D;
   const T *K = (const T *)a.k + ((int64_t)b * a.kv_heads + kvh) * n * D;
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
   wave_setup(a.params + 2 * (int64_t)h * a.pstride, s, n, r0, lane, w);
 
   constexpr int E = D / 64;
-  for (int t = 0; t < 32 && r0 + t < n; ++t) {
+  for (int t = t_lo; t < t_lo + 8 && r0 + t < n; ++t) {
     const int i = r0 + t;
     int ulo = n, uhi = 0;
     for (int k = lane; k < s; k += 64) {
@@ -2316,7 +2320,7 @@ void launch_k(void (*kern)(Args...), dim3 grid, dim3 block, size_t shm, hipStrea
 plsh_status launch_valu(const dev::AttnArgs &a, int d, plsh_dtype dtype, int causal, hipStream_t st,
                         const char *who) {
   const size_t shm = 4 * dev::valu_wave_bytes(a.s, d);
-  const dim3 grid((unsigned)((int64_t)a.groups * a.batch * a.heads)), block(256);
+  const dim3 grid((unsigned)((int64_t)((a.n + 31) / 32) * a.batch * a.heads)), block(256);
   auto *tm = timer_slot();
   if (dtype == PLSH_F32) {
     if (d == 64) launch_k(dev::attn_valu_kernel<float, 64>, grid, block, shm, st, tm, a, causal);
