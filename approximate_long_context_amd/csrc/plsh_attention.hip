@@ -526,9 +526,13 @@ __host__ __device__ constexpr size_t rec_diag_off(int s) { return 16 + (size_t)1
 __host__ __device__ constexpr size_t rec_bytes(int s) { return rec_diag_off(s) + 1024; }
 constexpr int kMaxMfmaSamples = 124;
 
+// With CAUSAL false and ws_causal set, the same pass also writes the causal
+// record of every group to ws_causal: the same sorted leads, the group's end
+// as its key limit, and the diagonal table without the keys after the row
+// (the block ends only count for those keys, so the rest is the same).
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) void edges_kernel(const double *params, int pstride, int n, int heads, int s,
-                                                    int g32, uint8_t *ws) {
+                                                    int g32, uint8_t *ws, uint8_t *ws_causal) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = lane & 31, hh = lane >> 5;
@@ -548,6 +552,8 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int ps
   uint8_t *rec = ws + (size_t)item * rec_bytes(s);
   u32x2 *evl = (u32x2 *)(rec + rec_evl_off());
   u32x2 *evt = (u32x2 *)(rec + rec_evt_off(s));
+  uint8_t *rec_c = (!CAUSAL && ws_causal) ? ws_causal + (size_t)item * rec_bytes(s) : nullptr;
+  u32x2 *evl_c = rec_c ? (u32x2 *)(rec_c + rec_evl_off()) : nullptr;
   int mn = INT32_MAX, mx = INT32_MIN;
   for (int k = lane; k < s; k += 64) {
     const int32_t lk = w.lead[k], tk = w.trail[k];
@@ -566,14 +572,17 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int ps
     const uint32_t wt = mk ? ~((1u << (31 - __builtin_clz(mk))) - 1u) : 0xFFFFFFFFu;
     evl[rl] = u32x2{(uint32_t)lk, wl};
     if (!CAUSAL) evt[rt] = u32x2{(uint32_t)tk, wt};
+    if (evl_c) evl_c[rl] = u32x2{(uint32_t)lk, wl};
   }
   if (lane < kSentinels) {
     evl[s + lane] = u32x2{0x7FFFFFFFu, 0u};
     if (!CAUSAL) evt[s + lane] = u32x2{0x7FFFFFFFu, 0u};
+    if (evl_c) evl_c[s + lane] = u32x2{0x7FFFFFFFu, 0u};
   }
   const int U0w = wave_min_i(mn) & ~31;
   const int U1w = CAUSAL ? r0 + 32 : ((wave_max_i(mx) + 31) & ~31);
   if (lane == 0) *(int4 *)rec = make_int4(nact, U0w, U1w, 0);
+  if (rec_c && lane == 0) *(int4 *)rec_c = make_int4(nact, U0w, r0 + 32, 0);
 
   // diagonal tile: row t's block starts inside the rows (highest mask bit <= t)
   // and, non-causal, its block ends inside them (lowest bit > t), as per-row
@@ -620,6 +629,14 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int ps
       if ((CAUSAL && u > t) || r0 + u > last) c[i] &= ~(0xFFu << (8 * r));
     }
   *(u32x4 *)(rec + rec_diag_off(s) + 32 * t + 16 * hh) = c;
+  if (rec_c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (16 * hh + 4 * i + r > t) c[i] &= ~(0xFFu << (8 * r));
+    *(u32x4 *)(rec_c + rec_diag_off(s) + 32 * t + 16 * hh) = c;
+  }
 }
 
 // max of three finite floats in one instruction (the compiler's max of
@@ -2337,13 +2354,15 @@ size_t records_bytes(int n, int heads, int s) { return (size_t)heads * ((n + 31)
 
 // The block-edge records of every (head, 32-row group), causal or not, into
 // ws (records_bytes(a.n, a.heads, a.s) bytes, 16-byte aligned).
-plsh_status launch_edges(const dev::AttnArgs &a, bool causal, hipStream_t st, const char *who, void *ws) {
+// (non-causal with ws_causal set: both record sets in one pass)
+plsh_status launch_edges(const dev::AttnArgs &a, bool causal, hipStream_t st, const char *who, void *ws,
+                         void *ws_causal = nullptr) {
   const int g32 = (a.n + 31) / 32;
   const int items = a.heads * g32;
   const dim3 egrid((unsigned)((items + 3) / 4)), eblock(256);
   const size_t eshm = 4 * (dev::wavetab_bytes(a.s) + 32 * 16 * 4);
-  if (causal) hipLaunchKernelGGL(dev::edges_kernel<true>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)ws);
-  else hipLaunchKernelGGL(dev::edges_kernel<false>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)ws);
+  if (causal) hipLaunchKernelGGL(dev::edges_kernel<true>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)ws, (uint8_t *)nullptr);
+  else hipLaunchKernelGGL(dev::edges_kernel<false>, egrid, eblock, eshm, st, a.params, a.pstride, a.n, a.heads, a.s, g32, (uint8_t *)ws, (uint8_t *)ws_causal);
   return launch_check(who);
 }
 
@@ -2360,6 +2379,24 @@ plsh_status build_records(const dev::AttnArgs &a, bool causal, hipStream_t st, c
                 hipGetErrorString(e));
   }
   return launch_edges(a, causal, st, who, *ws);
+}
+
+// Causal and non-causal records in one pre-pass (the causal backward's two
+// record sets), each in its own workspace from the stream-ordered allocator.
+plsh_status build_record_pair(const dev::AttnArgs &a, hipStream_t st, const char *who, void **ws_causal,
+                              void **ws_nc) {
+  const size_t ws_bytes = records_bytes(a.n, a.heads, a.s);
+  *ws_causal = *ws_nc = nullptr;
+  for (void **p : {ws_causal, ws_nc}) {
+    const hipError_t e = hipMallocAsync(p, ws_bytes, st);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      *p = nullptr;
+      return fail(PLSH_ERR_HIP, "%s: workspace allocation of %zu bytes failed: %s", who, ws_bytes,
+                  hipGetErrorString(e));
+    }
+  }
+  return launch_edges(a, false, st, who, *ws_nc, *ws_causal);
 }
 
 plsh_status free_records(void *ws, hipStream_t st, const char *who, plsh_status rc) {
@@ -2738,9 +2775,13 @@ static plsh_status backward_common(const char *who, const void *q, const void *k
     rc = launch_check(who);
   }
   // the records of the estimator serve its statistics pass and dQ; dK/dV
-  // takes non-causal ones (the same records when the call is not causal)
+  // takes non-causal ones (the same records when the call is not causal;
+  // a causal call gets both sets from one pre-pass)
   void *rec = nullptr, *rec_nc = nullptr;
-  if (rc == PLSH_OK) rc = build_records(a, causal != 0, hs, who, &rec);
+  if (rc == PLSH_OK) {
+    if (causal) rc = build_record_pair(a, hs, who, &rec, &rec_nc);
+    else rc = build_records(a, false, hs, who, &rec);
+  }
   if (rc == PLSH_OK && !saved) {
     // statistics: each row's normaliser and D = dO . O
     a.stat_lse2 = (float *)stats;
@@ -2754,7 +2795,6 @@ static plsh_status backward_common(const char *who, const void *q, const void *k
     a.dvec = dvec;
     rc = launch_attn(a, d, causal != 0, hs, who, 1, rec);
   }
-  if (rc == PLSH_OK && causal) rc = build_records(a, false, hs, who, &rec_nc);
   if (rc == PLSH_OK) {
     // dK/dV workgroups run per KV head: the group with the largest summed
     // sigma first
