@@ -83,6 +83,10 @@ struct AttnArgs {
   // when set, the MFMA kernel writes lse2 ([batch, heads, ns], rows n .. ns - 1
   // hold 0) beside out: the statistic a later backward reads
   float *save_lse2;
+  // backward from a saved forward: the dQ kernel forms D = dO . O from this
+  // output ([batch, heads, n, d], bf16) itself and writes it to stat_dvec
+  // (rows n .. ns - 1: 0) for the dK/dV kernel, instead of reading dvec
+  const void *saved_out;
   int32_t order[kMaxHeadsArg];  // head processed in slot i, heaviest sigma first
 };
 
@@ -1238,10 +1242,33 @@ void attn_dq_kernel(AttnArgs a, const uint8_t *ws) {
       if (active && i < n) raw = *(const u32x4 *)(dOp + (int64_t)i * D + 32 * c + 8 * gq);
       dof[c] = __builtin_bit_cast(bf16x8, raw);
     }
+    const int ns = (n + 31) & ~31;
+    const int64_t row = ((int64_t)b * a.heads + h) * ns + i;  // rows padded to 32
     if (active && i < n) {
-      const int64_t row = ((int64_t)b * a.heads + h) * ((n + 31) & ~31) + i;  // rows padded to 32
       lse2r = a.lse2[row];
-      dvr = a.dvec[row];
+      if (!a.saved_out) dvr = a.dvec[row];
+    }
+    if (a.saved_out) {
+      // D_i = dO_i . O_i from the saved output, in the dO fragment's layout:
+      // the lane's 8 NC dims, then the sum over the row's four lanes
+      const uint16_t *Op = (const uint16_t *)a.saved_out + ((int64_t)b * a.heads + h) * n * D;
+      float acc = 0.f;
+      if (active && i < n) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const u32x4 o = *(const u32x4 *)(Op + (int64_t)i * D + 32 * c + 8 * gq);
+          const u32x4 g = __builtin_bit_cast(u32x4, dof[c]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc = fmaf(__uint_as_float(o[e] << 16), __uint_as_float(g[e] << 16), acc);
+            acc = fmaf(__uint_as_float(o[e] & 0xFFFF0000u), __uint_as_float(g[e] & 0xFFFF0000u), acc);
+          }
+        }
+      }
+      acc += xor16_f(acc);
+      acc += other_half_f(acc, lane);
+      dvr = acc;
+      if (gq == 0 && i < ns) a.stat_dvec[row] = i < n ? acc : 0.f;
     }
   }
   // Everything loaded so far is needed before the first tile.  Waiting here,
@@ -2191,38 +2218,6 @@ void attn_dkv_kernel(AttnArgs a, const uint8_t *ws, uint16_t *dk_out, uint16_t *
   }
 }
 
-// ---------------------------------------------------------------------------
-// D_i = dO_i . O_i (fp32 sums of bf16 products) for the backward from a saved
-// forward; rows n .. ns - 1 of each (batch, head) get 0.  Sixteen lanes per
-// row, 16 bytes per lane and pass; rows are [batch * heads][ns].
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void dvec_kernel(const uint16_t *o, const uint16_t *dout, int n, int ns,
-                                                   int64_t rows, float *dvec) {
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int l = threadIdx.x & 15;
-  float acc = 0.f;
-  if (row < rows) {
-    const int64_t slab = row / ns;
-    const int i = (int)(row - slab * ns);
-    if (i < n) {
-      const uint16_t *orow = o + (slab * n + i) * D, *drow = dout + (slab * n + i) * D;
-#pragma unroll
-      for (int c = 8 * l; c < D; c += 128) {
-        const u32x4 ov = *(const u32x4 *)(orow + c), dv = *(const u32x4 *)(drow + c);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          acc = fmaf(__uint_as_float(ov[w] << 16), __uint_as_float(dv[w] << 16), acc);
-          acc = fmaf(__uint_as_float(ov[w] & 0xFFFF0000u), __uint_as_float(dv[w] & 0xFFFF0000u), acc);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-  if (row < rows && l == 0) dvec[row] = acc;
-}
-
 }  // namespace dev
 
 // ---------------------------------------------------------------------------
@@ -2293,6 +2288,7 @@ void fill_args(dev::AttnArgs &a, const void *q, const void *k, const void *v, vo
   a.stat_lse2 = nullptr;
   a.stat_dvec = nullptr;
   a.save_lse2 = nullptr;
+  a.saved_out = nullptr;
   // heavy heads first: per-row work grows with sigma
   int idx[dev::kMaxHeadsArg];
   std::iota(idx, idx + heads, 0);
@@ -2763,17 +2759,6 @@ static plsh_status backward_common(const char *who, const void *q, const void *k
   fill_args(a, q, k, v, dq, batch, n, heads, kv_heads, sigma, s, boundaries);
   a.dout = dout;
   plsh_status rc = PLSH_OK;
-  if (saved) {
-    // D = dO . O from the saved output
-    const dim3 grid((unsigned)((prows + 15) / 16)), block(256);
-    if (d == 64)
-      hipLaunchKernelGGL(dev::dvec_kernel<64>, grid, block, 0, hs, (const uint16_t *)saved_out,
-                         (const uint16_t *)dout, n, ns, prows, dvec);
-    else
-      hipLaunchKernelGGL(dev::dvec_kernel<128>, grid, block, 0, hs, (const uint16_t *)saved_out,
-                         (const uint16_t *)dout, n, ns, prows, dvec);
-    rc = launch_check(who);
-  }
   // the records of the estimator serve its statistics pass and dQ; dK/dV
   // takes non-causal ones (the same records when the call is not causal;
   // a causal call gets both sets from one pre-pass)
@@ -2789,11 +2774,16 @@ static plsh_status backward_common(const char *who, const void *q, const void *k
     rc = launch_attn(a, d, causal != 0, hs, who, 0, rec);
   }
   if (rc == PLSH_OK) {
+    // dQ; from a saved forward it also forms D = dO . O into dvec
     a.stat_lse2 = nullptr;
-    a.stat_dvec = nullptr;
+    a.stat_dvec = saved ? dvec : nullptr;
+    a.saved_out = saved ? saved_out : nullptr;
     a.lse2 = lse2;
-    a.dvec = dvec;
+    a.dvec = saved ? nullptr : dvec;
     rc = launch_attn(a, d, causal != 0, hs, who, 1, rec);
+    a.stat_dvec = nullptr;
+    a.saved_out = nullptr;
+    a.dvec = dvec;
   }
   if (rc == PLSH_OK) {
     // dK/dV workgroups run per KV head: the group with the largest summed

@@ -334,12 +334,13 @@ plsh_status plsh_alibi_attention_lse(const void *q, const void *k, const void *v
  * plsh_alibi_attention_backward_saved -- plsh_alibi_attention_backward from a
  * saved forward: `out` and `lse2` as written by plsh_alibi_attention_lse for
  * the same q, k, v, tables and causal flag (Experimental Validation: training
- * with the method).  The statistics pass is replaced by one streaming kernel
- * for D_i = dO_i . out_i (fp32 sums of the bf16 products); every other
- * launch is plsh_alibi_attention_backward's.  Because D is taken from the
- * bf16 output rather than the fp32 estimate, the gradients differ from
- * plsh_alibi_attention_backward's by the output's rounding (relative 2^-9
- * per element of D).
+ * with the method).  There is no statistics pass: the dQ kernel forms
+ * D_i = dO_i . out_i (fp32 sums of the bf16 products) from the saved output
+ * and writes it for the dK/dV kernel; the other launches are
+ * plsh_alibi_attention_backward's.  Because D is taken from the bf16 output
+ * rather than the fp32 estimate, the gradients differ from
+ * plsh_alibi_attention_backward's by the output's rounding (relative 2^-8
+ * per element at most).
  *   out    DEVICE [batch, heads, n, d] bf16, 16-byte aligned
  *   lse2   DEVICE float [batch][heads][ceil32(n)], 16-byte aligned
  *   the other arguments as for plsh_alibi_attention_backward.
