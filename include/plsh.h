@@ -286,12 +286,13 @@ plsh_status plsh_alibi_attention_walk(const void *q, const void *k, const void *
  *   dq          DEVICE [batch, heads, n, d] output
  *   dk, dv      DEVICE [batch, kv_heads, n, d] outputs
  *   the other arguments as for plsh_alibi_attention; bf16, s <= 124.
- * Launches: the block-edge pre-pass; a pass of the estimator that writes,
- * in place of O, each row's normaliser and D_i = dO_i.O_i (O in fp32); the
- * dQ kernel (rows as in the estimator, same records); for causal calls a
- * non-causal pre-pass; the dK/dV kernel (key positions in place of rows,
- * using c_ij = c_ji; one workgroup per 128 key positions of a KV head,
- * looping over that head's query heads).  dq, dk, dv are written whole (no
+ * Launches: the block-edge pre-pass (for causal calls one pass that writes
+ * both the causal records and the non-causal ones the dK/dV kernel takes); a
+ * pass of the estimator that writes, in place of O, each row's normaliser
+ * and D_i = dO_i.O_i (O in fp32); the dQ kernel (rows as in the estimator,
+ * same records); the dK/dV kernel (key positions in place of rows, using
+ * c_ij = c_ji; one workgroup per 128 key positions of a KV head, looping
+ * over that head's query heads).  dq, dk, dv are written whole (no
  * accumulation into them).
  * Device memory: 8 * batch*heads*ceil32(n) bytes of statistics from the
  * stream-ordered allocator on `stream`, released within the call, plus the
