@@ -253,11 +253,12 @@ def workspace_size(n: int, heads: int, s: int, dtype: torch.dtype) -> int:
 def attention(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
               out: Optional[torch.Tensor] = None, stream: Optional[int] = None,
               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The estimator, q [B,H,n,d], k/v [B,Hkv,n,d].  On torch's current
-    stream: plsh_alibi_attention_ws with `workspace` (a device uint8 tensor
-    of at least workspace_size() bytes) or one from torch's caching
-    allocator.  With an explicit `stream` and no workspace:
-    plsh_alibi_attention (the library's stream-ordered workspace)."""
+    """The estimator, q [B,H,n,d], k/v [B,Hkv,n,d]: plsh_alibi_attention_ws
+    with `workspace` (a device uint8 tensor of at least workspace_size()
+    bytes) or, on torch's current stream, one from torch's caching
+    allocator.  The call runs on `stream` if given (with no workspace it is
+    then plsh_alibi_attention, with the library's stream-ordered workspace),
+    else on torch's current stream."""
     if stream is not None and workspace is None:
         return _attention(lib().plsh_alibi_attention, q, k, v, sigma, s, tables, causal, out, stream)
     need = workspace_size(q.shape[2], q.shape[1], s, q.dtype)
