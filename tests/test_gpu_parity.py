@@ -740,3 +740,27 @@ def test_lse_forward_workspace_paths_bitwise(dev):
                                      stream=torch.cuda.current_stream(dev).cuda_stream)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_saved_backward_slopes_non_causal_sampled(dev):
+    """The per-head-slopes workload (batch 2, 8 heads, n = 4096, d = 64,
+    non-causal, s = 16, sigma 2..256) from a saved forward: lse2 and dq at
+    sampled rows of every head and batch element, dk and dv at sampled keys
+    of the heaviest head, against the oracle."""
+    w = W.get("slopes-n4096")
+    (q, k, v, do, tabs), (out, lse2, plain), (gq, gk, gv) = run_saved(dev, w, w.causal)
+    assert torch.equal(out, plain)
+    qf, kf, vf, dof = W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do)
+    rows = W.sample_rows(w.n, 12, seed=47)
+    ref = orc.lsh_row_log_normaliser(qf, kf, tabs, w.causal, rows=rows) / math.log(2.0)
+    err = float(np.abs(lse2.cpu().double().numpy()[:, :, rows] - ref).max())
+    say("lse2 slopes", f"max|lse2 - oracle| = {err:.3e}")
+    assert err <= LSE2_TOL, err
+    rq = orc.lsh_grad_rows(qf, kf, vf, dof, tabs, w.causal, rows)
+    check_grad(gq[:, :, rows], rq, "saved dq slopes sampled rows")
+    keys = W.sample_rows(w.n, 4, seed=53)
+    h = w.heads - 1   # sigma 256, its own kv head
+    rk, rv = orc.lsh_grad_keys(qf[:, h:h + 1], kf[:, h:h + 1], vf[:, h:h + 1], dof[:, h:h + 1], tabs[h:h + 1],
+                               w.causal, keys)
+    check_grad(gk[:, h:h + 1][:, :, keys], rk, "saved dk slopes heaviest head")
+    check_grad(gv[:, h:h + 1][:, :, keys], rv, "saved dv slopes heaviest head")
