@@ -160,10 +160,11 @@ SWEEP = ["tiny-f32-n512", "slopes-n4096", "qwen3-0.6b-n8192-s10", "qwen3-0.6b-n8
 
 def sweep(settle_s: float) -> None:
     """Every workload: the call's time and throughput, the attention kernel's
-    time and HBM roofline fraction, and (informational) the estimate's error
+    time and HBM roofline fraction, (informational) the estimate's error
     against exact ALiBi on the whole output, the exact output from the dense
-    exact-ALiBi kernel (bf16 workloads; the fp32 one has no exact kernel).
-    One JSON line per workload."""
+    exact-ALiBi kernel, and the time of the backward from a saved forward
+    (bf16 workloads; the fp32 one has neither an exact nor a backward
+    kernel).  One JSON line per workload."""
     dev = torch.device("cuda:0")
     for name in SWEEP:
         w = W.get(name)
@@ -184,6 +185,17 @@ def sweep(settle_s: float) -> None:
         B, H, Hkv, n, d, s = w.batch, w.heads, w.kv_heads, w.n, w.d, w.s
         bytes_min = w.esz * B * n * d * (2 * H + 2 * Hkv)
         err = error_stats(out, exact_reference(w, qd, kd, vd)) if w.dtype == "bf16" else None
+        bwd = None
+        if w.dtype == "bf16" and s <= 124:
+            # the backward from a saved forward (output and row statistics)
+            g = torch.Generator().manual_seed(3)
+            dod = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+            o_s, l_s = plsh.attention_with_lse(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal)
+            bw_ms, _ = time_calls(lambda: plsh.attention_backward(qd, kd, vd, dod, w.sigma, w.s, dt,
+                                                                  causal=w.causal, out=o_s, lse2=l_s),
+                                  5 if n <= 16384 else 3, 2)
+            bwd = {"saved_forward_backward_ms": bw_ms, "over_forward_call": bw_ms / ms}
+            del dod, o_s, l_s
         del qd, kd, vd, out
         torch.cuda.empty_cache()
         rec = {"sweep": True, "workload": name, "batch": B, "heads": H, "kv_heads": Hkv, "n": n, "d": d,
@@ -192,10 +204,11 @@ def sweep(settle_s: float) -> None:
                "useful_tflops": 4.0 * d * B * pairs_distinct / (ms / 1e3) / 1e12,
                "s_walk_equivalent_tflops": 4.0 * d * B * pairs_alg / (ms / 1e3) / 1e12,
                "hbm_frac_kernel": bytes_min / (kernel_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
-               "error_vs_exact_alibi": err}
+               "error_vs_exact_alibi": err, "backward": bwd}
         log(f"[sweep] {name}: {ms:.4f} ms/call, kernel {kernel_ms:.4f} ms, "
             f"{rec['rows_samples_per_s']:.3g} rows*samples/s, HBM frac {rec['hbm_frac_kernel']:.2f}, "
-            f"rel. error vs exact {'n/a' if err is None else format(err['rel_fro'], '.3f')}")
+            f"rel. error vs exact {'n/a' if err is None else format(err['rel_fro'], '.3f')}, "
+            f"backward {'n/a' if bwd is None else format(bwd['saved_forward_backward_ms'], '.3f') + ' ms'}")
         print(json.dumps(rec), flush=True)
         del q, k, v
 
