@@ -32,17 +32,20 @@ PLSH_HD double bin_of(int32_t x, double delta, double u) {
 // a = fl(x + u), Q = a / delta exact, D = fl(Q) the correctly rounded
 // quotient and q = fl(a * rinv), rinv = fl(1 / delta): each of the three
 // roundings errs by at most 2^-53 relative, so |q - D| <= 3.02 * 2^-53 |q|.
-// If no integer lies within 2^-50 |q| of q, then D and q have the same floor.
-// (q - f and (f + 1) - q are exact by Sterbenz's lemma below 2^52; from 2^52
-// on every double is an integer, q - f == 0 and the division is taken; a
-// fused multiply-add in either difference only makes it more accurate.)
-// Otherwise, and for q == 0, inf or NaN, the defining division decides.
+// If no integer lies within that distance of q, D and q have the same floor
+// f.  The test: r = q - f (exact by Sterbenz's lemma), accepted when
+// |r - 1/2| < 1/2 - 2^-50 |q|, i.e. r farther than 2^-50 |q| from 0 and 1.
+// The two remaining roundings (of r - 1/2 and of the bound) err by at most
+// 2^-54 together, which leaves a margin above 3.02 * 2^-53 |q| for
+// |q| >= 1/10; below that f = 0 and 0 <= D < 1 anyway.  q == 0 gives
+// |r - 1/2| == 1/2, |q| >= 2^49 a bound <= 0, inf and NaN a NaN: all rejected,
+// so the defining division decides (a fused multiply-add in the bound is
+// exact, the product being a power-of-two scaling).
 PLSH_HD double bin_of_r(int32_t x, double delta, double u, double rinv) {
   const double a = (double)x + u;
   const double q = a * rinv;
   const double f = floor(q);
-  const double tol = fabs(q) * 0x1p-50;
-  if (q - f > tol && (f + 1.0) - q > tol) return f;
+  if (fabs((q - f) - 0.5) < 0.5 - fabs(q) * 0x1p-50) return f;
   return floor(a / delta);
 }
 
