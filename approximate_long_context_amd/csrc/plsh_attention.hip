@@ -154,10 +154,13 @@ struct WaveTab {
   int32_t *trail;  // [s]
   uint32_t *mask;  // [s]
   int32_t *act;    // [s] samples with a block start inside the wave's rows
+  u32x4 *lst;      // [64][2] operands of up to 64 listed samples: (delta, u), (1 / delta, k)
 };
 
 // bytes of LDS a WaveTab needs (16-byte multiple)
-__host__ __device__ constexpr size_t wavetab_bytes(int s) { return ((size_t)16 * s + 16 * s + 15) & ~(size_t)15; }
+__host__ __device__ constexpr size_t wavetab_bytes(int s) {
+  return (((size_t)16 * s + 16 * s + 15) & ~(size_t)15) + 64 * 32;
+}
 
 __device__ __forceinline__ WaveTab carve_wavetab(uint8_t *base, int s) {
   WaveTab w;
@@ -166,6 +169,7 @@ __device__ __forceinline__ WaveTab carve_wavetab(uint8_t *base, int s) {
   w.trail = w.lead + s;
   w.mask = (uint32_t *)(w.trail + s);
   w.act = (int32_t *)(w.mask + s);
+  w.lst = (u32x4 *)(base + (((size_t)16 * s + 16 * s + 15) & ~(size_t)15));
   return w;
 }
 
@@ -207,6 +211,15 @@ __device__ int wave_ends(const double *prm, int s, int n, int r0, int lane, cons
   return nact;
 }
 
+// x from lane l - 1 (all 64 lanes in one DPP move per half of the double;
+// lane 0 gets 0): the lane's left neighbour's value without an LDS round trip
+__device__ __forceinline__ double from_left_lane(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, 0x138 /* wave_shr:1 */, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), 0x138, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // Step 2: start masks of the listed samples.  The two half-waves take one
 // sample each and lane t evaluates the bin of position r0 + t, so a start is
 // a bin change between neighbouring lanes.
@@ -215,26 +228,38 @@ __device__ void wave_masks(int n, int r0, int lane, int nact, const WaveTab &w) 
   const int t = lane & 31, hh = lane >> 5;
   const int x = r0 + t;
   for (int c0 = 0; c0 < nact; c0 += 64) {
-    // the chunk's listed samples, one per lane, so that the loop below takes
-    // its operands from registers instead of dependent LDS reads
-    const int kc = c0 + lane < nact ? w.act[c0 + lane] : 0;
-    const double dlc = w.prm[2 * kc], uc = w.prm[2 * kc + 1];
-    const double ric = 1.0 / dlc;
+    // the chunk's listed samples, one per lane, staged as 32-byte operand
+    // records; each half-wave then reads its sample's record with two
+    // broadcast reads per step
     const int m = min(64, nact - c0);
+    if (lane < m) {
+      const int kc = w.act[c0 + lane];
+      const double dlc = w.prm[2 * kc], uc = w.prm[2 * kc + 1];
+      const double ric = 1.0 / dlc;
+      const uint64_t bd = (uint64_t)__double_as_longlong(dlc), bu = (uint64_t)__double_as_longlong(uc);
+      const uint64_t br = (uint64_t)__double_as_longlong(ric);
+      w.lst[2 * lane] = u32x4{(uint32_t)bd, (uint32_t)(bd >> 32), (uint32_t)bu, (uint32_t)(bu >> 32)};
+      w.lst[2 * lane + 1] = u32x4{(uint32_t)br, (uint32_t)(br >> 32), (uint32_t)kc, 0u};
+    }
+    wave_sync();
 #pragma unroll 2
     for (int a0 = 0; a0 < m; a0 += 2) {
       // half-wave hh takes listed sample c0 + a0 + hh
       const int src = min(a0 + hh, m - 1);
-      const int k = __shfl(kc, src);
-      const double dl = __shfl(dlc, src), u = __shfl(uc, src), ri = __shfl(ric, src);
+      const u32x4 r0 = w.lst[2 * src], r1 = w.lst[2 * src + 1];
+      const double dl = __longlong_as_double((long long)(((uint64_t)r0[1] << 32) | r0[0]));
+      const double u = __longlong_as_double((long long)(((uint64_t)r0[3] << 32) | r0[2]));
+      const double ri = __longlong_as_double((long long)(((uint64_t)r1[1] << 32) | r1[0]));
+      const int k = (int)r1[2];
       const bool have = a0 + hh < m;
       const bool valid = have && x <= last;
       double b = 0.0;
       if (valid) b = bin_of_r(x, dl, u, ri);
-      const double bp = __shfl_up(b, 1, 32);
+      const double bp = from_left_lane(b);  // (lanes 0 and 32 have t == 0: unused)
       const uint64_t bal = __ballot(valid && t > 0 && b != bp);
       if (t == 0 && have) w.mask[k] = (uint32_t)(bal >> (32 * hh));
     }
+    wave_sync();  // every read of the records before the next chunk's
   }
 }
 
