@@ -492,6 +492,28 @@ __device__ __forceinline__ uint32_t swz(int key, int c) {
   return (uint32_t)(key * D * 2 + ((c ^ swz_key<D>(key)) << 4));
 }
 
+// The forward kernel's K tiles (and its staged Q rows, read the same way)
+// use a swizzle of their own at D = 128.  Measured on gfx950 (bank-conflict
+// counter over single read patterns): a 16-byte read serves in one cycle the
+// lanes 0..7 of a 16-lane block together with lanes 8..15 of its neighbour
+// (lanes 0-7 with 24-31, 8-15 with 16-23, and likewise in the upper half),
+// whereas 8-byte reads serve 32 consecutive lanes.  The K operand read has
+// lane (qc, gq) read key qc at chunk 4 c + gq, so keys 0..7 of block gq and
+// keys 8..15 of block gq ^ 1 share a cycle; XOR with the key's low four bits
+// keeps the two halves on disjoint chunk sets (bit 3 of the chunk stays that
+// of the key, XOR 4 c permuting both sets alike).  The V operand's 8-byte
+// transposing reads need the key's low three bits spread over chunk pairs
+// instead, which swz_key provides, so V tiles keep it.
+template <int D>
+__device__ __forceinline__ int swz_key_k(int key) {
+  return D == 128 ? (key & 15) : swz_key<D>(key);
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t swz_k(int key, int c) {
+  return (uint32_t)(key * D * 2 + ((c ^ swz_key_k<D>(key)) << 4));
+}
+
 // LDS address of a pointer into LDS (the generic-to-LDS cast; on static
 // shared variables it folds to a constant)
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_void_t *)p; }
@@ -825,7 +847,7 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   #pragma unroll
       for (int c0 = 0; c0 < 16 * CPR_Q; c0 += 64) {
         const int row = (c0 + lane) / CPR_Q, ch = (c0 + lane) % CPR_Q;
-        const int64_t off = (int64_t)min(r0 + row, n - 1) * (2 * D) + 16 * (ch ^ swz_key<D>(row));
+        const int64_t off = (int64_t)min(r0 + row, n - 1) * (2 * D) + 16 * (ch ^ swz_key_k<D>(row));
         dma16((const char *)Q + off, q_lds + 16 * c0);
       }
     }
@@ -837,16 +859,18 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     constexpr int CPW = 4 * D / kWaves;   // chunks per wave, stage and matrix (<= 64)
     constexpr int LPS = 2;                // loads per thread per stage (K and V)
     const char *Kb = (const char *)K, *Vb = (const char *)V;
-    // the lane's chunk of every stage: row dkey of the tile, 16 bytes at dofs
+    // the lane's chunk of every stage: row dkey of the tile, 16 bytes at
+    // dofs_k (K tile) and dofs_v (V tile)
     const int dslot = wave * CPW + lane;
     const int dkey = dslot / CPR;
-    const int dofs = 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
+    const int dofs_k = 16 * ((dslot % CPR) ^ swz_key_k<D>(dkey));
+    const int dofs_v = 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
     const uint32_t kv_lds = lds_addr(&lds.kv[0][0][0]) + wave * CPW * 16;
     auto issue_stage = [&](int st, int q) {  // q = st % kRing
       if (lane < CPW) {
-        const int64_t off = (int64_t)min(U0 + kTileKeys * st + dkey, n - 1) * (2 * D) + dofs;
-        dma16(Kb + off, kv_lds + (uint32_t)(2 * q) * (kTileKeys * D * 2));
-        dma16(Vb + off, kv_lds + (uint32_t)(2 * q + 1) * (kTileKeys * D * 2));
+        const int64_t row = (int64_t)min(U0 + kTileKeys * st + dkey, n - 1) * (2 * D);
+        dma16(Kb + row + dofs_k, kv_lds + (uint32_t)(2 * q) * (kTileKeys * D * 2));
+        dma16(Vb + row + dofs_v, kv_lds + (uint32_t)(2 * q + 1) * (kTileKeys * D * 2));
       }
     };
     // stages 0 and 1 now; the pair starting at stage st issues st + 2, st + 3
@@ -870,7 +894,7 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     // K operand: key 16 b + qc, chunk 4 c + gq; b = 1 lies 16 rows further
     uint32_t kofs[NC];
   #pragma unroll
-    for (int c = 0; c < NC; ++c) kofs[c] = swz<D>(qc, 4 * c + gq);
+    for (int c = 0; c < NC; ++c) kofs[c] = swz_k<D>(qc, 4 * c + gq);
     // V operand (v_ds_read_b64_tr_b16): in each 16-lane group gq, lane r names
     // the row (key 4 gq + r / 4, dims 16 db + 4 (r % 4) .. + 3), and lane i
     // receives V[4 gq + e][16 db + i], e = 0..3; keys + 16 lie 16 rows further
@@ -1064,7 +1088,7 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
         // has its fragment before slots 2, 3 take stages 2, 3
         const char *qt = (const char *)lds.kv[2][0] + wave * 32 * D;
   #pragma unroll
-        for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qt + swz<D>(qc, 4 * c + gq)));
+        for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qt + swz_k<D>(qc, 4 * c + gq)));
         PLSH_WAIT_VM_LGKM0(0);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
