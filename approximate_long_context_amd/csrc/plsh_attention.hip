@@ -514,6 +514,19 @@ __device__ __forceinline__ uint32_t swz_k(int key, int c) {
   return (uint32_t)(key * D * 2 + ((c ^ swz_key_k<D>(key)) << 4));
 }
 
+// The forward kernel's V tiles at D = 128 are not stored row by row: the
+// 64-byte piece of key `key` holding dims 32 m .. 32 m + 31 (chunks 4 m ..
+// 4 m + 3) lies at m * 2048 + key * 64, its chunk pairs swapped when bit 2 of
+// the key is set.  Each group of four copy lanes still reads one 64-byte
+// segment of a row; the transposing 8-byte reads of a 16-dim block (32
+// lanes: keys 0..7, two chunks, two halves) cover 256 distinct bytes; and
+// the reads of all eight dim blocks differ by immediate offsets, so they need
+// two address registers instead of eight (with eight, the compiler recycled
+// the operand registers and serialised every read behind a matrix op).
+__device__ __forceinline__ uint32_t vpiece128(int key, int chunk) {
+  return (uint32_t)((chunk >> 2) * 2048 + key * 64 + (((chunk & 3) ^ (((key >> 2) & 1) << 1)) << 4));
+}
+
 // LDS address of a pointer into LDS (the generic-to-LDS cast; on static
 // shared variables it folds to a constant)
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_void_t *)p; }
@@ -864,13 +877,18 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     const int dslot = wave * CPW + lane;
     const int dkey = dslot / CPR;
     const int dofs_k = 16 * ((dslot % CPR) ^ swz_key_k<D>(dkey));
-    const int dofs_v = 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
+    // V (D = 128): slot dslot holds key (dslot / 4) % 32, chunk 4 (dslot / 128)
+    // + (dslot % 4 with its pair swapped by bit 2 of the key); else as K rows
+    const int vkey = D == 128 ? (dslot >> 2) & 31 : dkey;
+    const int dofs_v = D == 128 ? 16 * (4 * (dslot >> 7) + ((dslot & 3) ^ (((vkey >> 2) & 1) << 1)))
+                                : 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
     const uint32_t kv_lds = lds_addr(&lds.kv[0][0][0]) + wave * CPW * 16;
     auto issue_stage = [&](int st, int q) {  // q = st % kRing
       if (lane < CPW) {
         const int64_t row = (int64_t)min(U0 + kTileKeys * st + dkey, n - 1) * (2 * D);
+        const int64_t vrow = (int64_t)min(U0 + kTileKeys * st + vkey, n - 1) * (2 * D);
         dma16(Kb + row + dofs_k, kv_lds + (uint32_t)(2 * q) * (kTileKeys * D * 2));
-        dma16(Vb + row + dofs_v, kv_lds + (uint32_t)(2 * q + 1) * (kTileKeys * D * 2));
+        dma16(Vb + vrow + dofs_v, kv_lds + (uint32_t)(2 * q + 1) * (kTileKeys * D * 2));
       }
     };
     // stages 0 and 1 now; the pair starting at stage st issues st + 2, st + 3
@@ -897,12 +915,24 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     for (int c = 0; c < NC; ++c) kofs[c] = swz_k<D>(qc, 4 * c + gq);
     // V operand (v_ds_read_b64_tr_b16): in each 16-lane group gq, lane r names
     // the row (key 4 gq + r / 4, dims 16 db + 4 (r % 4) .. + 3), and lane i
-    // receives V[4 gq + e][16 db + i], e = 0..3; keys + 16 lie 16 rows further
+    // receives V[4 gq + e][16 db + i], e = 0..3; keys + 16 lie vhi bytes
+    // further.  At D = 128 (vpiece128) the offsets of dim blocks db and
+    // db + 2 differ by 2048: two bases, the rest immediates.
     uint32_t vofs[NDB];
+    constexpr uint32_t vhi = D == 128 ? 16 * 64 : 16 * 2 * D;
+    if constexpr (D == 128) {
+      const int vk = 4 * gq + (qc >> 2);
+      uint32_t vb[2];
   #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int dim = 16 * db + 4 * (qc & 3);
-      vofs[db] = swz<D>(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1);
+      for (int e = 0; e < 2; ++e) vb[e] = vpiece128(vk, 2 * e + ((qc >> 1) & 1)) + 8 * (qc & 1);
+  #pragma unroll
+      for (int db = 0; db < NDB; ++db) vofs[db] = vb[db & 1] + 2048 * (db >> 1);
+    } else {
+  #pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int dim = 16 * db + 4 * (qc & 3);
+        vofs[db] = swz<D>(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1);
+      }
     }
 
     // this wave's tiles are the stages [sa, sb)
@@ -1061,7 +1091,7 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
         for (int j = 0; j < NB; ++j) {
           const char *va = vt + vofs[d0 + j];
           const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)va);
-          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(va + 16 * 2 * D));
+          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(va + vhi));
           vop[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
