@@ -514,6 +514,15 @@ __device__ __forceinline__ uint32_t swz_k(int key, int c) {
   return (uint32_t)(key * D * 2 + ((c ^ swz_key_k<D>(key)) << 4));
 }
 
+// The backward dQ kernel's K and V tiles at D = 128 are stored the same way,
+// with K's chunk pairs swapped like V's (piece128): K is read there both as
+// a 16-byte operand (key qc, chunk 4 c + gq) and through the transposing
+// reads, and the conflict counter shows both free of conflicts in that
+// layout; V is read as a 16-byte operand.
+__device__ __forceinline__ uint32_t piece128(int key, int chunk) {
+  return (uint32_t)((chunk >> 2) * 2048 + key * 64 + (((chunk & 3) ^ (((key >> 2) & 1) << 1)) << 4));
+}
+
 // The forward kernel's V tiles at D = 128 are not stored row by row: the
 // 64-byte piece of key `key` holding dims 32 m .. 32 m + 31 (chunks 4 m ..
 // 4 m + 3) lies at m * 2048 + key * 64, its chunk pairs swapped when bit 2 of
@@ -1380,7 +1389,7 @@ void attn_dq_kernel(AttnArgs a, const uint8_t *ws) {
 #pragma unroll
     for (int c0 = 0; c0 < 16 * CPR_Q; c0 += 64) {
       const int row = (c0 + lane) / CPR_Q, ch = (c0 + lane) % CPR_Q;
-      const int64_t off = (int64_t)min(r0 + row, n - 1) * (2 * D) + 16 * (ch ^ swz_key<D>(row));
+      const int64_t off = (int64_t)min(r0 + row, n - 1) * (2 * D) + 16 * (ch ^ swz_key_k<D>(row));
       dma16((const char *)Q + off, q_lds + 16 * c0);
     }
   }
@@ -1393,9 +1402,12 @@ void attn_dq_kernel(AttnArgs a, const uint8_t *ws) {
   constexpr int LPS = 2;                // loads per thread per stage (K and V)
   const char *Kb = (const char *)K, *Vb = (const char *)V;
   // the lane's chunk of every stage: row dkey of the tile, 16 bytes at dofs
+  // (D = 128: slot dslot holds key (dslot / 4) % 32, chunk 4 (dslot / 128) +
+  // (dslot % 4, its pair swapped by bit 2 of the key: piece128))
   const int dslot = wave * CPW + lane;
-  const int dkey = dslot / CPR;
-  const int dofs = 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
+  const int dkey = D == 128 ? (dslot >> 2) & 31 : dslot / CPR;
+  const int dofs = D == 128 ? 16 * (4 * (dslot >> 7) + ((dslot & 3) ^ (((dkey >> 2) & 1) << 1)))
+                            : 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
   const uint32_t kv_lds = lds_addr(&lds.kv[0][0][0]) + wave * CPW * 16;
   auto issue_stage = [&](int st, int q) {  // q = st % kRing
     if (lane < CPW) {
@@ -1422,18 +1434,22 @@ void attn_dq_kernel(AttnArgs a, const uint8_t *ws) {
   float lg = 0.f;
   // edge positions read at a wave-uniform index are wave-uniform
   auto pos_at = [&](const u32x2 *ev, int i) { return (int32_t)__builtin_amdgcn_readfirstlane(ev[i][0]); };
-  // K operand: key 16 b + qc, chunk 4 c + gq; b = 1 lies 16 rows further
+  // K operand: key 16 b + qc, chunk 4 c + gq; b = 1 lies khi bytes further
   uint32_t kofs[NC];
+  constexpr uint32_t khi = D == 128 ? 16 * 64 : 16 * 2 * D;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) kofs[c] = swz<D>(qc, 4 * c + gq);
-  // V operand (v_ds_read_b64_tr_b16): in each 16-lane group gq, lane r names
-  // the row (key 4 gq + r / 4, dims 16 db + 4 (r % 4) .. + 3), and lane i
-  // receives V[4 gq + e][16 db + i], e = 0..3; keys + 16 lie 16 rows further
+  for (int c = 0; c < NC; ++c)  // (= piece128(qc, 4 c + gq) at D = 128)
+    kofs[c] = D == 128 ? qc * 64 + ((gq ^ (((qc >> 2) & 1) << 1)) << 4) + 2048 * c : swz<D>(qc, 4 * c + gq);
+  // transposing operand (v_ds_read_b64_tr_b16): in each 16-lane group gq,
+  // lane r names the row (key 4 gq + r / 4, dims 16 db + 4 (r % 4) .. + 3),
+  // and lane i receives X[4 gq + e][16 db + i], e = 0..3; keys + 16 lie khi
+  // bytes further
   uint32_t vofs[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int dim = 16 * db + 4 * (qc & 3);
-    vofs[db] = swz<D>(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1);
+    vofs[db] = D == 128 ? piece128(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1)
+                        : swz<D>(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1);
   }
 
   // this wave's tiles are the stages [sa, sb)
@@ -1450,7 +1466,7 @@ void attn_dq_kernel(AttnArgs a, const uint8_t *ws) {
     for (int bb = 0; bb < 2; ++bb) {
       u32x4 kr[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kr[c] = *(const u32x4 *)(kt + kofs[c] + 32 * D * bb);
+      for (int c = 0; c < NC; ++c) kr[c] = *(const u32x4 *)(kt + kofs[c] + khi * bb);
       sacc[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -1556,7 +1572,7 @@ void attn_dq_kernel(AttnArgs a, const uint8_t *ws) {
     for (int bb = 0; bb < 2; ++bb) {
       u32x4 vr[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) vr[c] = *(const u32x4 *)(vt + kofs[c] + 32 * D * bb);
+      for (int c = 0; c < NC; ++c) vr[c] = *(const u32x4 *)(vt + kofs[c] + khi * bb);
       dpacc[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -1581,7 +1597,7 @@ void attn_dq_kernel(AttnArgs a, const uint8_t *ws) {
       for (int j = 0; j < NB; ++j) {
         const char *ka = kt + vofs[d0 + j];
         const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)ka);
-        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(ka + 16 * 2 * D));
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(ka + khi));
         kop[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
@@ -1608,7 +1624,7 @@ void attn_dq_kernel(AttnArgs a, const uint8_t *ws) {
       // has its fragment before slots 2, 3 take stages 2, 3
       const char *qt = (const char *)lds.kv[2][0] + wave * 32 * D;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qt + swz<D>(qc, 4 * c + gq)));
+      for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qt + swz_k<D>(qc, 4 * c + gq)));
       PLSH_WAIT_VM_LGKM0(0);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
