@@ -2025,14 +2025,20 @@ void attn_dkv_kernel(AttnArgs a, const uint8_t *ws, uint16_t *dk_out, uint16_t *
       vf[c] = __builtin_bit_cast(bf16x8, rv);
     }
   }
+  // tile operands (Q and dO tiles, D = 128: the piece layout of piece128,
+  // whose rows + 16 lie khi bytes further): 16-byte reads at kofs, the
+  // transposing reads at vofs
   uint32_t kofs[NC];
+  constexpr uint32_t khi = D == 128 ? 16 * 64 : 16 * 2 * D;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) kofs[c] = swz<D>(qc, 4 * c + gq);
+  for (int c = 0; c < NC; ++c)  // (= piece128(qc, 4 c + gq) at D = 128)
+    kofs[c] = D == 128 ? qc * 64 + ((gq ^ (((qc >> 2) & 1) << 1)) << 4) + 2048 * c : swz<D>(qc, 4 * c + gq);
   uint32_t vofs[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int dim = 16 * db + 4 * (qc & 3);
-    vofs[db] = swz<D>(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1);
+    vofs[db] = D == 128 ? piece128(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1)
+                        : swz<D>(4 * gq + (qc >> 2), dim >> 3) + ((dim & 4) << 1);
   }
   floatx4 dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -2042,8 +2048,11 @@ void attn_dkv_kernel(AttnArgs a, const uint8_t *ws, uint16_t *dk_out, uint16_t *
   u32x2 *evl = (u32x2 *)(dyn + (size_t)grp * ev_wave_bytes(s, false));
   u32x2 *evt = evl + ev_count(s);
   const int dslot = wave * CPW + lane;
-  const int dkey = dslot / CPR;
-  const int dofs = 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
+  // (D = 128: slot dslot holds row (dslot / 4) % 32, chunk 4 (dslot / 128) +
+  // (dslot % 4, its pair swapped by bit 2 of the row: piece128))
+  const int dkey = D == 128 ? (dslot >> 2) & 31 : dslot / CPR;
+  const int dofs = D == 128 ? 16 * (4 * (dslot >> 7) + ((dslot & 3) ^ (((dkey >> 2) & 1) << 1)))
+                            : 16 * ((dslot % CPR) ^ swz_key<D>(dkey));
   const uint32_t kv_lds = lds_addr(&lds.kv[0][0][0]) + wave * CPW * 16;
   const uint32_t rs_lds = lds_addr(&lds.rs[0][0]);
   auto pos_at = [&](const u32x2 *ev, int i) { return (int32_t)__builtin_amdgcn_readfirstlane(ev[i][0]); };
@@ -2132,7 +2141,7 @@ void attn_dkv_kernel(AttnArgs a, const uint8_t *ws, uint16_t *dk_out, uint16_t *
       for (int bb = 0; bb < 2; ++bb) {
         u32x4 qr[NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) qr[c] = *(const u32x4 *)(qt + kofs[c] + 32 * D * bb);
+        for (int c = 0; c < NC; ++c) qr[c] = *(const u32x4 *)(qt + kofs[c] + khi * bb);
         sacc[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NC; ++c)
@@ -2150,7 +2159,7 @@ void attn_dkv_kernel(AttnArgs a, const uint8_t *ws, uint16_t *dk_out, uint16_t *
         for (int jj = 0; jj < NB; ++jj) {
           const char *ta = tile + vofs[d0 + jj];
           const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)ta);
-          const short4_t hi2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(ta + 16 * 2 * D));
+          const short4_t hi2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(ta + khi));
           op[jj] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi2, hi2, 0, 1)),
@@ -2243,7 +2252,7 @@ void attn_dkv_kernel(AttnArgs a, const uint8_t *ws, uint16_t *dk_out, uint16_t *
       for (int bb = 0; bb < 2; ++bb) {
         u32x4 orr[NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) orr[c] = *(const u32x4 *)(dot + kofs[c] + 32 * D * bb);
+        for (int c = 0; c < NC; ++c) orr[c] = *(const u32x4 *)(dot + kofs[c] + khi * bb);
         dpacc[bb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NC; ++c)
