@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libplsh.so")
 ARCH = os.environ.get("PLSH_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-COMMON = ["-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function"]
+COMMON = ["-std=c++17", "-O3", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function"]
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-ffp-contract=fast",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -41,7 +41,7 @@ def build(verbose: bool = False) -> str:
     host_obj = os.path.join(objdir, "plsh_host.o")
     dev_obj = os.path.join(objdir, "plsh_attention.o")
     # host half: plain C++ (no HIP), strict IEEE binary64
-    _run(["g++", "-std=c++17", "-O2", "-fPIC", "-ffp-contract=off", "-Wall", "-c",
+    _run(["g++", "-std=c++17", "-O2", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off", "-Wall", "-c",
           os.path.join(CSRC, "plsh_host.cpp"), "-o", host_obj])
     _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "plsh_attention.hip"), "-o", dev_obj])
     # the device sampler: no contraction, so its draws round as the host's

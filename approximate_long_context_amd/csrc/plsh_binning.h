@@ -59,8 +59,11 @@ PLSH_HD double bin_of_r(int32_t x, double delta, double u, double rinv) {
 // arithmetic overlaps.
 PLSH_HD int32_t first_at_least(double m, int32_t lo, int32_t hi, double delta, double u, double rinv) {
   const double c = ceil(m * delta - u);
-  int32_t y = (c <= (double)lo) ? lo : (c >= (double)hi ? hi : (int32_t)c);
-  for (int it = 0; it < 4; ++it) {
+  // (a NaN guess, possible only for parameters the callers reject, skips to
+  // the bisection instead of converting NaN to an integer)
+  const bool guess = c == c;
+  int32_t y = !guess || c <= (double)lo ? lo : (c >= (double)hi ? hi : (int32_t)c);
+  for (int it = 0; it < (guess ? 4 : 0); ++it) {
     const double bl = bin_of_r(y > lo ? y - 1 : lo, delta, u, rinv);
     const double by = bin_of_r(y < hi ? y : lo, delta, u, rinv);
     if (y > lo && bl >= m) { --y; continue; }

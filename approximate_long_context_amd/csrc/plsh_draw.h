@@ -51,6 +51,14 @@ PLSH_DRAW_HD uint64_t splitmix64_at(uint64_t seed, uint64_t i) {
 PLSH_DRAW_HD double unit_open(uint64_t z) { return ((double)(z >> 11) + 0.5) * 0x1p-53; }
 PLSH_DRAW_HD double unit_halfopen(uint64_t z) { return (double)(z >> 11) * 0x1p-53; }
 
+// The scales both samplers accept.  A pitch is sigma times e = -(ln U1 +
+// ln U2), and with U1, U2 in [2^-54, 1 - 2^-54] e lies in [2^-53, 75]: for
+// sigma in [kSigmaMin, kSigmaMax] every pitch is a finite normal double, its
+// bins of positions below 2^31 stay finite, and u = delta U3 < delta.
+constexpr double kSigmaMin = 1e-280;
+constexpr double kSigmaMax = 1e300;
+PLSH_DRAW_HD bool sigma_in_range(double sigma) { return sigma >= kSigmaMin && sigma <= kSigmaMax; }
+
 // one stream position per (head, sample, draw j < 4), independent of s
 PLSH_DRAW_HD uint64_t draw_index(uint64_t head, uint64_t sample, uint64_t j) {
   return ((head << 32) | sample) * 4 + j;

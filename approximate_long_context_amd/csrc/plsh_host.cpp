@@ -71,8 +71,9 @@ extern "C" plsh_status plsh_sample_tables(uint64_t seed, int32_t n, int32_t head
   if (starts && starts_capacity < 0)
     return fail(PLSH_ERR_ARG, "plsh_sample_tables: negative starts_capacity");
   for (int32_t h = 0; h < heads; ++h)
-    if (!finite_pos(sigma[h]))
-      return fail(PLSH_ERR_ARG, "plsh_sample_tables: sigma[%d] must be finite and > 0", h);
+    if (!draw::sigma_in_range(sigma[h]))
+      return fail(PLSH_ERR_ARG, "plsh_sample_tables: sigma[%d] = %g outside [%g, %g]", h, sigma[h],
+                  draw::kSigmaMin, draw::kSigmaMax);
 
   const int64_t rows = (int64_t)heads * s;
   std::vector<int32_t> all;
@@ -84,6 +85,11 @@ extern "C" plsh_status plsh_sample_tables(uint64_t seed, int32_t n, int32_t head
       double delta, u;  // Erlang-2 = Gamma(2, sigma) pitch, offset in [0, delta)
       draw::hash_params(seed, (uint64_t)h, (uint64_t)k, sg, &delta, &u);
       const int64_t r = (int64_t)h * s + k;
+      // (holds for every sigma in range; checked so that no draw can reach
+      // the scan otherwise)
+      if (!(isnormal(delta) && delta > 0.0 && u >= 0.0 && u < delta))
+        return fail(PLSH_ERR_ARG, "plsh_sample_tables: sigma[%d] drew an unusable pitch %g (sample %d)", h,
+                    delta, k);
       params[2 * r] = delta;
       params[2 * r + 1] = u;
       one.clear();
@@ -115,9 +121,11 @@ extern "C" plsh_status plsh_build_tables(int32_t n, int32_t heads, int32_t s, co
   const int64_t rows = (int64_t)heads * s;
   for (int64_t r = 0; r < rows; ++r) {
     const double delta = params[2 * r], u = params[2 * r + 1];
-    if (!finite_pos(delta) || !(u >= 0.0) || !(u < delta))
-      return fail(PLSH_ERR_ARG, "plsh_build_tables: row %lld: need delta > 0 finite and 0 <= u < delta",
-                  (long long)r);
+    if (!finite_pos(delta) || !isnormal(delta) || !(u >= 0.0) || !(u < delta) ||
+        !isfinite(((double)n + u) / delta))
+      return fail(PLSH_ERR_ARG,
+                  "plsh_build_tables: row %lld: need delta > 0 finite and normal, 0 <= u < delta, and finite "
+                  "bins (n + u) / delta", (long long)r);
   }
   std::vector<int32_t> all, one;
   offsets[0] = 0;

@@ -51,8 +51,9 @@ extern "C" plsh_status plsh_sample_params_device(uint64_t seed, int32_t heads, c
     return fail(PLSH_ERR_UNSUPPORTED, "%s: heads = %d exceeds %d", who, heads, dev::kMaxSampleHeads);
   if (s > kMaxSamples) return fail(PLSH_ERR_UNSUPPORTED, "%s: s = %d exceeds %d", who, s, kMaxSamples);
   for (int32_t h = 0; h < heads; ++h)
-    if (!(isfinite(sigma[h]) && sigma[h] > 0.0))
-      return fail(PLSH_ERR_ARG, "%s: sigma[%d] must be finite and > 0", who, h);
+    if (!draw::sigma_in_range(sigma[h]))
+      return fail(PLSH_ERR_ARG, "%s: sigma[%d] = %g outside [%g, %g]", who, h, sigma[h], draw::kSigmaMin,
+                  draw::kSigmaMax);
   if ((uintptr_t)params & 15u) return fail(PLSH_ERR_ARG, "%s: params must be 16-byte aligned", who);
   plsh_status st = have_device(who);
   if (st != PLSH_OK) return st;

@@ -156,6 +156,8 @@ def sample_params_device(seed: int, sigma: Sequence[float], s: int, device,
                          stream: Optional[int] = None) -> torch.Tensor:
     """plsh_sample_params_device: float64 [heads * s, 2] (delta, u) drawn on
     the GPU, bit for bit those of sample_tables(seed, ...)."""
+    if torch.device(device).type != "cuda":
+        raise PlshError(PLSH_ERR_ARG, f"device must be a CUDA device, not {device}")
     sig = np.ascontiguousarray(sigma, dtype=np.float64)
     params = torch.empty((sig.size * s, 2), dtype=torch.float64, device=device)
     if stream is None:
@@ -219,15 +221,50 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise PlshError(PLSH_ERR_UNSUPPORTED, f"dtype {t.dtype} not supported")
 
 
-def _attention(fn, q, k, v, sigma, s, tables: DeviceTables, causal, out, stream, ws=None):
-    for name, x in (("q", q), ("k", k), ("v", v)):
+def _require_device_tables(tables, device: torch.device) -> None:
+    """The kernels dereference params on the device: only a DeviceTables whose
+    params is a contiguous float64 [heads*s, 2] tensor on `device` may reach
+    the library (a host Tables would hand it host addresses)."""
+    if not isinstance(tables, DeviceTables):
+        raise PlshError(PLSH_ERR_ARG, "tables must be a DeviceTables (Tables.to(device)), "
+                                      f"not {type(tables).__name__}")
+    p = tables.params
+    if not isinstance(p, torch.Tensor) or p.device != device or p.dtype != torch.float64 or \
+            not p.is_contiguous() or tuple(p.shape) != (tables.heads * tables.s, 2):
+        raise PlshError(PLSH_ERR_ARG, "tables.params must be a contiguous float64 "
+                                      f"[heads*s, 2] tensor on {device}")
+
+
+def _require_cuda(device: Optional[torch.device] = None, **tensors) -> torch.device:
+    """Every tensor is a contiguous CUDA tensor on one device (the first's,
+    or `device`); returns that device."""
+    for name, x in tensors.items():
+        if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+            raise PlshError(PLSH_ERR_ARG, f"{name} must be a CUDA tensor")
+        if device is None:
+            device = x.device
+        elif x.device != device:
+            raise PlshError(PLSH_ERR_ARG, f"{name} is on {x.device}, expected {device}")
         if not x.is_contiguous():
             raise PlshError(PLSH_ERR_ARG, f"{name} must be contiguous")
+    return device
+
+
+def _require_like(name: str, x: torch.Tensor, ref: torch.Tensor) -> None:
+    if tuple(x.shape) != tuple(ref.shape) or x.dtype != ref.dtype:
+        raise PlshError(PLSH_ERR_ARG, f"{name} must have shape {tuple(ref.shape)} and dtype {ref.dtype}")
+
+
+def _attention(fn, q, k, v, sigma, s, tables: DeviceTables, causal, out, stream, ws=None):
+    dev = _require_cuda(q=q, k=k, v=v)
+    _require_device_tables(tables, dev)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or q.dtype != k.dtype or q.dtype != v.dtype:
         raise PlshError(PLSH_ERR_ARG, "q [B,H,n,d], k/v [B,Hkv,n,d] with one dtype expected")
     B, H, n, d = q.shape
     if out is None:
         out = torch.empty_like(q)
+    _require_cuda(dev, out=out)
+    _require_like("out", out, q)
     sig = np.ascontiguousarray(sigma, dtype=np.float64)
     if sig.size != H:
         raise PlshError(PLSH_ERR_ARG, "sigma must have one entry per query head")
@@ -302,8 +339,9 @@ def attention_with_lse(q, k, v, sigma, s, tables: DeviceTables, causal: bool = F
     shape = (B, H, (n + 31) // 32 * 32)
     if lse2 is None:
         lse2 = torch.empty(shape, dtype=torch.float32, device=q.device)
-    elif lse2.dtype != torch.float32 or tuple(lse2.shape) != shape or not lse2.is_contiguous():
-        raise PlshError(PLSH_ERR_ARG, "lse2 must be a contiguous float32 [B, H, ceil32(n)] tensor")
+    elif lse2.dtype != torch.float32 or tuple(lse2.shape) != shape or not lse2.is_contiguous() or \
+            lse2.device != q.device:
+        raise PlshError(PLSH_ERR_ARG, "lse2 must be a contiguous float32 [B, H, ceil32(n)] tensor on q's device")
     if stream is None:
         need = workspace_size(n, H, s, q.dtype)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -325,10 +363,10 @@ def attention_backward(q, k, v, dout, sigma, s, tables: DeviceTables, causal: bo
     lse2 (attention_with_lse), plsh_alibi_attention_backward_saved."""
     if (out is None) != (lse2 is None):
         raise PlshError(PLSH_ERR_ARG, "out and lse2 go together")
-    for name, x in (("q", q), ("k", k), ("v", v), ("dout", dout)) + \
-            ((("out", out), ("lse2", lse2)) if out is not None else ()):
-        if not x.is_contiguous():
-            raise PlshError(PLSH_ERR_ARG, f"{name} must be contiguous")
+    dev = _require_cuda(q=q, k=k, v=v, dout=dout)
+    if out is not None:
+        _require_cuda(dev, out=out, lse2=lse2)
+    _require_device_tables(tables, dev)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or dout.shape != q.shape or \
             len({q.dtype, k.dtype, v.dtype, dout.dtype}) != 1:
         raise PlshError(PLSH_ERR_ARG, "q/dout [B,H,n,d], k/v [B,Hkv,n,d] with one dtype expected")
@@ -361,14 +399,14 @@ def exact_alibi_attention(q, k, v, sigma, causal: bool = False, out: Optional[to
                           stream: Optional[int] = None) -> torch.Tensor:
     """plsh_exact_alibi_attention (dense exact ALiBi, bf16) on the current
     stream: q [B,H,n,d], k/v [B,Hkv,n,d]."""
-    for name, x in (("q", q), ("k", k), ("v", v)):
-        if not x.is_contiguous():
-            raise PlshError(PLSH_ERR_ARG, f"{name} must be contiguous")
+    dev = _require_cuda(q=q, k=k, v=v)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or q.dtype != k.dtype or q.dtype != v.dtype:
         raise PlshError(PLSH_ERR_ARG, "q [B,H,n,d], k/v [B,Hkv,n,d] with one dtype expected")
     B, H, n, d = q.shape
     if out is None:
         out = torch.empty_like(q)
+    _require_cuda(dev, out=out)
+    _require_like("out", out, q)
     sig = np.ascontiguousarray(sigma, dtype=np.float64)
     if sig.size != H:
         raise PlshError(PLSH_ERR_ARG, "sigma must have one entry per query head")
@@ -389,6 +427,9 @@ def attention_reference(q, k, v, sigma, s, tables: DeviceTables, causal: bool = 
 
 def debug_block_intervals(tables: DeviceTables, stream: Optional[int] = None) -> torch.Tensor:
     """int32 [heads*s, n, 2] (lo, hi) recomputed on the GPU."""
+    if not isinstance(tables, DeviceTables) or tables.params.device.type != "cuda":
+        raise PlshError(PLSH_ERR_ARG, "tables must be a DeviceTables with params on the GPU")
+    _require_device_tables(tables, tables.params.device)
     lohi = torch.empty((tables.heads * tables.s, tables.n, 2), dtype=torch.int32,
                        device=tables.params.device)
     if stream is None:

@@ -17,9 +17,14 @@
  * with C the optional causal mask and logits q.k taken with scale 1.
  *
  * Conventions shared by every entry point:
- *   - Every call returns a plsh_status; nothing throws across the ABI.  On a
- *     non-OK status no device work has been enqueued and plsh_last_error()
- *     describes the failure.
+ *   - Every call returns a plsh_status; nothing throws across the ABI, and
+ *     plsh_last_error() describes a non-OK status.  PLSH_ERR_ARG,
+ *     PLSH_ERR_TABLE, PLSH_ERR_UNSUPPORTED and PLSH_ERR_CAPACITY come from the
+ *     argument checks, before any device work is enqueued.  PLSH_ERR_HIP can
+ *     come after part of a call's work is on the stream (a launch that fails
+ *     after the block-edge pre-pass, or after some of the unfused form's
+ *     per-sample passes): the outputs are then undefined, and the work
+ *     already enqueued still runs and reads the buffers.
  *   - Host pointers are read during the call only; the library keeps no
  *     reference to any caller buffer after it returns (device work enqueued on
  *     `stream` reads device buffers until it completes: they must stay alive
@@ -38,6 +43,14 @@
 #define PLSH_H
 
 #include <stdint.h>
+
+/* The library is built with hidden visibility: the functions declared here
+ * are its only exported symbols. */
+#if defined(__GNUC__) || defined(__clang__)
+#define PLSH_API __attribute__((visibility("default")))
+#else
+#define PLSH_API
+#endif
 
 #ifdef __cplusplus
 extern "C" {
@@ -86,7 +99,8 @@ typedef struct {
  * in (seed, n, sigma[], s); sample k of head h does not depend on s.
  *   seed            generator key
  *   n               sequence length, >= 1
- *   heads, sigma    sigma[heads] (host), each finite and > 0
+ *   heads, sigma    sigma[heads] (host), each in [1e-280, 1e300] (so that
+ *                   every pitch is a finite normal double with finite bins)
  *   s               samples per head, >= 1
  *   params          out, host [heads*s][2]
  *   offsets         out, host [heads*s + 1]
@@ -97,7 +111,7 @@ typedef struct {
  * (starts == NULL) or PLSH_ERR_CAPACITY (capacity too small); a second call
  * with a large enough buffer fills starts.  Needs no GPU.
  */
-plsh_status plsh_sample_tables(uint64_t seed, int32_t n, int32_t heads, const double *sigma,
+PLSH_API plsh_status plsh_sample_tables(uint64_t seed, int32_t n, int32_t heads, const double *sigma,
                                int32_t s, double *params, int32_t *offsets, int32_t *starts,
                                int64_t starts_capacity, int64_t *starts_needed);
 
@@ -112,10 +126,11 @@ plsh_status plsh_sample_tables(uint64_t seed, int32_t n, int32_t heads, const do
  * starts == NULL it fills offsets ([heads*s + 1]) and *starts_needed; the
  * second call also fills starts.
  * Errors: PLSH_ERR_ARG (null pointer, n/heads/s < 1, a row without
- * delta > 0 finite and 0 <= u < delta), PLSH_ERR_CAPACITY (starts_capacity
+ * delta > 0 finite and normal, 0 <= u < delta and (n + u) / delta finite),
+ * PLSH_ERR_CAPACITY (starts_capacity
  * too small, or more than 2^31 - 1 entries).
  */
-plsh_status plsh_build_tables(int32_t n, int32_t heads, int32_t s, const double *params,
+PLSH_API plsh_status plsh_build_tables(int32_t n, int32_t heads, int32_t s, const double *params,
                               int32_t *offsets, int32_t *starts, int64_t starts_capacity,
                               int64_t *starts_needed);
 
@@ -127,7 +142,7 @@ plsh_status plsh_build_tables(int32_t n, int32_t heads, int32_t s, const double 
  * contiguous and non-overlapping).  Returns PLSH_ERR_TABLE on the first
  * violation.  Needs no GPU.
  */
-plsh_status plsh_validate_tables(const plsh_tables *host_tables);
+PLSH_API plsh_status plsh_validate_tables(const plsh_tables *host_tables);
 
 /*
  * plsh_count_work -- work counts of one batch element, summed over heads
@@ -139,7 +154,7 @@ plsh_status plsh_validate_tables(const plsh_tables *host_tables);
  *                    or [0, i] when causal: the nonzeros of M~ o C.
  * Needs no GPU.
  */
-plsh_status plsh_count_work(const plsh_tables *host_tables, int32_t causal,
+PLSH_API plsh_status plsh_count_work(const plsh_tables *host_tables, int32_t causal,
                             int64_t *pairs_alg, int64_t *pairs_distinct);
 
 /*
@@ -176,7 +191,7 @@ plsh_status plsh_count_work(const plsh_tables *host_tables, int32_t causal,
  * allocation failure).  Execution
  * faults surface at the caller's next synchronisation.
  */
-plsh_status plsh_alibi_attention(const void *q, const void *k, const void *v, void *out,
+PLSH_API plsh_status plsh_alibi_attention(const void *q, const void *k, const void *v, void *out,
                                  int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
                                  int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
                                  const plsh_tables *boundaries, int32_t causal,
@@ -192,7 +207,7 @@ plsh_status plsh_alibi_attention(const void *q, const void *k, const void *v, vo
  * Errors: PLSH_ERR_ARG (null pointer, n, heads or s < 1),
  * PLSH_ERR_UNSUPPORTED (unknown dtype).
  */
-plsh_status plsh_attention_workspace_size(int32_t n, int32_t heads, int32_t s, plsh_dtype dtype,
+PLSH_API plsh_status plsh_attention_workspace_size(int32_t n, int32_t heads, int32_t s, plsh_dtype dtype,
                                           int64_t *bytes);
 
 /*
@@ -213,7 +228,7 @@ plsh_status plsh_attention_workspace_size(int32_t n, int32_t heads, int32_t s, p
  * smaller than needed) and PLSH_ERR_ARG (null or misaligned workspace, or one
  * overlapping q, k, v or out).
  */
-plsh_status plsh_alibi_attention_ws(const void *q, const void *k, const void *v, void *out,
+PLSH_API plsh_status plsh_alibi_attention_ws(const void *q, const void *k, const void *v, void *out,
                                     int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
                                     int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
                                     const plsh_tables *boundaries, int32_t causal, void *workspace,
@@ -229,7 +244,8 @@ plsh_status plsh_alibi_attention_ws(const void *q, const void *k, const void *v,
  * training step on the device: the attention entry points read only params
  * (offsets and starts of a plsh_tables may be null there).
  *   seed    generator seed (one per step for per-step resampling)
- *   heads   1 .. 128; sigma HOST double [heads], finite and > 0
+ *   heads   1 .. 128; sigma HOST double [heads], each in [1e-280, 1e300]
+ *           (the range plsh_sample_tables accepts)
  *   s       1 .. 255 samples per head
  *   params  DEVICE double [heads*s][2] output, 16-byte aligned
  *   stream  HIP stream for the launch (one kernel, one thread per row)
@@ -237,7 +253,7 @@ plsh_status plsh_alibi_attention_ws(const void *q, const void *k, const void *v,
  * PLSH_ERR_UNSUPPORTED (heads > 128, s > 255), PLSH_ERR_HIP (no device,
  * launch error).
  */
-plsh_status plsh_sample_params_device(uint64_t seed, int32_t heads, const double *sigma, int32_t s,
+PLSH_API plsh_status plsh_sample_params_device(uint64_t seed, int32_t heads, const double *sigma, int32_t s,
                                       double *params, plsh_stream_t stream);
 
 /*
@@ -248,8 +264,28 @@ plsh_status plsh_sample_params_device(uint64_t seed, int32_t heads, const double
  * boundaries as for plsh_alibi_attention (params on the device).  Test aid:
  * the result must equal the host table bit for bit.
  */
-plsh_status plsh_debug_block_intervals(const plsh_tables *boundaries, int32_t *lohi,
+PLSH_API plsh_status plsh_debug_block_intervals(const plsh_tables *boundaries, int32_t *lohi,
                                        plsh_stream_t stream);
+
+/*
+ * plsh_debug_attention_reference -- the estimator of plsh_alibi_attention
+ * (Methodology §3, Theorem 2.2: the s block-local attentions fused as one
+ * ratio of sums with weights c_ij = #{k : j in B_k(i)}) through a second,
+ * independent GPU formulation: one wave per query row, the row's s block
+ * intervals recomputed from (delta, u) with the binary64 predicate of
+ * plsh_debug_block_intervals, c_ij counted key by key, logits and weights in
+ * fp32 (exp, no matrix cores), P rounded to bf16 for the value sum on the
+ * bf16 path as in the MFMA kernel.  Test aid: the same estimate computed
+ * another way, and the path every fp32 call of plsh_alibi_attention takes.
+ * Arguments, layouts and errors as plsh_alibi_attention (bf16 or fp32,
+ * d 64 or 128, s <= 255); it launches one kernel and allocates no device
+ * memory.
+ */
+PLSH_API plsh_status plsh_debug_attention_reference(const void *q, const void *k, const void *v, void *out,
+                                           int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                           int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                           const plsh_tables *boundaries, int32_t causal,
+                                           plsh_stream_t stream);
 
 /*
  * plsh_alibi_attention_walk -- the same estimate as plsh_alibi_attention,
@@ -268,7 +304,7 @@ plsh_status plsh_debug_block_intervals(const plsh_tables *boundaries, int32_t *l
  * Errors: as plsh_alibi_attention, and PLSH_ERR_UNSUPPORTED for fp32 or when
  * heads*s*ceil(n/32) exceeds 2^31.
  */
-plsh_status plsh_alibi_attention_walk(const void *q, const void *k, const void *v, void *out,
+PLSH_API plsh_status plsh_alibi_attention_walk(const void *q, const void *k, const void *v, void *out,
                                       int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
                                       int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
                                       const plsh_tables *boundaries, int32_t causal,
@@ -301,7 +337,7 @@ plsh_status plsh_alibi_attention_walk(const void *q, const void *k, const void *
  * Errors: as plsh_alibi_attention (null dout, dq, dk or dv, misalignment and
  * aliasing: PLSH_ERR_ARG), and PLSH_ERR_UNSUPPORTED for fp32 or s > 124.
  */
-plsh_status plsh_alibi_attention_backward(const void *q, const void *k, const void *v,
+PLSH_API plsh_status plsh_alibi_attention_backward(const void *q, const void *k, const void *v,
                                           const void *dout, void *dq, void *dk, void *dv,
                                           int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
                                           int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
@@ -325,7 +361,7 @@ plsh_status plsh_alibi_attention_backward(const void *q, const void *k, const vo
  * overlapping lse2; misaligned or overlapping workspace), PLSH_ERR_CAPACITY
  * (workspace too small) and PLSH_ERR_UNSUPPORTED (fp32 or s > 124).
  */
-plsh_status plsh_alibi_attention_lse(const void *q, const void *k, const void *v, void *out,
+PLSH_API plsh_status plsh_alibi_attention_lse(const void *q, const void *k, const void *v, void *out,
                                      int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
                                      int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
                                      const plsh_tables *boundaries, int32_t causal, float *lse2,
@@ -352,7 +388,7 @@ plsh_status plsh_alibi_attention_lse(const void *q, const void *k, const void *v
  * Errors: as plsh_alibi_attention_backward, plus PLSH_ERR_ARG for a null or
  * misaligned out or lse2.
  */
-plsh_status plsh_alibi_attention_backward_saved(const void *q, const void *k, const void *v,
+PLSH_API plsh_status plsh_alibi_attention_backward_saved(const void *q, const void *k, const void *v,
                                                 const void *out, const float *lse2,
                                                 const void *dout, void *dq, void *dk, void *dv,
                                                 int32_t batch, int32_t n, int32_t heads,
@@ -374,7 +410,7 @@ plsh_status plsh_alibi_attention_backward_saved(const void *q, const void *k, co
  * within the call, plus each pass's pre-pass workspace.
  * Errors: as plsh_alibi_attention, and PLSH_ERR_UNSUPPORTED for fp32.
  */
-plsh_status plsh_alibi_attention_unfused(const void *q, const void *k, const void *v, void *out,
+PLSH_API plsh_status plsh_alibi_attention_unfused(const void *q, const void *k, const void *v, void *out,
                                          int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
                                          int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
                                          const plsh_tables *boundaries, int32_t causal,
@@ -396,7 +432,7 @@ plsh_status plsh_alibi_attention_unfused(const void *q, const void *k, const voi
  * misalignment), PLSH_ERR_UNSUPPORTED (dtype not bf16, d not 64/128,
  * batch*heads*n*d >= 2^31, heads > 128), PLSH_ERR_HIP (launch error).
  */
-plsh_status plsh_exact_alibi_attention(const void *q, const void *k, const void *v, void *out,
+PLSH_API plsh_status plsh_exact_alibi_attention(const void *q, const void *k, const void *v, void *out,
                                        int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
                                        int32_t d, plsh_dtype dtype, const double *sigma,
                                        int32_t causal, plsh_stream_t stream);
@@ -411,7 +447,7 @@ plsh_status plsh_exact_alibi_attention(const void *q, const void *k, const void 
  * stops recording.  Either call discards pairs not yet read.  The events are
  * created on first use and kept for reuse by the thread.
  */
-plsh_status plsh_kernel_timer(int32_t enable);
+PLSH_API plsh_status plsh_kernel_timer(int32_t enable);
 
 /*
  * plsh_kernel_timer_read -- waits for the recorded pairs of this thread,
@@ -419,11 +455,11 @@ plsh_status plsh_kernel_timer(int32_t enable);
  * *total_ms, and discards them.  PLSH_ERR_ARG on null pointers, PLSH_ERR_HIP
  * if an event cannot be read.
  */
-plsh_status plsh_kernel_timer_read(int32_t *launches, double *total_ms);
+PLSH_API plsh_status plsh_kernel_timer_read(int32_t *launches, double *total_ms);
 
 /* Thread-local, NUL-terminated description of the last non-OK status of this
  * thread ("" if none).  Valid until the thread's next plsh_* call. */
-const char *plsh_last_error(void);
+PLSH_API const char *plsh_last_error(void);
 
 #ifdef __cplusplus
 }

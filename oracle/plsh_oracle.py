@@ -40,7 +40,8 @@ Parity status per function:
                            error-bound inequality, convex hull)
   lsh_estimate_multiplicity pinned (brute force)
   lsh_row_log_normaliser   pinned (brute-force row sums of A o (sum_k M) o C)
-  mask_mean / matrix_errors pinned (variance identity, 1/sqrt(s) slope)
+  mask_mean / matrix_errors pinned (variance identity, 1/sqrt(s) slope,
+                           hand-worked spectral / max / Frobenius norms)
   work_counts              pinned (brute-force pair enumeration)
   lsh_estimate_grad /      pinned (central finite differences of the
   lsh_grad_rows /          block-walk lsh_estimate; subsets against the

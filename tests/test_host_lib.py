@@ -31,7 +31,9 @@ def _declared():
     return sorted(set(re.findall(r"\b(plsh_[a-z_]+)\s*\(", src)))
 
 
-def test_library_exports_every_declared_symbol():
+def test_library_exports_exactly_the_declared_symbols():
+    """The header's functions are exported, and nothing else is: the
+    library's dynamic text symbols equal the declarations, both ways."""
     names = _declared()
     assert "plsh_alibi_attention" in names and "plsh_last_error" in names
     L = plsh.lib()
@@ -39,8 +41,9 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, nm), nm
     dyn = subprocess.run(["nm", "-D", "--defined-only", plsh.LIB_PATH], capture_output=True,
                          text=True).stdout
-    for nm in names:
-        assert re.search(rf"\bT {nm}\b", dyn), nm
+    exported = sorted(m.group(1) for m in re.finditer(r"^[0-9a-f]+ T (\S+)$", dyn, flags=re.M))
+    assert exported == names
+    assert sorted(plsh.EXPORTED) == names
 
 
 @pytest.mark.parametrize("seed,n,sigma,s", [
@@ -85,11 +88,19 @@ def test_two_call_protocol_and_capacity():
     assert st == plsh.PLSH_ERR_CAPACITY and b"capacity" in L.plsh_last_error()
 
 
-@pytest.mark.parametrize("bad", [float("nan"), 0.0, -1.0, float("inf")])
+@pytest.mark.parametrize("bad", [float("nan"), 0.0, -1.0, float("inf"), 1e308, 1e-310, 5e300, 1e-285])
 def test_sampler_rejects_bad_sigma(bad):
+    """Scales outside [1e-280, 1e300] could draw an infinite or subnormal
+    pitch: refused (an infinite pitch once sent the scan into a loop)."""
     with pytest.raises(plsh.PlshError) as e:
         plsh.sample_tables(0, 10, [1.0, bad], 2)
     assert e.value.status == plsh.PLSH_ERR_ARG
+
+
+def test_sampler_accepts_the_range_ends():
+    t = plsh.sample_tables(3, 50, [1e-280, 1e300], 4)
+    assert np.all(np.isfinite(t.params)) and np.all(t.params[:, 0] > 0)
+    plsh.validate_tables(t)
 
 
 def test_sampler_rejects_bad_sizes():
@@ -420,6 +431,8 @@ def _sample_dev_call(seed=1, heads=4, sigma=(2.0, 4.0, 8.0, 16.0), s=3, params=0
     (dict(s=256), plsh.PLSH_ERR_UNSUPPORTED),
     (dict(sigma=(2.0, float("inf"), 8.0, 16.0)), plsh.PLSH_ERR_ARG),
     (dict(sigma=(2.0, -1.0, 8.0, 16.0)), plsh.PLSH_ERR_ARG),
+    (dict(sigma=(2.0, 1e308, 8.0, 16.0)), plsh.PLSH_ERR_ARG),
+    (dict(sigma=(2.0, 1e-310, 8.0, 16.0)), plsh.PLSH_ERR_ARG),
     (dict(params=0x10008), plsh.PLSH_ERR_ARG),
 ])
 def test_device_sampler_argument_errors(over, status):
@@ -485,7 +498,7 @@ def test_build_tables_reproduces_the_sampler():
 
 
 @pytest.mark.parametrize("row", [(0.0, 0.0), (-1.0, 0.0), (float("nan"), 0.0), (4.0, -0.5), (4.0, 4.0),
-                                 (float("inf"), 0.0)])
+                                 (float("inf"), 0.0), (1e-310, 0.0), (2.5e-308, 0.0)])
 def test_build_tables_rejects_bad_rows(row):
     params = np.array([[8.0, 1.0], row], dtype=np.float64)
     with pytest.raises(plsh.PlshError) as e:
@@ -504,3 +517,60 @@ def test_build_tables_capacity_protocol():
     small_buf = np.empty(5, dtype=np.int32)
     assert L.plsh_build_tables(30, 1, 1, params.ctypes.data, offsets.ctypes.data, small_buf.ctypes.data, 5,
                                ctypes.byref(need)) == plsh.PLSH_ERR_CAPACITY
+
+
+# ------------------------------------------------ binding argument checks ---
+def _cpu_qkv(n=64, d=64, H=2, Hkv=1):
+    import torch
+    q = torch.zeros((1, H, n, d), dtype=torch.bfloat16)
+    k = torch.zeros((1, Hkv, n, d), dtype=torch.bfloat16)
+    return q, k, k.clone()
+
+
+def test_binding_rejects_host_tables_before_any_call(monkeypatch):
+    """A host Tables holds host addresses; the binding refuses it (and CPU
+    tensors) before the library is called, so nothing is launched."""
+    q, k, v = _cpu_qkv()
+    t = plsh.sample_tables(0, 64, [4.0, 8.0], 3)
+    real = plsh.lib()
+    calls = []
+
+    class Recorder:   # forwards the host-only size query, records anything else
+        def __getattr__(self, name):
+            if name == "plsh_attention_workspace_size":
+                return getattr(real, name)
+            return lambda *a: calls.append(name) or 0
+    monkeypatch.setattr(plsh, "lib", lambda: Recorder())
+    for fn in (plsh.attention, plsh.attention_library_workspace, plsh.attention_unfused,
+               plsh.attention_walk, plsh.attention_reference, plsh.attention_with_lse):
+        with pytest.raises(plsh.PlshError) as e:
+            fn(q, k, v, [4.0, 8.0], 3, t, causal=True)
+        assert "CUDA" in str(e.value) or "DeviceTables" in str(e.value)
+    with pytest.raises(plsh.PlshError):
+        plsh.attention_backward(q, k, v, q.clone(), [4.0, 8.0], 3, t, causal=True)
+    with pytest.raises(plsh.PlshError):
+        plsh.exact_alibi_attention(q, k, v, [4.0, 8.0])
+    with pytest.raises(plsh.PlshError):
+        plsh.debug_block_intervals(t)
+    with pytest.raises(plsh.PlshError):
+        plsh.sample_params_device(0, [4.0], 3, "cpu")
+    assert calls == []
+
+
+def test_binding_tables_check():
+    """_require_device_tables: a host Tables, params of the wrong dtype,
+    shape or device are refused."""
+    import torch
+    t = plsh.sample_tables(0, 64, [4.0, 8.0], 3)
+    with pytest.raises(plsh.PlshError, match="DeviceTables"):
+        plsh._require_device_tables(t, torch.device("cpu"))
+    dt = t.to("cpu")   # a DeviceTables whose tensors happen to be on the CPU
+    plsh._require_device_tables(dt, torch.device("cpu"))
+    bad = plsh.DeviceTables(dt.n, dt.heads, dt.s, dt.params.float(), dt.offsets, dt.starts)
+    with pytest.raises(plsh.PlshError, match="float64"):
+        plsh._require_device_tables(bad, torch.device("cpu"))
+    bad = plsh.DeviceTables(dt.n, dt.heads, dt.s, dt.params[:-1], dt.offsets, dt.starts)
+    with pytest.raises(plsh.PlshError):
+        plsh._require_device_tables(bad, torch.device("cpu"))
+    with pytest.raises(plsh.PlshError):
+        plsh._require_device_tables(dt, torch.device("cuda", 0))

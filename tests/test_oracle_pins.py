@@ -62,6 +62,41 @@ def test_golden_worked_example():
         assert (alg, distinct) == (g[mode]["pairs_alg"], g[mode]["pairs_distinct"])
 
 
+def _closed_form(f):
+    """Value of one of the golden file's closed forms."""
+    p, r, q = f.get("p", 0), f.get("r", 0), f["q"]
+    return {"(p + sqrt(r)) / q": (p + math.sqrt(r)) / q,
+            "-(p + sqrt(r)) / q": -(p + math.sqrt(r)) / q,
+            "(sqrt(r) - p) / q": (math.sqrt(r) - p) / q,
+            "(p - sqrt(r)) / q": (p - math.sqrt(r)) / q,
+            "p / q": p / q, "-p / q": -p / q,
+            "sqrt(r / q)": math.sqrt(r / q)}[f["form"]]
+
+
+def test_golden_matrix_errors():
+    """Hand-worked spectral, max and Frobenius norms of L* - M~ (Methodology
+    §1 masks, §2 Theorem 2.1 norms): one case whose dominant eigenvalue is
+    negative and one whose is positive, so that a signed eigenvalue, a
+    missing absolute value or a Frobenius norm in place of the spectral one
+    all miss a value."""
+    g = json.load(open(os.path.join(GOLDEN, "matrix_errors.json")))
+    n = g["n"]
+    Ls = orc.alibi_matrix(n, 1.0 / math.log(2.0))
+    np.testing.assert_allclose(Ls, [[1, .5, .25], [.5, 1, .5], [.25, .5, 1]], rtol=0, atol=1e-15)
+    for case in g["cases"]:
+        starts = [orc.block_starts(n, hs["delta"], hs["u"]) for hs in case["hashes"]]
+        Mt = orc.mask_mean(n, starts)
+        want_m = np.array([[float(Fraction(x)) for x in row] for row in case["mtilde"]])
+        assert np.array_equal(Mt, want_m), case["name"]
+        e = orc.matrix_errors(Ls, Mt)
+        assert e["max"] == pytest.approx(float(Fraction(case["max"])), abs=1e-15)
+        assert e["spectral"] == pytest.approx(_closed_form(case["spectral"]), abs=1e-14)
+        assert e["fro"] == pytest.approx(_closed_form(case["fro"]), abs=1e-14)
+        # the eigenvalues of the derivation (sorted) are those of L* - M~
+        ev = sorted(_closed_form(f) for f in case["eigenvalues"])
+        np.testing.assert_allclose(np.linalg.eigvalsh(Ls - Mt), ev, rtol=0, atol=1e-14)
+
+
 # ------------------------------------------------------------------- P1 ---
 @pytest.mark.parametrize("sigma", [1.0, 16.0, 64.0])
 def test_p1_pitch_law_reproduces_laplacian_kernel(sigma):
@@ -102,7 +137,7 @@ def test_p2_unbiased_mean_and_variance_identity():
     for r in range(R):
         _, tabs = _tables(1000 + r, [sigma], s, n)
         Mt = orc.mask_mean(n, tabs[0])
-        fro2[r] = ((Mt - Ls) ** 2).sum()
+        fro2[r] = orc.matrix_errors(Ls, Mt)["fro"] ** 2
         pooled += Mt
     pooled /= R
     expect = (Ls * (1 - Ls)).sum() / s
