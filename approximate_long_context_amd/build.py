@@ -44,12 +44,14 @@ def build(verbose: bool = False) -> str:
     _run(["g++", "-std=c++17", "-O2", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off", "-Wall", "-c",
           os.path.join(CSRC, "plsh_host.cpp"), "-o", host_obj])
     _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "plsh_attention.hip"), "-o", dev_obj])
+    fwd_obj = os.path.join(objdir, "plsh_fwd.o")
+    _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "plsh_fwd.hip"), "-o", fwd_obj])
     # the device sampler: no contraction, so its draws round as the host's
     samp_obj = os.path.join(objdir, "plsh_sample.o")
     _run([HIPCC, *COMMON, *DEVICE, "-ffp-contract=off", "-c", os.path.join(CSRC, "plsh_sample.hip"),
           "-o", samp_obj])
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", host_obj, dev_obj, samp_obj, "-o", tmp])
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", host_obj, dev_obj, fwd_obj, samp_obj, "-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -38,22 +38,14 @@
 #include <vector>
 
 #include "plsh_binning.h"
+#include "plsh_device.h"
+#include "plsh_fwd.h"
 #include "plsh_internal.h"
 #include "plsh_hip_status.h"
 
 namespace plsh {
 namespace dev {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float floatx2 __attribute__((ext_vector_type(2)));
-
-constexpr int kMaxHeadsArg = 128;
-constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
   const void *q;
@@ -90,61 +82,6 @@ struct AttnArgs {
   int32_t order[kMaxHeadsArg];  // head processed in slot i, heaviest sigma first
 };
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  __bf16 h = (__bf16)f;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, h);
-}
-
-// Orders the wave's LDS traffic: lanes see each other's LDS writes after this.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-__device__ __forceinline__ int wave_min_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
-  return x;
-}
-
-// Value of x in the other half of the wave (lane l <-> l ^ 32), via the two
-// results of v_permlane32_swap: lanes < 32 get the upper half in [1], lanes
-// >= 32 get the lower half in [0].
-__device__ __forceinline__ uint32_t other_half(uint32_t x, int lane) {
-  auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return lane < 32 ? p[1] : p[0];
-}
-__device__ __forceinline__ float other_half_f(float x, int lane) {
-  return __uint_as_float(other_half(__float_as_uint(x), lane));
-}
-__device__ __forceinline__ double other_half_d(double x, int lane) {
-  const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const uint64_t lo = other_half((uint32_t)b, lane), hi = other_half((uint32_t)(b >> 32), lane);
-  return __longlong_as_double((long long)(lo | (hi << 32)));
-}
-
-// bits 1..t of a 32-bit mask (t in [0, 31])
-__device__ __forceinline__ uint32_t bits_1_to(int t) {
-  return t == 0 ? 0u : ((0xFFFFFFFFu >> (31 - t)) & ~1u);
-}
 
 // Per-wave block setup for rows [r0, r0 + 32) of one head (see file header),
 // in LDS scratch of the wave.
@@ -477,9 +414,6 @@ struct MfmaLds {
   uint32_t step[kTileKeys][kTileKeys / 4];
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 template <int D>
 __device__ __forceinline__ int swz_key(int key) {
@@ -523,38 +457,6 @@ __device__ __forceinline__ uint32_t piece128(int key, int chunk) {
   return (uint32_t)((chunk >> 2) * 2048 + key * 64 + (((chunk & 3) ^ (((key >> 2) & 1) << 1)) << 4));
 }
 
-// The forward kernel's V tiles at D = 128 are not stored row by row: the
-// 64-byte piece of key `key` holding dims 32 m .. 32 m + 31 (chunks 4 m ..
-// 4 m + 3) lies at m * 2048 + key * 64, its chunk pairs swapped when bit 2 of
-// the key is set.  Each group of four copy lanes still reads one 64-byte
-// segment of a row; the transposing 8-byte reads of a 16-dim block (32
-// lanes: keys 0..7, two chunks, two halves) cover 256 distinct bytes; and
-// the reads of all eight dim blocks differ by immediate offsets, so they need
-// two address registers instead of eight (with eight, the compiler recycled
-// the operand registers and serialised every read behind a matrix op).
-__device__ __forceinline__ uint32_t vpiece128(int key, int chunk) {
-  return (uint32_t)((chunk >> 2) * 2048 + key * 64 + (((chunk & 3) ^ (((key >> 2) & 1) << 1)) << 4));
-}
-
-// LDS address of a pointer into LDS (the generic-to-LDS cast; on static
-// shared variables it folds to a constant)
-__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_void_t *)p; }
-
-// Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at LDS
-// address lds_base + 16 l (lds_base wave-uniform).  Issued as inline assembly so that
-// the ring's only ordering is the explicit vmcnt wait + barrier of each stage
-// (the compiler would otherwise wait for every outstanding copy before any
-// LDS read, since it cannot tell which ring stage a copy targets).
-__device__ __forceinline__ void dma16(const void *gsrc, uint32_t lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gsrc), "s"(m0)
-               : "memory", "m0");
-}
-
-// s_waitcnt with vmcnt <= v and lgkmcnt == 0 (gfx9 encoding)
-#define PLSH_WAIT_VM_LGKM0(v) __builtin_amdgcn_s_waitcnt(((v) & 15) | (((v) >> 4) << 14) | (7 << 4))
 
 // prefix-sum 16 bytes held in 4 dwords (bytes never exceed 255)
 __device__ __forceinline__ uint32_t prefix16(u32x4 &x) {
@@ -572,32 +474,11 @@ __device__ __forceinline__ uint32_t prefix16(u32x4 &x) {
 }
 
 // ---------------------------------------------------------------------------
-// Block-edge pre-pass: one record per (head, 32-row group), in a workspace.
-//   [0, 16)              int32 nnz, U0w, U1w, 0: number of samples with a block
-//                        start inside the group's rows; the group's key range
-//                        [U0w, U1w) (32-aligned)
-//   [16, +8 E)           (lead, W) of every sample sorted by (lead, k), then
-//                        16 sentinels (0x7FFFFFFF, 0); E = s + 16 rounded up
-//                        to even, so that each list is whole 16-byte chunks;
-//                        bit t of W is set when row r0 + t's block of that
-//                        sample starts at the lead (no block start in rows
-//                        r0 + 1 .. r0 + t)
-//   [.., +8 E)           (trail, W) sorted by (trail, k), 16 sentinels
-//                        (written by the non-causal pass only); bit t of W is
-//                        set when row r0 + t's block ends at the trail (no
-//                        block start in rows r0 + t + 1 .. r0 + 31)
-//   [.., +1024)          multiplicity of the diagonal tile: byte [t][u] is
-//                        c(r0 + t, r0 + u), zero where j > i (causal) or j >= n
+// Block-edge pre-pass: one record per (head, 32-row group), in a workspace
+// (record format beside its constants in plsh_device.h).
 // The fp64 block searches are latency-bound; as a kernel of their own they
 // run at high occupancy instead of stalling the MFMA kernel.
 // ---------------------------------------------------------------------------
-constexpr int kSentinels = 16;
-__host__ __device__ constexpr int ev_count(int s) { return (s + kSentinels + 1) & ~1; }
-__host__ __device__ constexpr size_t rec_evl_off() { return 16; }
-__host__ __device__ constexpr size_t rec_evt_off(int s) { return 16 + (size_t)8 * ev_count(s); }
-__host__ __device__ constexpr size_t rec_diag_off(int s) { return 16 + (size_t)16 * ev_count(s); }
-__host__ __device__ constexpr size_t rec_bytes(int s) { return rec_diag_off(s) + 1024; }
-constexpr int kMaxMfmaSamples = 124;
 
 // With CAUSAL false and ws_causal set, the same pass also writes the causal
 // record of every group to ws_causal: the same sorted leads, the group's end
@@ -712,31 +593,6 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int ps
   }
 }
 
-// max of three finite floats in one instruction (the compiler's max of
-// floats first quiets each operand's NaN payload, one extra instruction per
-// operand; logits are never NaN)
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// x from lane l ^ 16 (within each 32-lane half; ds_swizzle bit mode, no
-// memory access)
-__device__ __forceinline__ float xor16_f(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
-}
-
-// four byte counters for keys k, k + 1, k + 2, k + 3: 1 in byte r when
-// r >= d, i.e. the keys at or after an edge d keys past k
-__device__ __forceinline__ uint32_t step4(int d) {
-  const int dc = min(max(d, 0), 4);
-  return dc < 4 ? (0x01010101u << (8 * dc)) : 0u;
-}
-
-__host__ __device__ constexpr size_t ev_wave_bytes(int s, bool causal) {
-  return (size_t)(causal ? 8 : 16) * ev_count(s);
-}
 
 template <int D, bool CAUSAL, bool WALK = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves), amdgpu_waves_per_eu(4, 4)))
@@ -2559,15 +2415,38 @@ plsh_status launch_attn(const dev::AttnArgs &a, int d, int causal, hipStream_t s
 // The estimator: its records, then attn_mfma_kernel.  The records go to the
 // caller's workspace when one is given, else to one from the stream-ordered
 // allocator.
-plsh_status launch_mfma(const dev::AttnArgs &a, int d, int causal, hipStream_t st, const char *who,
-                        void *caller_ws = nullptr) {
+plsh_status launch_mfma(const dev::AttnArgs &a, const double *sigma, int d, int causal, hipStream_t st,
+                        const char *who, void *caller_ws = nullptr) {
+  auto forward = [&](const void *ws) {
+    FwdCall c;
+    c.q = a.q;
+    c.k = a.k;
+    c.v = a.v;
+    c.out = a.out;
+    c.save_lse2 = a.save_lse2;
+    c.ws = ws;
+    c.sigma = sigma;
+    c.batch = a.batch;
+    c.n = a.n;
+    c.heads = a.heads;
+    c.kv_heads = a.kv_heads;
+    c.d = d;
+    c.s = a.s;
+    c.causal = causal != 0;
+    return launch_fwd(c, st, timer_slot(), who);
+  };
+  // (the fp32 partials of the unfused form come from attn_mfma_kernel, the
+  // only kernel with that epilogue and a head stride into the table)
+  auto attend = [&](const void *ws) {
+    return a.o32 ? launch_attn(a, d, causal, st, who, 0, ws) : forward(ws);
+  };
   if (caller_ws) {
     plsh_status rc = launch_edges(a, causal != 0, st, who, caller_ws);
-    return rc == PLSH_OK ? launch_attn(a, d, causal, st, who, 0, caller_ws) : rc;
+    return rc == PLSH_OK ? attend(caller_ws) : rc;
   }
   void *ws = nullptr;
   plsh_status rc = build_records(a, causal != 0, st, who, &ws);
-  if (rc == PLSH_OK) rc = launch_attn(a, d, causal, st, who, 0, ws);
+  if (rc == PLSH_OK) rc = attend(ws);
   return free_records(ws, st, who, rc);
 }
 
@@ -2630,7 +2509,7 @@ extern "C" plsh_status plsh_alibi_attention(const void *q, const void *k, const 
   if ((st = have_device(who)) != PLSH_OK) return st;
   dev::AttnArgs a;
   fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
-  if (dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples) return launch_mfma(a, d, causal != 0, (hipStream_t)stream, who);
+  if (dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples) return launch_mfma(a, sigma, d, causal != 0, (hipStream_t)stream, who);
   return launch_valu(a, d, dtype, causal != 0, (hipStream_t)stream, who);
 }
 
@@ -2673,7 +2552,7 @@ extern "C" plsh_status plsh_alibi_attention_ws(const void *q, const void *k, con
   if ((st = have_device(who)) != PLSH_OK) return st;
   dev::AttnArgs a;
   fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
-  if (mfma) return launch_mfma(a, d, causal != 0, (hipStream_t)stream, who, workspace);
+  if (mfma) return launch_mfma(a, sigma, d, causal != 0, (hipStream_t)stream, who, workspace);
   return launch_valu(a, d, dtype, causal != 0, (hipStream_t)stream, who);
 }
 
@@ -2766,7 +2645,7 @@ extern "C" plsh_status plsh_alibi_attention_unfused(const void *q, const void *k
     a.s = 1;
     a.o32 = o32 + (size_t)kk * rows * d;
     a.lse = lse + (size_t)kk * rows;
-    rc = launch_mfma(a, d, causal != 0, hs, who);
+    rc = launch_mfma(a, sigma, d, causal != 0, hs, who);
   }
   if (rc == PLSH_OK) {
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
@@ -2968,7 +2847,7 @@ extern "C" plsh_status plsh_alibi_attention_lse(const void *q, const void *k, co
   dev::AttnArgs a;
   fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
   a.save_lse2 = lse2;
-  return launch_mfma(a, d, causal != 0, (hipStream_t)stream, who, workspace);
+  return launch_mfma(a, sigma, d, causal != 0, (hipStream_t)stream, who, workspace);
 }
 
 extern "C" plsh_status plsh_kernel_timer(int32_t enable) {

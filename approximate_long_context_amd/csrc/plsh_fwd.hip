@@ -1,0 +1,583 @@
+// plsh_fwd.hip -- the estimator's forward kernel for gfx950 with 32-row
+// waves on 32 x 32 x 16 bf16 matrix ops.
+//
+// "Positional LSH: Binary Block Matrix Approximation for Attention with Linear
+// Biases", Methodology §3 (Theorem 2.2): ALiBi attention as s randomized
+// short-context attentions without positional bias, here fused over the
+// samples as one ratio of sums per row,
+//   T~_i = sum_j c_ij e^{q_i.k_j} v_j / sum_j c_ij e^{q_i.k_j},
+//   c_ij = #{k : j in B_k(i)}  (times the causal mask),
+// each in-block pair evaluated once with its multiplicity c_ij (the union of
+// the s blocks holding i is one interval, Methodology §1: every block holds
+// i).  The multiplicities come from the block-edge records of the pre-pass
+// (format in plsh_device.h): per 32-row group, the samples' block starts
+// left of the group (leads), ends right of it (trails) and the diagonal
+// tile's counts.
+//
+// Layout of the work.  A wave owns one 32-row group of one head (the rows of
+// one record).  A workgroup is four waves sharing one K/V stream: either four
+// consecutive row groups of one head, or, for light heads (small sigma:
+// short blocks), the same row group of up to four query heads of one GQA
+// group, which read the same K/V head and need nearly the same short key
+// range, so each K/V stage is staged once for all of them.
+//
+// Per 32-key stage a wave computes S^T = K Q^T (32 keys x 32 queries) with
+// eight v_mfma_f32_32x32x16_bf16 (D = 128): lane l holds query l % 32 and
+// keys 8 (r / 4) + 4 (l / 32) + r % 4 in accumulator r, so a row's softmax
+// statistics need one exchange between lanes l and l ^ 32.  O^T (D x 32
+// queries) += V^T P^T takes P straight from those accumulators: contraction
+// slot 8 (l / 32) + i of 16-key chunk c stands for key 16 c + 8 (i / 4) +
+// 4 (l / 32) + i % 4, and the transposing LDS reads (ds_read_b64_tr_b16)
+// deliver V^T in that order.  Each K and V fragment read from LDS feeds a
+// 32-query product, half the LDS bytes per pair of 16-query tiles.
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <numeric>
+#include <vector>
+
+#include "plsh_device.h"
+#include "plsh_fwd.h"
+#include "plsh_hip_status.h"
+
+namespace plsh {
+namespace dev {
+
+constexpr int kFwdWaves = 4;   // waves per workgroup, one 32-row group each
+constexpr int kFwdRing = 4;    // K/V ring stages (the tile loop is written for 4)
+constexpr int kKeys = 32;      // keys per stage
+constexpr int kMaxUnits = 128;
+
+struct FwdArgs {
+  const uint16_t *q, *k, *v;
+  uint16_t *out;
+  float *save_lse2;
+  const uint8_t *ws;
+  int32_t batch, n, heads, kv_heads, s, g32;
+  int32_t nunits;
+  // unit u = a set of unit_hw[u] consecutive query heads from unit_head[u]
+  // (one GQA group); its workgroups are unit_start[u] .. unit_start[u+1]-1,
+  // batch * ceil(g32 / (4 / unit_hw[u])) of them; units heaviest first
+  int32_t unit_start[kMaxUnits + 1];
+  uint8_t unit_head[kMaxUnits];
+  uint8_t unit_hw[kMaxUnits];
+};
+
+template <int D>
+struct FwdLds {
+  alignas(16) uint16_t kv[kFwdRing][2][kKeys * D];
+  // step[u][4 hf + i]: word 2 i + hf of the byte counters of a tile (keys
+  // 4 w .. 4 w + 3 in word w) with 1 in every key at or after offset u
+  alignas(16) uint32_t step[kKeys][8];
+};
+
+template <int Q>
+struct Slot {
+  static constexpr int value = Q;
+};
+
+// 16-byte chunk swizzle of K rows (and of the staged Q and O rows): the
+// operand reads have lanes 0..31 read keys 0..31 at one chunk, and a 16-byte
+// read serves lanes 0-7 with 24-31 and 8-15 with 16-23 per cycle, which this
+// XOR keeps on 16 distinct chunk positions (D = 64: two keys per 256 bytes).
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+  return D == 128 ? (key & 15) : ((key >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ uint32_t kpos(int key, int chunk) {
+  return (uint32_t)(key * 2 * D + ((chunk ^ kswz<D>(key)) << 4));
+}
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kFwdWaves, 64 * kFwdWaves), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdArgs a) {
+  using L = FwdLds<D>;
+  __shared__ __attribute__((aligned(16))) L lds;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  const int s = a.s, n = a.n;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int t = lane & 31, hf = lane >> 5;
+  {
+    const int u = threadIdx.x >> 3, e = threadIdx.x & 7;  // 256 threads: 32 x 8 entries
+    lds.step[u][e] = step4(u - 4 * (2 * (e & 3) + (e >> 2)));
+  }
+
+  // ---- workgroup -> (unit, batch, row block); XCD-aware: workgroups are
+  // dealt to the 8 XCDs round-robin, and each XCD takes a contiguous run of
+  // the unit's row blocks, so neighbouring blocks share K/V in its L2
+  const int p = blockIdx.x;
+  int unit = 0;
+  {
+    int hi = a.nunits - 1;
+    while (unit < hi) {
+      const int mid = (unit + hi + 1) >> 1;
+      if (a.unit_start[mid] <= p) unit = mid; else hi = mid - 1;
+    }
+  }
+  const int ustart = a.unit_start[unit];
+  const int G = a.unit_start[unit + 1] - ustart;
+  const int tu = p - ustart;
+  const int xcd = p & 7, base_mod = ustart & 7;
+  int start = 0, t0c = 0;
+  for (int c = 0; c < 8; ++c) {
+    const int t0 = (c - base_mod + 8) & 7;
+    const int cnt = t0 < G ? (G - t0 + 7) / 8 : 0;
+    if (c == xcd) { t0c = t0; break; }
+    start += cnt;
+  }
+  const int gidx = start + (tu - t0c) / 8;
+  const int hw = a.unit_hw[unit], gw = 4 / hw;
+  const int nblk = (a.g32 + gw - 1) / gw;
+  const int b = gidx / nblk, blk = gidx - b * nblk;
+  const int h0 = a.unit_head[unit];
+  const int h = h0 + wave / gw;
+  const int grp = blk * gw + wave % gw;
+  const int r0 = 32 * grp;
+  const bool active = grp < a.g32;
+  const int kvh = h / (a.heads / a.kv_heads);
+  const size_t rb = rec_bytes(s);
+  const uint8_t *rec = a.ws + ((size_t)h * a.g32 + min(grp, a.g32 - 1)) * rb;
+
+  const uint16_t *Q = a.q + ((int64_t)b * a.heads + h) * n * D;
+  const char *Kb = (const char *)(a.k + ((int64_t)b * a.kv_heads + kvh) * n * D);
+  const char *Vb = (const char *)(a.v + ((int64_t)b * a.kv_heads + kvh) * n * D);
+
+  // ---- key ranges of the four waves' groups (one round trip), the union is
+  // the workgroup's stream; the lane's diagonal-tile counts
+  int U0 = INT32_MAX, U1 = INT32_MIN, U0w = 0, U1w = 0;
+  {
+    int4 hdr[kFwdWaves];
+#pragma unroll
+    for (int w = 0; w < kFwdWaves; ++w) {
+      const int g2 = min(blk * gw + w % gw, a.g32 - 1);
+      hdr[w] = *(const int4 *)(a.ws + ((size_t)(h0 + w / gw) * a.g32 + g2) * rb);
+    }
+#pragma unroll
+    for (int w = 0; w < kFwdWaves; ++w) {
+      if (blk * gw + w % gw < a.g32) {
+        U0 = min(U0, hdr[w].y);
+        U1 = max(U1, hdr[w].z);
+      }
+      if (w == wave) { U0w = hdr[w].y; U1w = hdr[w].z; }
+    }
+  }
+  u32x4 dA = {0u, 0u, 0u, 0u}, dB = {0u, 0u, 0u, 0u};
+  if (active) {
+    const uint8_t *drow = rec + rec_diag_off(s) + 32 * t;
+    dA = *(const u32x4 *)drow;
+    dB = *(const u32x4 *)(drow + 16);
+  }
+  const int nst = (U1 > U0) ? (U1 - U0) / kKeys : 0;
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+  // the lane's words 2 i + hf of its row of the diagonal table
+  uint32_t dg[4] = {hf ? dA[1] : dA[0], hf ? dA[3] : dA[2], hf ? dB[1] : dB[0], hf ? dB[3] : dB[2]};
+  const int dlast = (int)(dB[3] >> 24);  // c(row, r0 + 31): the count after the diagonal tile
+
+  // ---- the wave's sorted edge lists into its LDS slice (16 bytes = two
+  // edges per lane), complete at the first stage's wait
+  const int nch = ev_count(s) / 2;
+  u32x2 *evl = (u32x2 *)(dyn + (size_t)wave * ev_wave_bytes(s, CAUSAL));
+  u32x2 *evt = evl + ev_count(s);
+  if (active) {
+    for (int c0 = 0; c0 < nch; c0 += 64)
+      if (c0 + lane < nch) dma16(rec + rec_evl_off() + 16 * (c0 + lane), lds_addr(evl + 2 * c0));
+    if (!CAUSAL)
+      for (int c0 = 0; c0 < nch; c0 += 64)
+        if (c0 + lane < nch) dma16(rec + rec_evt_off(s) + 16 * (c0 + lane), lds_addr(evt + 2 * c0));
+  }
+
+  // ---- the wave's 32 query rows into ring slots 2, 3 (free until the first
+  // pair has read them), whole rows per copy instruction, K-row swizzle
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const uint32_t q_lds = lds_addr(&lds.kv[2][0][0]) + wave * 32 * D * 2;
+  if (active) {
+#pragma unroll
+    for (int c0 = 0; c0 < 32 * CPR; c0 += 64) {
+      const int row = (c0 + lane) / CPR, ch = (c0 + lane) % CPR;
+      const int64_t off = (int64_t)min(r0 + row, n - 1) * (2 * D) + 16 * (ch ^ kswz<D>(row));
+      dma16((const char *)Q + off, q_lds + 16 * c0);
+    }
+  }
+
+  // ---- K/V staging: a K tile is 32 whole rows (K-row swizzle), a V tile 32
+  // keys x D as 64-byte pieces per 32 dims (vpiece128); each tile is 4 D
+  // 16-byte chunks, wave w copies chunks [w D, (w + 1) D).  Keys past the
+  // end read row n - 1, whose products get c = 0.
+  constexpr int NCW = D / 64;  // copy instructions per wave, tile and stage
+  const uint32_t kv_lds = lds_addr(&lds.kv[0][0][0]);
+  int ck_key[NCW], ck_off[NCW], cv_key[NCW], cv_off[NCW];
+#pragma unroll
+  for (int j = 0; j < NCW; ++j) {
+    const int ci = wave * D + 64 * j + lane;  // the lane's chunk position in the tile
+    ck_key[j] = ci / CPR;
+    ck_off[j] = 16 * ((ci % CPR) ^ kswz<D>(ci / CPR));
+    const int P = 16 * ci;
+    const int vkey = (P >> 6) & 31;
+    cv_key[j] = vkey;
+    cv_off[j] = 16 * (4 * (P >> 11) + (((P >> 4) & 3) ^ (((vkey >> 2) & 1) << 1)));
+  }
+  auto issue_stage = [&](int st, int q) {  // q = st % kFwdRing
+    const int j0 = U0 + kKeys * st;
+#pragma unroll
+    for (int j = 0; j < NCW; ++j) {
+      const int64_t krow = (int64_t)min(j0 + ck_key[j], n - 1) * (2 * D);
+      const int64_t vrow = (int64_t)min(j0 + cv_key[j], n - 1) * (2 * D);
+      const uint32_t dst = kv_lds + (uint32_t)(2 * q) * (kKeys * D * 2) + 16 * (wave * D + 64 * j);
+      dma16(Kb + krow + ck_off[j], dst);
+      dma16(Vb + vrow + cv_off[j], dst + kKeys * D * 2);
+    }
+  };
+  if (nst > 0) issue_stage(0, 0);
+  if (nst > 1) issue_stage(1, 1);
+
+  // ---- running state of the lane's row
+  constexpr int NC = D / 16;  // QK^T products per stage
+  constexpr int NB = D / 32;  // 32-dim blocks of O^T
+  floatx16 oacc[NB];
+#pragma unroll
+  for (int db = 0; db < NB; ++db) oacc[db] = floatx16{};
+  float m2 = -INFINITY;  // running max, log2 units
+  float lsum = 0.f;      // this lane's share of the row sum
+  int base = 0;          // the row's multiplicity just before the current tile
+  int lp = 0, tp = 0;    // next unconsumed lead / trail edge
+  int pl = 0, pt = 0;    // their positions (wave-uniform)
+  int lg_base = -1;      // the count whose log2 is lg
+  float lg = 0.f;
+  bf16x8 qf[NC];
+  auto pos_at = [&](const u32x2 *ev, int i) { return (int32_t)__builtin_amdgcn_readfirstlane(ev[i][0]); };
+
+  // K operand of product c: key t, chunk 2 c + hf
+  uint32_t kofs[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) kofs[c] = kpos<D>(t, 2 * c + hf);
+  // V operand (transposing reads): lane (g = l / 16, r = l % 16) names key
+  // 4 (g / 2) + r / 4 (+ 16 c + 8 e) at dims 32 b + 16 (g % 2) + 4 (r % 4);
+  // every read of a stage is this address plus an immediate
+  uint32_t vofs;
+  {
+    const int g = lane >> 4, r = lane & 15;
+    const int kk = 4 * (g >> 1) + (r >> 2);
+    const int x = 2 * (g & 1) + ((r & 3) >> 1);  // 16-byte chunk inside the 64-byte piece
+    vofs = (uint32_t)(kk * 64 + ((x ^ (((kk >> 2) & 1) << 1)) << 4) + 8 * (r & 1));
+  }
+  const int sa = active ? (U0w - U0) / kKeys : 0;
+  const int sb = active ? (U1w - U0) / kKeys : 0;
+
+  // a5: S^T = K Q^T for the stages in ring slots Q0 (and Q1): every K
+  // fragment read is issued first, then the products; with two tiles their
+  // two accumulation chains alternate, so no product waits for the previous
+  // one of its own chain
+  auto qk_tiles = [&](auto s0, auto s1, bool two, floatx16 &SA, floatx16 &SB) {
+    const char *ka = (const char *)lds.kv[decltype(s0)::value][0];
+    const char *kb = (const char *)lds.kv[decltype(s1)::value][0];
+    u32x4 kra[NC], krb[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kra[c] = *(const u32x4 *)(ka + kofs[c]);
+    if (two) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) krb[c] = *(const u32x4 *)(kb + kofs[c]);
+    }
+    SA = floatx16{};
+    SB = floatx16{};
+    if (two) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        SA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kra[c]), qf[c], SA, 0, 0, 0);
+        SB = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, krb[c]), qf[c], SB, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NC, 0);  // every K read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NC, 0);  // then the products
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        SA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kra[c]), qf[c], SA, 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NC, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NC, 0);
+    }
+  };
+
+  // Visits, in order, the edges of a sorted list at positions < jend from
+  // index ptr (position pp) and advances both: lane l reads edge ptr + l, so up
+  // to 64 edges are found with one LDS read and a ballot (the list ends in 16
+  // sentinels at INT32_MAX; reads stay inside it).
+  const int ev_last = s + kSentinels - 1;
+  auto edges_in_tile = [&](const u32x2 *ev, int &ptr, int &pp, int jend, auto &&visit) {
+    while (pp < jend) {
+      const u32x2 e = ev[min(ptr + lane, ev_last)];
+      const int k = __popcll(__ballot((int32_t)e[0] < jend));  // a prefix of the lanes
+      for (int i = 0; i < k; ++i)
+        visit((int32_t)__builtin_amdgcn_readlane(e[0], i), __builtin_amdgcn_readlane(e[1], i));
+      ptr += k;
+      pp = k < 64 ? (int32_t)__builtin_amdgcn_readlane(e[0], k) : pos_at(ev, ptr);
+    }
+  };
+
+  // a4, a6, a7 for the stage in ring slot Q, whose logits are in sacc
+  auto finish_tile = [&](int st, auto slotc, const floatx16 &sacc) {
+    const char *vt = (const char *)lds.kv[decltype(slotc)::value][1];
+    const int j0 = U0 + kKeys * st;
+    const int jend = j0 + kKeys;
+    // a4: multiplicity of keys j0 + 8 (r / 4) + 4 hf + r % 4, byte r % 4 of
+    // counter word r / 4 (tile word 2 (r / 4) + hf):
+    //  * diagonal tile: the row's bytes of the record's table;
+    //  * a tile holding edges (leads left of the diagonal, trails right of it;
+    //    positions wave-uniform): base +- sum over edges of [row's block
+    //    starts / ends there] [key >= edge];
+    //  * otherwise one count, base, for every key of the tile.
+    float cf[16];
+    int kind;  // 0: one count for the tile, 1: per-key counts
+    if (j0 == r0) {
+      uint32_t d0 = dg[0], d1 = dg[1], d2 = dg[2], d3 = dg[3];
+      asm volatile("" : "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3));
+      const uint32_t dd[4] = {d0, d1, d2, d3};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cf[r] = (float)((dd[r >> 2] >> (8 * (r & 3))) & 0xFFu);
+      // the table already counts every edge up to the tile's end
+      edges_in_tile(evl, lp, pl, jend, [](int, uint32_t) {});
+      if (!CAUSAL) {
+        edges_in_tile(evt, tp, pt, jend, [](int, uint32_t) {});
+        base = dlast;
+      }
+      kind = 1;
+    } else if (pl < jend || (!CAUSAL && pt < jend)) {
+      const uint32_t b4 = (uint32_t)base * 0x01010101u;
+      uint32_t cw[4] = {b4, b4, b4, b4};
+      const uint32_t *srow = &lds.step[0][4 * hf];
+      edges_in_tile(evl, lp, pl, jend, [&](int pos, uint32_t W) {
+        const uint32_t w = (W >> t) & 1u;
+        const u32x4 sr = *(const u32x4 *)(srow + 8 * (pos - j0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cw[i] += w * sr[i];
+        base += (int)w;
+      });
+      if (!CAUSAL)
+        edges_in_tile(evt, tp, pt, jend, [&](int pos, uint32_t W) {
+          const uint32_t w = (W >> t) & 1u;
+          const u32x4 sr = *(const u32x4 *)(srow + 8 * (pos - j0));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cw[i] -= w * sr[i];
+          base -= (int)w;
+        });
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cf[r] = (float)((cw[r >> 2] >> (8 * (r & 3))) & 0xFFu);
+      kind = 1;
+    } else {
+      cf[0] = (float)base;
+      kind = 0;
+    }
+
+    // a6: weighted online softmax in the log2 domain; the running max is
+    // raised only when a logit exceeds it by more than 2^8 (the result does
+    // not depend on the max used), and then for both lanes of the row
+    float mx = max3f(max3f(sacc[0], sacc[1], sacc[2]), max3f(sacc[3], sacc[4], sacc[5]),
+                     max3f(sacc[6], sacc[7], sacc[8]));
+    mx = max3f(mx, max3f(sacc[9], sacc[10], sacc[11]), max3f(sacc[12], sacc[13], sacc[14]));
+    mx = max3f(mx, sacc[15], sacc[15]);
+    if (__any(mx * kLog2e > m2 + 8.0f)) {
+      mx = max3f(mx, other_half_f(mx, lane), mx) * kLog2e;
+      const bool need = mx > m2 + 8.0f;
+      const float mnew = need ? mx : m2;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NB; ++db) oacc[db] *= alpha;
+      m2 = mnew;
+    }
+    // P = c 2^(x - m2), rounded to bf16 in pairs; the row sum adds exactly
+    // the rounded weights that enter PV.  A tile with one count folds
+    // log2 c into the exponent bias (c = 0: bias +inf, P = 0).
+    u32x4 pw[2];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    if (__builtin_amdgcn_readfirstlane(kind) == 0) {
+      if (__any(base != lg_base)) {
+        lg = __builtin_amdgcn_logf(cf[0]);
+        lg_base = base;
+      }
+      const float bias = m2 - lg;
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const floatx2 pf = {__builtin_amdgcn_exp2f(fmaf(sacc[r], kLog2e, -bias)),
+                            __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], kLog2e, -bias))};
+        const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+        pw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const floatx2 pf = {cf[r] * __builtin_amdgcn_exp2f(fmaf(sacc[r], kLog2e, -m2)),
+                            cf[r + 1] * __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], kLog2e, -m2))};
+        const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+        pw[r >> 3][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
+      }
+    }
+
+    // a7: O^T += V^T P^T, two 16-key chunks, V^T by transposing reads (each
+    // chunk's reads issued together ahead of its products)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      u32x4 vop[NB];
+#pragma unroll
+      for (int db = 0; db < NB; ++db) {
+        const char *va = vt + vofs + db * 2048 + cc * 1024;
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)va);
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t *)(va + 512));
+        vop[db] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+      }
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[db]),
+                                                           __builtin_bit_cast(bf16x8, pw[cc]), oacc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NB, 0);  // the chunk's reads
+      __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);      // then its products
+    }
+  };
+
+  // Two stages per barrier: the pair starting at stage st waits for stages
+  // st, st + 1, refills the slots of stages st - 2, st - 1 (every wave is
+  // past them) with st + 2, st + 3, and computes its two tiles.
+  auto pair = [&](int st, auto s0, auto s1) {
+    PLSH_WAIT_VM_LGKM0(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st == 0) {
+      // the Q fragment (B operand: query t, dims 16 c + 8 hf .. + 7), then a
+      // barrier: every wave has its fragment before slots 2, 3 take stages 2, 3
+      const char *qt = (const char *)lds.kv[2][0] + wave * 32 * D * 2;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qt + kpos<D>(t, 2 * c + hf)));
+      PLSH_WAIT_VM_LGKM0(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (active) {  // the edge lists landed with stage 0
+        pl = pos_at(evl, 0);
+        if (!CAUSAL) pt = pos_at(evt, 0);
+      }
+    }
+    if (st + 2 < nst) issue_stage(st + 2, (decltype(s0)::value + 2) % kFwdRing);
+    if (st + 3 < nst) issue_stage(st + 3, (decltype(s1)::value + 2) % kFwdRing);
+    const bool ta = st >= sa && st < sb;
+    const bool tb = st + 1 < nst && st + 1 >= sa && st + 1 < sb;
+    floatx16 SA, SB;
+    if (ta) {
+      qk_tiles(s0, s0, false, SA, SB);
+      finish_tile(st, s0, SA);
+    }
+    if (tb) {
+      qk_tiles(s1, s1, false, SA, SB);
+      finish_tile(st + 1, s1, SA);
+    }
+  };
+  for (int st0 = 0; st0 < nst; st0 += kFwdRing) {
+    pair(st0, Slot<0>{}, Slot<1>{});
+    if (st0 + 2 < nst) pair(st0 + 2, Slot<2>{}, Slot<3>{});
+  }
+
+  // ---- a8: O = acc / l, rounded to bf16, staged in the two ring slots the
+  // last pair does not use (every wave is past them) and stored whole rows
+  // per instruction
+  if (!active) return;
+  const float ltot = lsum + other_half_f(lsum, lane);
+  const float inv = 1.0f / ltot;
+  const int ns = 32 * a.g32;
+  if (a.save_lse2 && hf == 0)
+    a.save_lse2[((int64_t)b * a.heads + h) * ns + r0 + t] = r0 + t < n ? m2 + __log2f(ltot) : 0.f;
+  const int free_slot = (((nst - 1) >> 1) & 1) ? 0 : 2;
+  char *ob = (char *)lds.kv[free_slot][0] + wave * 32 * D * 2;
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // dims 32 db + 8 j + 4 hf .. + 3: half hf of chunk 4 db + j
+      const bf16x2 h0 = __builtin_convertvector((floatx2{oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv}), bf16x2);
+      const bf16x2 h1 =
+          __builtin_convertvector((floatx2{oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv}), bf16x2);
+      *(u32x2 *)(ob + kpos<D>(t, 4 * db + j) + 8 * hf) =
+          u32x2{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+    }
+  wave_sync();
+  uint16_t *O = a.out + ((int64_t)b * a.heads + h) * n * D;
+#pragma unroll
+  for (int c0 = 0; c0 < 32 * CPR; c0 += 64) {
+    const int row = (c0 + lane) / CPR, ch = (c0 + lane) % CPR;
+    const u32x4 val = *(const u32x4 *)(ob + kpos<D>(row, ch));
+    const int i = r0 + row;
+    if (i < n) *(u32x4 *)(O + (int64_t)i * D + 8 * ch) = val;
+  }
+}
+
+}  // namespace dev
+
+plsh_status launch_fwd(const FwdCall &c, hipStream_t st, std::pair<hipEvent_t, hipEvent_t> *timer,
+                       const char *who) {
+  if (c.heads > dev::kMaxUnits) return fail(PLSH_ERR_UNSUPPORTED, "%s: heads = %d exceeds %d", who, c.heads, dev::kMaxUnits);
+  dev::FwdArgs a;
+  a.q = (const uint16_t *)c.q;
+  a.k = (const uint16_t *)c.k;
+  a.v = (const uint16_t *)c.v;
+  a.out = (uint16_t *)c.out;
+  a.save_lse2 = c.save_lse2;
+  a.ws = (const uint8_t *)c.ws;
+  a.batch = c.batch;
+  a.n = c.n;
+  a.heads = c.heads;
+  a.kv_heads = c.kv_heads;
+  a.s = c.s;
+  a.g32 = (c.n + 31) / 32;
+  // head sets: within each GQA group, sets of hw consecutive heads, hw the
+  // largest of 4, 2 that divides the group size when every head of the group
+  // is light (sigma <= kSharedKvSigma), else single heads; heaviest set first
+  const int grp = c.heads / c.kv_heads;
+  struct U { int head, hw; double key; };
+  std::vector<U> units;
+  for (int g0 = 0; g0 < c.heads; g0 += grp) {
+    double smax = 0.0;
+    for (int h = g0; h < g0 + grp; ++h) smax = std::max(smax, c.sigma[h]);
+    const int hw = smax <= kSharedKvSigma ? (grp % 4 == 0 ? 4 : grp % 2 == 0 ? 2 : 1) : 1;
+    for (int h = g0; h < g0 + grp; h += hw) {
+      double key = 0.0;
+      for (int x = h; x < h + hw; ++x) key = std::max(key, c.sigma[x]);
+      units.push_back({h, hw, key});
+    }
+  }
+  std::stable_sort(units.begin(), units.end(), [](const U &x, const U &y) { return x.key > y.key; });
+  a.nunits = (int32_t)units.size();
+  int64_t total = 0;
+  for (size_t u = 0; u < units.size(); ++u) {
+    a.unit_start[u] = (int32_t)total;
+    a.unit_head[u] = (uint8_t)units[u].head;
+    a.unit_hw[u] = (uint8_t)units[u].hw;
+    const int gw = 4 / units[u].hw;
+    total += (int64_t)c.batch * ((a.g32 + gw - 1) / gw);
+    if (total >= ((int64_t)1 << 31)) return fail(PLSH_ERR_UNSUPPORTED, "%s: too many workgroups", who);
+  }
+  a.unit_start[units.size()] = (int32_t)total;
+  for (size_t u = units.size() + 1; u <= (size_t)dev::kMaxUnits; ++u) a.unit_start[u] = (int32_t)total;
+  const dim3 grid((unsigned)total), block(64 * dev::kFwdWaves);
+  const size_t shm = dev::kFwdWaves * dev::ev_wave_bytes(c.s, c.causal);
+  auto go = [&](auto kern) {
+    if (timer) hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)shm, st, timer->first, timer->second, 0u, a);
+    else hipLaunchKernelGGL(kern, grid, block, shm, st, a);
+  };
+  if (c.d == 64) {
+    if (c.causal) go(dev::attn_fwd_kernel<64, true>);
+    else go(dev::attn_fwd_kernel<64, false>);
+  } else {
+    if (c.causal) go(dev::attn_fwd_kernel<128, true>);
+    else go(dev::attn_fwd_kernel<128, false>);
+  }
+  return launch_check(who);
+}
+
+}  // namespace plsh
