@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <numeric>
 #include <utility>
 #include <vector>
@@ -2267,6 +2268,42 @@ struct KernelTimer {
 };
 thread_local KernelTimer g_timer;
 
+// Scratch of the allocation-free entry point: the block-edge records of one
+// call in a file-scope device array (each device that loads the library
+// holds its own copy until the process ends).  Host code never uses the
+// array's name as an address: the address on the current device comes from
+// hipGetSymbolAddress, taken once per device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The scratch array's address on the current device.
+plsh_status scratch_ptr(const char *who, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PLSH_ERR_HIP, "%s: no HIP device: %s", who, hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(PLSH_ERR_UNSUPPORTED, "%s: device %d beyond the %d the scratch table covers", who, dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(PLSH_ERR_HIP, "%s: scratch address on device %d: %s", who, dev, hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PLSH_OK;
+}
+
 // the event pair for the next timed launch, or nullptr when timing is off
 std::pair<hipEvent_t, hipEvent_t> *timer_slot() {
   if (!g_timer.on) return nullptr;
@@ -2554,6 +2591,31 @@ extern "C" plsh_status plsh_alibi_attention_ws(const void *q, const void *k, con
   fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
   if (mfma) return launch_mfma(a, sigma, d, causal != 0, (hipStream_t)stream, who, workspace);
   return launch_valu(a, d, dtype, causal != 0, (hipStream_t)stream, who);
+}
+
+// plsh_alibi_attention with its records in the library's static scratch: no
+// device memory is allocated by the call (see include/plsh.h).
+extern "C" plsh_status plsh_alibi_attention_noalloc(const void *q, const void *k, const void *v, void *out,
+                                                    int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                                    int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                                    const plsh_tables *boundaries, int32_t causal,
+                                                    plsh_stream_t stream) {
+  static const char *who = "plsh_alibi_attention_noalloc";
+  clear_error();
+  plsh_status st = check_common(q, k, v, out, batch, n, heads, kv_heads, d, dtype, sigma, s, boundaries, who);
+  if (st != PLSH_OK) return st;
+  const bool mfma = dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples;
+  const size_t need = mfma ? records_bytes(n, heads, s) : 0;
+  if (need > kScratchBytes)
+    return fail(PLSH_ERR_CAPACITY, "%s: the call's records need %zu bytes, the static scratch holds %zu", who, need,
+                kScratchBytes);
+  if ((st = have_device(who)) != PLSH_OK) return st;
+  dev::AttnArgs a;
+  fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
+  if (!mfma) return launch_valu(a, d, dtype, causal != 0, (hipStream_t)stream, who);
+  void *ws = nullptr;
+  if ((st = scratch_ptr(who, &ws)) != PLSH_OK) return st;
+  return launch_mfma(a, sigma, d, causal != 0, (hipStream_t)stream, who, ws);
 }
 
 // Test aid: the same estimator through the one-row-per-wave VALU kernel.

@@ -25,6 +25,7 @@ STATUS_NAMES = {0: "PLSH_OK", 1: "PLSH_ERR_ARG", 2: "PLSH_ERR_TABLE", 3: "PLSH_E
 
 EXPORTED = ["plsh_sample_tables", "plsh_build_tables", "plsh_validate_tables", "plsh_count_work",
             "plsh_alibi_attention", "plsh_alibi_attention_ws", "plsh_attention_workspace_size",
+            "plsh_alibi_attention_noalloc",
             "plsh_debug_block_intervals",
             "plsh_debug_attention_reference", "plsh_alibi_attention_unfused", "plsh_alibi_attention_walk",
             "plsh_alibi_attention_backward", "plsh_alibi_attention_backward_saved",
@@ -66,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.plsh_debug_attention_reference.argtypes = attn
         L.plsh_alibi_attention_unfused.argtypes = attn
         L.plsh_alibi_attention_walk.argtypes = attn
+        L.plsh_alibi_attention_noalloc.argtypes = attn
         L.plsh_alibi_attention_ws.argtypes = attn[:-1] + [vp, i64, vp]
         L.plsh_attention_workspace_size.argtypes = [i32, i32, i32, ctypes.c_int, ctypes.POINTER(i64)]
         L.plsh_alibi_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
@@ -305,6 +307,14 @@ def attention(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
         raise PlshError(PLSH_ERR_ARG, "workspace must be a contiguous uint8 tensor on q's device")
     ws = (workspace.data_ptr(), workspace.numel())
     return _attention(lib().plsh_alibi_attention_ws, q, k, v, sigma, s, tables, causal, out, stream, ws)
+
+
+def attention_noalloc(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
+                      out: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
+    """plsh_alibi_attention_noalloc: the records in the library's static
+    scratch (the call allocates no device memory; pass `out` to allocate
+    nothing here either).  Calls that overlap on one device race."""
+    return _attention(lib().plsh_alibi_attention_noalloc, q, k, v, sigma, s, tables, causal, out, stream)
 
 
 def attention_library_workspace(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,

@@ -235,6 +235,32 @@ PLSH_API plsh_status plsh_alibi_attention_ws(const void *q, const void *k, const
                                     int64_t workspace_bytes, plsh_stream_t stream);
 
 /*
+ * plsh_alibi_attention_noalloc -- plsh_alibi_attention (same estimator, same
+ * kernels, bitwise the same output) for callers that cannot allocate device
+ * memory during the call: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The pre-pass records go to a static
+ * scratch array of the library (64 MiB, allocated with the library's code
+ * object on each device it runs on and held until the process ends); the
+ * call allocates nothing and frees nothing.  Every argument is as for
+ * plsh_alibi_attention.
+ *   Limit: heads * ceil(n/32) * (1040 + 16 * E) <= 64 MiB (E = s + 16
+ *   rounded up to even) on the bf16 path with s <= 124 (e.g. 32 heads,
+ *   n = 16384, s <= 56); the fp32 path and s > 124 use no scratch.
+ *   Concurrency: every call on one device shares that device's scratch and
+ *   overwrites it (each call's pre-pass writes every record its attention
+ *   kernel reads, so nothing carries over): calls whose work overlaps on one
+ *   device (different streams, or threads) race and must be ordered by the
+ *   caller.
+ * Errors: those of plsh_alibi_attention, plus PLSH_ERR_CAPACITY (records
+ * beyond the scratch size) and PLSH_ERR_UNSUPPORTED (device ordinal >= 64).
+ */
+PLSH_API plsh_status plsh_alibi_attention_noalloc(const void *q, const void *k, const void *v, void *out,
+                                                  int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                                  int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                                  const plsh_tables *boundaries, int32_t causal,
+                                                  plsh_stream_t stream);
+
+/*
  * plsh_sample_params_device -- the hash parameters of plsh_sample_tables,
  * drawn on the GPU (Methodology §1 random binning, §2 Gamma(2, sigma)
  * pitch): params[h*s + k] = (delta, u) of sample k of head h, bit for bit

@@ -258,6 +258,37 @@ def test_attention_ws_argument_errors():
         assert st == plsh.PLSH_ERR_HIP, msg
 
 
+def test_noalloc_argument_errors_before_any_device_work():
+    """The allocation-free entry point: records beyond its 64 MiB static
+    scratch are refused (PLSH_ERR_CAPACITY) before any device access, and
+    the common argument checks apply; without a device it reports
+    PLSH_ERR_HIP."""
+    import torch
+    L, a, keep = _attn_args()
+
+    def call(**over):
+        L2, b, keep2 = _attn_args(**over)
+        st = L2.plsh_alibi_attention_noalloc(b["q"], b["k"], b["v"], b["out"], b["batch"], b["n"], b["heads"],
+                                             b["kv_heads"], b["d"], b["dtype"], b["sigma"], b["s"], b["tables"],
+                                             b["causal"], b["stream"])
+        return st, L2.plsh_last_error().decode()
+
+    assert call(q=None)[0] == plsh.PLSH_ERR_ARG
+    assert call(d=96)[0] == plsh.PLSH_ERR_UNSUPPORTED
+    # 8 heads, n = 131072, s = 48: 8 * 4096 * 2064 bytes of records > 64 MiB
+    n, heads, s = 131072, 8, 48
+    sig = np.full(heads, 64.0)
+    params = np.zeros((heads * s, 2))
+    tb = plsh._Tables(n, heads, s, params.ctypes.data, None, None)
+    st = L.plsh_alibi_attention_noalloc(0x10000, 0x20000, 0x30000, 0x40000000, 1, n, heads, heads, 128,
+                                        plsh.PLSH_BF16, sig.ctypes.data, s, ctypes.byref(tb), 1, None)
+    assert st == plsh.PLSH_ERR_CAPACITY, L.plsh_last_error()
+    assert b"scratch" in L.plsh_last_error()
+    assert plsh.workspace_size(n, heads, s, torch.bfloat16) > (64 << 20)
+    if not torch.cuda.is_available():
+        assert call()[0] == plsh.PLSH_ERR_HIP
+
+
 def test_lse_and_saved_backward_argument_errors():
     """plsh_alibi_attention_lse and plsh_alibi_attention_backward_saved check
     their extra operands before any device work: null or misaligned lse2 /
