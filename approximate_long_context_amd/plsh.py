@@ -139,19 +139,30 @@ class DeviceTables:
 
 
 def sample_tables(seed: int, n: int, sigma: Sequence[float], s: int) -> Tables:
-    """plsh_sample_tables (two-call protocol)."""
+    """plsh_sample_tables.  The starts buffer is first sized from the
+    expected table size (a pitch drawn from Gamma(2, sigma) has E[1/delta] =
+    1/sigma, so a hash has about n/sigma + 2 entries, at most n + 1), with
+    room to spare, so that one call usually fills it; only a table larger
+    than that takes the protocol's second call."""
     L = lib()
     sig = np.ascontiguousarray(sigma, dtype=np.float64)
     heads = len(sig)
     params = np.empty((heads * s, 2), dtype=np.float64)
     offsets = np.empty(heads * s + 1, dtype=np.int32)
     need = ctypes.c_int64(0)
-    _check(L.plsh_sample_tables(seed, n, heads, _ptr(sig), s, _ptr(params), _ptr(offsets), None, 0,
-                                ctypes.byref(need)))
-    starts = np.empty(max(need.value, 1), dtype=np.int32)
-    _check(L.plsh_sample_tables(seed, n, heads, _ptr(sig), s, _ptr(params), _ptr(offsets),
-                                _ptr(starts), starts.size, ctypes.byref(need)))
-    return Tables(n, heads, s, params, offsets, starts[:need.value])
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        per_row = np.minimum(float(max(n, 0) + 1), 2.0 * n / sig + 3.0)
+    per_row = np.where(np.isfinite(per_row) & (per_row > 0), per_row, float(max(n, 0) + 1))
+    guess = int(min(float(heads) * s * (max(n, 0) + 1), s * float(per_row.sum()) + 2.0 * (max(n, 0) + 1)))
+    starts = np.empty(max(guess, 1), dtype=np.int32)
+    st = L.plsh_sample_tables(seed, n, heads, _ptr(sig), s, _ptr(params), _ptr(offsets),
+                              _ptr(starts), starts.size, ctypes.byref(need))
+    if st == PLSH_ERR_CAPACITY and need.value > starts.size:
+        starts = np.empty(max(need.value, 1), dtype=np.int32)
+        st = L.plsh_sample_tables(seed, n, heads, _ptr(sig), s, _ptr(params), _ptr(offsets),
+                                  _ptr(starts), starts.size, ctypes.byref(need))
+    _check(st)
+    return Tables(n, heads, s, params, offsets, starts[:need.value].copy())
 
 
 def sample_params_device(seed: int, sigma: Sequence[float], s: int, device,

@@ -55,7 +55,10 @@ from approximate_long_context_amd import plsh, workloads as W
 HERE = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-KERNEL_SRC = os.path.join(HERE, "approximate_long_context_amd", "csrc", "plsh_attention.hip")
+# the measured forward kernel's source (its hash keys the committed counter runs)
+KERNEL_SRCS = [os.path.join(HERE, "approximate_long_context_amd", "csrc", f)
+               for f in ("plsh_fwd.hip", "plsh_device.h")]
+FLUSH_BYTES = 1 << 30          # > the 256 MB Infinity Cache and every L2
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 MFMA_FILE = os.path.join(HERE, "profiles", "mfma.json")
 
@@ -182,6 +185,8 @@ def sweep(settle_s: float) -> None:
         reps = 50 if w.n <= 16384 else 10
         ms, kernel_ms = time_calls(lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal,
                                                           out=out), reps)
+        warm = per_call_stats(lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out),
+                              reps)
         B, H, Hkv, n, d, s = w.batch, w.heads, w.kv_heads, w.n, w.d, w.s
         bytes_min = w.esz * B * n * d * (2 * H + 2 * Hkv)
         err = error_stats(out, exact_reference(w, qd, kd, vd)) if w.dtype == "bf16" else None
@@ -204,7 +209,8 @@ def sweep(settle_s: float) -> None:
                "useful_tflops": 4.0 * d * B * pairs_distinct / (ms / 1e3) / 1e12,
                "s_walk_equivalent_tflops": 4.0 * d * B * pairs_alg / (ms / 1e3) / 1e12,
                "hbm_frac_kernel": bytes_min / (kernel_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
-               "error_vs_exact_alibi": err, "backward": bwd}
+               "roofline": roofline_entry(w, pairs_distinct, kernel_ms, ms), "warm": warm,
+               "error_vs_exact_alibi": err, "backward": bwd, "kernel_sha": kernel_sha()}
         log(f"[sweep] {name}: {ms:.4f} ms/call, kernel {kernel_ms:.4f} ms, "
             f"{rec['rows_samples_per_s']:.3g} rows*samples/s, HBM frac {rec['hbm_frac_kernel']:.2f}, "
             f"rel. error vs exact {'n/a' if err is None else format(err['rel_fro'], '.3f')}, "
@@ -214,8 +220,8 @@ def sweep(settle_s: float) -> None:
 
 
 def issued_pairs(t: plsh.Tables, causal: bool) -> int:
-    """(row, key) pairs the MFMA kernel evaluates per batch element: each 16-row
-    wave computes the 32-key tiles of its 32-row group's key range, from the
+    """(row, key) pairs the MFMA kernel evaluates per batch element: each 32-row
+    wave computes the 32-key tiles of its group's key range, from the
     smallest block start of the group's rows (rounded down to 32) to the
     group's end (causal) or its largest block end (rounded up to 32)."""
     n, total = t.n, 0
@@ -249,14 +255,95 @@ def measured_mfma(workload: str):
 
 
 def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def kernel_name(w: W.Workload) -> str:
     """The attention kernel the library dispatches for this workload."""
     if w.dtype == "bf16" and w.s <= 124:
-        return f"attn_mfma_kernel<{w.d}, {'true' if w.causal else 'false'}>"
+        return f"attn_fwd_kernel<{w.d}, {'true' if w.causal else 'false'}>"
     return f"attn_valu_kernel<{'uint16_t' if w.dtype == 'bf16' else 'float'}, {w.d}>"
+
+
+def per_call_stats(fn, reps: int, flush: torch.Tensor = None) -> dict:
+    """Median and min over `reps` single calls, each synchronised: the call
+    (events around it on the current stream) and its attention kernel (events
+    stamped by the kernel's dispatch).  With `flush`, every call is preceded
+    by a write of that buffer (>= 1 GiB: evicts the Infinity Cache and the
+    L2s), so the call starts cold."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    calls, kerns = [], []
+    for i in range(reps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        plsh.kernel_timer(True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        launches, total = plsh.kernel_timer_read()
+        plsh.kernel_timer(False)
+        calls.append(e0.elapsed_time(e1))
+        kerns.append(total / max(launches, 1))
+    return {"reps": reps, "cold": flush is not None,
+            "call_ms_median": float(np.median(calls)), "call_ms_min": float(np.min(calls)),
+            "kernel_ms_median": float(np.median(kerns)), "kernel_ms_min": float(np.min(kerns))}
+
+
+def roofline_entry(w: W.Workload, pairs_distinct: int, kernel_ms: float, call_ms: float) -> dict:
+    """HBM roofline of the attention kernel on the algorithmic bytes, and the
+    useful-FLOP rate against the bf16 peak and against this workload's own
+    attainable rate min(P_bf16, AI x BW_HBM)."""
+    B, H, Hkv, n, d = w.batch, w.heads, w.kv_heads, w.n, w.d
+    bytes_min = w.esz * B * n * d * (2 * H + 2 * Hkv)
+    f_distinct = 4.0 * d * B * pairs_distinct
+    ai = f_distinct / bytes_min
+    attainable = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3)
+    useful_kernel = f_distinct / (kernel_ms / 1e3) / 1e12
+    ach = bytes_min / (kernel_ms / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+            "kernel_ms": kernel_ms, "call_ms": call_ms, "algorithmic_bytes_per_launch": bytes_min,
+            "arith_intensity_flop_per_byte": ai,
+            "attainable_useful_tflops": attainable,
+            "attainable_pct_bf16_peak": 100.0 * attainable / PEAK_BF16_TFLOPS,
+            "useful_tflops_in_kernel": useful_kernel,
+            "useful_pct_bf16_peak_in_kernel": 100.0 * useful_kernel / PEAK_BF16_TFLOPS,
+            "useful_tflops_per_call": f_distinct / (call_ms / 1e3) / 1e12,
+            "useful_pct_bf16_peak_per_call": 100.0 * f_distinct / (call_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def companion(name: str, settle_s: float, reps: int = 50) -> dict:
+    """Time, throughput and roofline of another configuration of the same
+    shape (e.g. s = 40, where the useful-FLOP target lies under the HBM roof)."""
+    dev = torch.device("cuda:0")
+    w = W.get(name)
+    q, k, v = W.make_qkv(w)
+    tables = plsh.sample_tables(w.hash_seed, w.n, w.sigma, w.s)
+    _, pairs_distinct = plsh.count_work(tables, w.causal)
+    dt = tables.to(dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(qd)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(10):
+            plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out)
+        torch.cuda.synchronize()
+    ms, kernel_ms = time_calls(lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out),
+                               reps)
+    warm = per_call_stats(lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out), reps)
+    rec = {"workload": name, "s": w.s, "ms_per_call": ms, "kernel_ms": kernel_ms,
+           "rows_samples_per_s": w.batch * w.heads * w.n * w.s / (ms / 1e3),
+           "roofline": roofline_entry(w, pairs_distinct, kernel_ms, ms), "warm": warm}
+    del qd, kd, vd, out, dt
+    torch.cuda.empty_cache()
+    return rec
 
 
 def measured_traffic(workload: str):
@@ -272,13 +359,40 @@ def measured_traffic(workload: str):
     return ent.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def bf16_excess(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max(|gpu - ref| - half an ulp of bf16 at |ref|): the error beyond the
+    rounding of the estimate itself to bf16."""
+    a = np.abs(ref)
+    half = np.where(a > 0, 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))) - 8), 0.0)
+    return float((np.abs(gpu - ref) - half).max())
+
+
 def cpu_baseline(w: W.Workload, q, k, v, t, budget_s: float, gpu_out: torch.Tensor):
-    """The fp64 oracle's LSH estimate, as it stands, on whole heads of the same
-    workload until `budget_s` seconds of CPU work have been spent; also its
-    agreement with the GPU's output on those heads (max-abs, outside the
-    timing)."""
+    """The fp64 CPU oracle as it stands, beside the GPU:
+    * its LSH estimate (O3) on whole heads of the same workload, heaviest
+      first, until `budget_s` seconds of CPU work (all BLAS threads): the
+      reported rate; and its agreement with the GPU's output on those heads
+      (max-abs, and the excess over bf16 rounding of the estimate);
+    * its exact ALiBi (O1) on sampled rows of the same workload;
+    * single-thread O3 on the tiny fp32 workload and on two heads of the
+      per-head-slopes workload; the tiny workload also on the GPU, with the
+      fp32 path's normwise and elementwise relative errors;
+    * the bias-matrix errors ||L* - M~|| (max, spectral, Frobenius; O4) of
+      the hashes of the workloads with n <= 4096.
+    Nothing here is inside the GPU's timed steps."""
     import oracle as orc
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
+    dev = torch.device("cuda:0")
     qf, kf, vf = W.to_f64(q), W.to_f64(k), W.to_f64(v)
     off, st = orc.tables_from_params(w.n, t.params)
     tabs = orc.starts_per_head(off, st, w.heads, w.s)
@@ -295,15 +409,73 @@ def cpu_baseline(w: W.Workload, q, k, v, t, budget_s: float, gpu_out: torch.Tens
         heads_done.append(h)
         if el >= budget_s:
             break
-    parity = max(float(np.abs(W.to_f64(gpu_out[:1, h:h + 1]) - r).max()) for h, r in zip(heads_done, results))
+    gpu64 = W.to_f64(gpu_out)
+    parity_abs = max(float(np.abs(gpu64[:1, h:h + 1] - r).max()) for h, r in zip(heads_done, results))
+    parity_ex = max(bf16_excess(gpu64[:1, h:h + 1], r) for h, r in zip(heads_done, results))
     threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+
+    # O1, exact ALiBi, on sampled rows of every head (all threads)
+    rows = W.sample_rows(w.n, 64, seed=11)
+    t0 = time.perf_counter()
+    orc.exact_alibi(qf[:1], kf[:1], vf[:1], w.sigma, w.causal, rows=rows)
+    ex_s = time.perf_counter() - t0
+    exact_rec = {"value": len(rows) * w.heads / ex_s, "unit": "query-rows/s", "cores": threads,
+                 "sample": f"fp64 oracle exact ALiBi, {len(rows)} sampled rows x {w.heads} heads "
+                           f"(batch 0), {ex_s:.1f} s"}
+
+    # single thread: the tiny fp32 workload (whole) and two heads of the
+    # per-head-slopes workload
+    single = {}
+    w1 = W.get("tiny-f32-n512")
+    q1, k1, v1 = W.make_qkv(w1)
+    t1 = plsh.sample_tables(w1.hash_seed, w1.n, w1.sigma, w1.s)
+    o1, s1 = orc.tables_from_params(w1.n, t1.params)
+    tabs1 = orc.starts_per_head(o1, s1, w1.heads, w1.s)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        ref1 = orc.lsh_estimate(W.to_f64(q1), W.to_f64(k1), W.to_f64(v1), tabs1, w1.causal)
+        e1 = time.perf_counter() - t0
+    single[w1.name] = {"value": w1.batch * w1.heads * w1.n * w1.s / e1, "unit": "query-rows*samples/s",
+                       "cores": 1, "sample": f"whole workload, {e1 * 1e3:.1f} ms"}
+    g1 = plsh.attention(q1.to(dev), k1.to(dev), v1.to(dev), w1.sigma, w1.s, t1.to(dev), causal=w1.causal)
+    torch.cuda.synchronize()
+    g1 = W.to_f64(g1)
+    big = np.abs(ref1) >= 1e-3 * np.abs(ref1).max()
+    rel = np.abs(g1 - ref1)[big] / np.abs(ref1)[big]
+    fp32_rec = {"workload": w1.name, "normwise_rel": float(np.abs(g1 - ref1).max() / np.abs(ref1).max()),
+                "elementwise_rel_max": float(rel.max()), "elementwise_rel_median": float(np.median(rel)),
+                "elementwise_over": "entries with |ref| >= 1e-3 max|ref|"}
+    w2 = W.get("slopes-n4096")
+    q2, k2, v2 = W.make_qkv(w2)
+    t2 = plsh.sample_tables(w2.hash_seed, w2.n, w2.sigma, w2.s)
+    o2, s2 = orc.tables_from_params(w2.n, t2.params)
+    tabs2 = orc.starts_per_head(o2, s2, w2.heads, w2.s)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        orc.lsh_estimate(W.to_f64(q2[:1, :2]), W.to_f64(k2[:1, :2]), W.to_f64(v2[:1, :2]), tabs2[:2], w2.causal)
+        e2 = time.perf_counter() - t0
+    single[w2.name] = {"value": 2 * w2.n * w2.s / e2, "unit": "query-rows*samples/s", "cores": 1,
+                       "sample": f"heads 0 and 1 of batch 0 (sigma 2 and 4), {e2 * 1e3:.1f} ms"}
+
+    # O4: ||L* - M~|| of the hashes, for the workloads with n <= 4096
+    matrix = {}
+    for wx, tabx, heads in ((w1, tabs1, (0,)), (w2, tabs2, (0, w2.heads - 1))):
+        for h in heads:
+            Ls = orc.alibi_matrix(wx.n, wx.sigma[h])
+            e = orc.matrix_errors(Ls, orc.mask_mean(wx.n, tabx[h]))
+            matrix[f"{wx.name} head {h} (sigma {wx.sigma[h]:g}, s {wx.s})"] = e
     return {"value": done_rows * w.s / el, "unit": "query-rows*samples/s", "cores": threads,
             "kind": "oracle",
             "sample": f"fp64 oracle LSH estimate, full rows of {len(heads_done)} of {w.heads} heads "
                       f"(batch 0, heads {heads_done[0]}..{heads_done[-1]}), {done_rows} rows x s={w.s}, "
-                      f"{el:.1f} s, host {platform.processor() or platform.machine()}, "
-                      f"os.cpu_count()={os.cpu_count()}",
-            "parity_with_gpu_max_abs": parity}
+                      f"{el:.1f} s",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+            "parity_with_gpu_max_abs": parity_abs,
+            "parity_with_gpu_excess_over_bf16_rounding": parity_ex,
+            "exact_alibi_oracle": exact_rec,
+            "single_thread": single,
+            "fp32_path_parity": fp32_rec,
+            "matrix_errors": matrix}
 
 
 def main():
@@ -326,6 +498,8 @@ def main():
                     help="every workload: time, throughput, roofline fraction, error (one line each)")
     ap.add_argument("--no-comparators", action="store_true",
                     help="skip the exact-ALiBi, fixed-blocks and unfused comparisons (profiling runs)")
+    ap.add_argument("--no-percall", action="store_true",
+                    help="skip the single-call warm and cold medians (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus above 1 is not supported "
@@ -383,6 +557,20 @@ def main():
     assert launches == args.steps, (launches, args.steps)
     kernel_ms = kernel_ms_total / launches
     log(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step, attention kernel {kernel_ms:.4f} ms")
+    # single synchronised calls: warm, and cold (a 1 GiB write before each)
+    one = lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out)
+    warm = cold = None
+    if not args.no_percall:
+        warm = per_call_stats(one, 50)
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        cold = per_call_stats(one, 50, flush)
+        del flush
+        torch.cuda.empty_cache()
+    if warm:
+        log(f"[bench] single calls, median/min: warm {warm['call_ms_median']:.4f}/{warm['call_ms_min']:.4f} ms "
+            f"(kernel {warm['kernel_ms_median']:.4f}/{warm['kernel_ms_min']:.4f}), cold "
+            f"{cold['call_ms_median']:.4f}/{cold['call_ms_min']:.4f} ms (kernel {cold['kernel_ms_median']:.4f}/"
+            f"{cold['kernel_ms_min']:.4f})")
 
     B, H, Hkv, n, d, s = w.batch, w.heads, w.kv_heads, w.n, w.d, w.s
     sec = ms / 1e3
@@ -512,6 +700,18 @@ def main():
             + ", ".join(f"{x:.1e}" for x in diffs))
         del dod, res, o_s, l_s, g_rec
 
+    # the same shape at the other sample counts (s = 40: the n = 16k case whose
+    # useful-FLOP target lies under the HBM roof)
+    companions = []
+    if not args.no_comparators and w.name.startswith("mistral-7b-n16384"):
+        for other in ("mistral-7b-n16384-s10", "mistral-7b-n16384-s40"):
+            if other != w.name:
+                c = companion(other, 0.3)
+                companions.append(c)
+                log(f"[bench] {other}: {c['ms_per_call']:.4f} ms/call, kernel {c['kernel_ms']:.4f} ms, HBM frac "
+                    f"{c['roofline']['frac']:.3f}, useful {c['roofline']['useful_pct_bf16_peak_in_kernel']:.1f}% "
+                    f"of bf16 peak in the kernel (attainable {c['roofline']['attainable_pct_bf16_peak']:.1f}%)")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, tables, args.cpu_budget, out)
@@ -540,13 +740,8 @@ def main():
         "s_walk_equivalent_tflops": f_alg / sec / 1e12,
         "pairs_distinct": B * pairs_distinct,
         "pairs_alg": B * pairs_alg,
-        "roofline": {"bound": "hbm", "achieved": ach_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": ach_gbs / PEAK_HBM_GBS, "traffic": traffic,
+        "roofline": {**roofline_entry(w, pairs_distinct, kernel_ms, ms), "traffic": traffic,
                      "kernel": kernel_name(w),
-                     "kernel_ms": kernel_ms,
-                     "algorithmic_bytes_per_launch": bytes_min,
-                     "arith_intensity_flop_per_byte": f_distinct / bytes_min,
-                     "useful_tflops_in_kernel": f_distinct / (kernel_ms / 1e3) / 1e12,
                      "issued_pairs": issued,
                      "issued_tflops_in_kernel": 4.0 * d * issued / (kernel_ms / 1e3) / 1e12,
                      "mfma_counters": None if mfma_flops is None else {
@@ -554,6 +749,9 @@ def main():
                          "tflops": mfma_flops / (kernel_ms / 1e3) / 1e12,
                          "pct_bf16_peak": 100.0 * mfma_flops / (kernel_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                          "source": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, profiles/mfma.json"}},
+        "timing": {"steps": {"ms_per_step": ms, "kernel_ms": kernel_ms, "mean_over": args.steps},
+                   "warm": warm, "cold": cold},
+        "other_sample_counts": companions,
         "cpu_baseline": cpu,
         "host_sample_ms": host_sample_ms,
         "error_vs_exact_alibi": err,
