@@ -271,7 +271,7 @@ __host__ __device__ constexpr size_t valu_wave_bytes(int s, int D) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) {
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal, int rpw) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int s = a.s, n = a.n;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -285,14 +285,17 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
   float *qrow = (float *)(rhi + s);
   float *pj = qrow + D;
 
+  // rpw rows per wave (1, 2, 4 or 8): 32 / (4 rpw) workgroups per 32-row group
   const int g32 = (n + 31) / 32;
-  const int unit = blockIdx.x / g32;
-  const int g = blockIdx.x % g32;
+  const int wgpg = 8 / rpw;
+  const int unit = blockIdx.x / (g32 * wgpg);
+  const int rem = blockIdx.x - unit * g32 * wgpg;
+  const int g = rem / wgpg, sub = rem % wgpg;
   const int h = a.order[unit / a.batch];
   const int b = unit % a.batch;
   const int kvh = h / (a.heads / a.kv_heads);
-  const int r0 = g * 32;             // the group's first row
-  const int t_lo = 8 * wave;         // this wave's rows r0 + t_lo .. + 7
+  const int r0 = g * 32;                    // the group's first row
+  const int t_lo = (4 * sub + wave) * rpw;  // this wave's rows r0 + t_lo .. + rpw - 1
   if (r0 + t_lo >= n) return;
 
   const T *Q = (const T *)a.q + ((int64_t)b * a.heads + h) * n * D;
@@ -303,7 +306,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a, int causal) 
   wave_setup(a.params + 2 * (int64_t)h * a.pstride, s, n, r0, lane, w);
 
   constexpr int E = D / 64;
-  for (int t = t_lo; t < t_lo + 8 && r0 + t < n; ++t) {
+  for (int t = t_lo; t < t_lo + rpw && r0 + t < n; ++t) {
     const int i = r0 + t;
     int ulo = n, uhi = 0;
     for (int k = lane; k < s; k += 64) {
@@ -2330,14 +2333,18 @@ void launch_k(void (*kern)(Args...), dim3 grid, dim3 block, size_t shm, hipStrea
 plsh_status launch_valu(const dev::AttnArgs &a, int d, plsh_dtype dtype, int causal, hipStream_t st,
                         const char *who) {
   const size_t shm = 4 * dev::valu_wave_bytes(a.s, d);
-  const dim3 grid((unsigned)((int64_t)((a.n + 31) / 32) * a.batch * a.heads)), block(256);
+  // rows per wave: fewer for small problems, so that their rows spread over
+  // the GPU's 256 compute units instead of running in sequence in few waves
+  const int64_t groups = (int64_t)((a.n + 31) / 32) * a.batch * a.heads;
+  const int rpw = groups <= 64 ? 1 : groups <= 256 ? 2 : groups <= 1024 ? 4 : 8;
+  const dim3 grid((unsigned)(groups * (8 / rpw))), block(256);
   auto *tm = timer_slot();
   if (dtype == PLSH_F32) {
-    if (d == 64) launch_k(dev::attn_valu_kernel<float, 64>, grid, block, shm, st, tm, a, causal);
-    else launch_k(dev::attn_valu_kernel<float, 128>, grid, block, shm, st, tm, a, causal);
+    if (d == 64) launch_k(dev::attn_valu_kernel<float, 64>, grid, block, shm, st, tm, a, causal, rpw);
+    else launch_k(dev::attn_valu_kernel<float, 128>, grid, block, shm, st, tm, a, causal, rpw);
   } else {
-    if (d == 64) launch_k(dev::attn_valu_kernel<uint16_t, 64>, grid, block, shm, st, tm, a, causal);
-    else launch_k(dev::attn_valu_kernel<uint16_t, 128>, grid, block, shm, st, tm, a, causal);
+    if (d == 64) launch_k(dev::attn_valu_kernel<uint16_t, 64>, grid, block, shm, st, tm, a, causal, rpw);
+    else launch_k(dev::attn_valu_kernel<uint16_t, 128>, grid, block, shm, st, tm, a, causal, rpw);
   }
   return launch_check(who);
 }
@@ -2546,7 +2553,7 @@ extern "C" plsh_status plsh_alibi_attention(const void *q, const void *k, const 
   if ((st = have_device(who)) != PLSH_OK) return st;
   dev::AttnArgs a;
   fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
-  if (dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples) return launch_mfma(a, sigma, d, causal != 0, (hipStream_t)stream, who);
+  if (dtype == PLSH_BF16 && s <= dev::kMaxFwdSamples) return launch_mfma(a, sigma, d, causal != 0, (hipStream_t)stream, who);
   return launch_valu(a, d, dtype, causal != 0, (hipStream_t)stream, who);
 }
 
@@ -2558,7 +2565,7 @@ extern "C" plsh_status plsh_attention_workspace_size(int32_t n, int32_t heads, i
   if (!bytes) return fail(PLSH_ERR_ARG, "plsh_attention_workspace_size: null pointer argument");
   if (n < 1 || heads < 1 || s < 1) return fail(PLSH_ERR_ARG, "plsh_attention_workspace_size: need n, heads, s >= 1");
   if (dtype != PLSH_BF16 && dtype != PLSH_F32) return fail(PLSH_ERR_UNSUPPORTED, "plsh_attention_workspace_size: unknown dtype");
-  *bytes = (dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples) ? (int64_t)records_bytes(n, heads, s) : 0;
+  *bytes = (dtype == PLSH_BF16 && s <= dev::kMaxFwdSamples) ? (int64_t)records_bytes(n, heads, s) : 0;
   return PLSH_OK;
 }
 
@@ -2572,7 +2579,7 @@ extern "C" plsh_status plsh_alibi_attention_ws(const void *q, const void *k, con
   clear_error();
   plsh_status st = check_common(q, k, v, out, batch, n, heads, kv_heads, d, dtype, sigma, s, boundaries, who);
   if (st != PLSH_OK) return st;
-  const bool mfma = dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples;
+  const bool mfma = dtype == PLSH_BF16 && s <= dev::kMaxFwdSamples;
   const size_t need = mfma ? records_bytes(n, heads, s) : 0;
   if (workspace_bytes < 0 || (size_t)workspace_bytes < need)
     return fail(PLSH_ERR_CAPACITY, "%s: workspace of %lld bytes, the call needs %zu", who,
@@ -2604,7 +2611,7 @@ extern "C" plsh_status plsh_alibi_attention_noalloc(const void *q, const void *k
   clear_error();
   plsh_status st = check_common(q, k, v, out, batch, n, heads, kv_heads, d, dtype, sigma, s, boundaries, who);
   if (st != PLSH_OK) return st;
-  const bool mfma = dtype == PLSH_BF16 && s <= dev::kMaxMfmaSamples;
+  const bool mfma = dtype == PLSH_BF16 && s <= dev::kMaxFwdSamples;
   const size_t need = mfma ? records_bytes(n, heads, s) : 0;
   if (need > kScratchBytes)
     return fail(PLSH_ERR_CAPACITY, "%s: the call's records need %zu bytes, the static scratch holds %zu", who, need,
@@ -2893,8 +2900,8 @@ extern "C" plsh_status plsh_alibi_attention_lse(const void *q, const void *k, co
   if (overlaps(lse2, lb, q, qb) || overlaps(lse2, lb, k, kb) || overlaps(lse2, lb, v, kb) ||
       overlaps(lse2, lb, out, qb))
     return fail(PLSH_ERR_ARG, "%s: lse2 overlaps q, k, v or out", who);
-  if (dtype != PLSH_BF16 || s > dev::kMaxMfmaSamples)
-    return fail(PLSH_ERR_UNSUPPORTED, "%s: bf16 with s <= %d only", who, dev::kMaxMfmaSamples);
+  if (dtype != PLSH_BF16 || s > dev::kMaxFwdSamples)
+    return fail(PLSH_ERR_UNSUPPORTED, "%s: bf16 with s <= %d only", who, dev::kMaxFwdSamples);
   if (workspace) {
     const size_t need = records_bytes(n, heads, s);
     if (workspace_bytes < 0 || (size_t)workspace_bytes < need)

@@ -140,6 +140,9 @@ __host__ __device__ constexpr size_t rec_evl_off() { return 16; }
 __host__ __device__ constexpr size_t rec_evt_off(int s) { return 16 + (size_t)8 * ev_count(s); }
 __host__ __device__ constexpr size_t rec_diag_off(int s) { return 16 + (size_t)16 * ev_count(s); }
 __host__ __device__ constexpr size_t rec_bytes(int s) { return rec_diag_off(s) + 1024; }
+// samples per head of the MFMA paths: the forward kernel (byte counters and
+// per-wave edge lists up to 255) and the backward kernels (124)
+constexpr int kMaxFwdSamples = 255;
 constexpr int kMaxMfmaSamples = 124;
 
 // max of three finite floats in one instruction (the compiler's max of

@@ -263,7 +263,7 @@ def kernel_sha() -> str:
 
 def kernel_name(w: W.Workload) -> str:
     """The attention kernel the library dispatches for this workload."""
-    if w.dtype == "bf16" and w.s <= 124:
+    if w.dtype == "bf16" and w.s <= 255:
         return f"attn_fwd_kernel<{w.d}, {'true' if w.causal else 'false'}>"
     return f"attn_valu_kernel<{'uint16_t' if w.dtype == 'bf16' else 'float'}, {w.d}>"
 

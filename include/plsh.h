@@ -179,9 +179,9 @@ PLSH_API plsh_status plsh_count_work(const plsh_tables *host_tables, int32_t cau
  *               NULL.  n/heads/s must match the call.
  *   causal      0 or 1
  *   stream      HIP stream for the launches
- * Kernels: bf16 with s <= 124 runs a block-edge pre-pass (per head and
+ * Kernels: bf16 (s <= 255) runs a block-edge pre-pass (per head and
  * 32-row group: sorted block ends and the diagonal tile's multiplicities,
- * into the workspace) and then the MFMA attention kernel; fp32, or s > 124,
+ * into the workspace) and then the MFMA attention kernel; fp32
  * runs the one-row-per-wave VALU kernel (no workspace).
  * Buffers must be 16-byte aligned; out must not overlap q, k or v.
  * Errors: PLSH_ERR_ARG (null pointer, n < 1, batch < 1, heads or kv_heads < 1,
@@ -201,7 +201,7 @@ PLSH_API plsh_status plsh_alibi_attention(const void *q, const void *k, const vo
  * plsh_attention_workspace_size -- bytes of device workspace that
  * plsh_alibi_attention_ws needs for a call with these sizes: the block-edge
  * records of the pre-pass, heads * ceil(n/32) * (1040 + 16 * E) bytes with
- * E = s + 16 rounded up to even (bf16 with s <= 124), else 0 (the VALU
+ * E = s + 16 rounded up to even (bf16), else 0 (the VALU
  * kernel needs none).  Host only; needs no device.
  *   bytes  HOST int64 output
  * Errors: PLSH_ERR_ARG (null pointer, n, heads or s < 1),
@@ -244,8 +244,8 @@ PLSH_API plsh_status plsh_alibi_attention_ws(const void *q, const void *k, const
  * call allocates nothing and frees nothing.  Every argument is as for
  * plsh_alibi_attention.
  *   Limit: heads * ceil(n/32) * (1040 + 16 * E) <= 64 MiB (E = s + 16
- *   rounded up to even) on the bf16 path with s <= 124 (e.g. 32 heads,
- *   n = 16384, s <= 56); the fp32 path and s > 124 use no scratch.
+ *   rounded up to even) on the bf16 path (e.g. 32 heads, n = 16384,
+ *   s <= 56); the fp32 path uses no scratch.
  *   Concurrency: every call on one device shares that device's scratch and
  *   overwrites it (each call's pre-pass writes every record its attention
  *   kernel reads, so nothing carries over): calls whose work overlaps on one
@@ -382,10 +382,10 @@ PLSH_API plsh_status plsh_alibi_attention_backward(const void *q, const void *k,
  *               the pre-pass workspace as for plsh_alibi_attention_ws, or
  *               NULL: then the call takes it from the stream-ordered
  *               allocator as plsh_alibi_attention does
- *   the other arguments as for plsh_alibi_attention; bf16, s <= 124.
+ *   the other arguments as for plsh_alibi_attention; bf16, s <= 255.
  * Errors: as plsh_alibi_attention, plus PLSH_ERR_ARG (null, misaligned or
  * overlapping lse2; misaligned or overlapping workspace), PLSH_ERR_CAPACITY
- * (workspace too small) and PLSH_ERR_UNSUPPORTED (fp32 or s > 124).
+ * (workspace too small) and PLSH_ERR_UNSUPPORTED (fp32).
  */
 PLSH_API plsh_status plsh_alibi_attention_lse(const void *q, const void *k, const void *v, void *out,
                                      int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,

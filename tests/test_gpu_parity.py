@@ -189,6 +189,15 @@ def test_bf16_sample_count_edges(dev, s):
     check_bf16(o, ref, what=w.name)
 
 
+@pytest.mark.parametrize("s,causal", [(200, False), (255, False), (255, True)])
+def test_bf16_many_samples_gqa_d128(dev, s, causal):
+    """s above 124 on the MFMA forward kernel: byte counters up to 255, the
+    non-causal edge lists at their largest (one workgroup per CU)."""
+    w = small(f"many-s{s}", 2, 4, 2, 611, 128, "bf16", causal, [1.3, 7.0, 40.0, 180.0], s)
+    o, ref, _ = run_case(dev, w)
+    check_bf16(o, ref, what=w.name)
+
+
 def test_g3_slopes_config_full(dev):
     w = W.get("slopes-n4096")
     o, ref, _ = run_case(dev, w)

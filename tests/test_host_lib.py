@@ -208,13 +208,13 @@ def test_attention_without_device_reports_hip_error():
 
 def test_workspace_size_formula():
     """Records of the pre-pass: heads * ceil(n/32) records of 16 + 16 E + 1024
-    bytes, E = s + 16 rounded up to even; none for fp32 or s > 124."""
-    for n, heads, s in ((1, 1, 1), (512, 1, 8), (16384, 32, 20), (8193, 16, 124), (100, 3, 7)):
+    bytes, E = s + 16 rounded up to even; none for fp32."""
+    for n, heads, s in ((1, 1, 1), (512, 1, 8), (16384, 32, 20), (8193, 16, 124), (100, 3, 7), (100, 2, 125),
+                        (700, 3, 255)):
         e = (s + 16 + 1) & ~1
         want = heads * ((n + 31) // 32) * (16 + 16 * e + 1024)
         assert plsh.workspace_size(n, heads, s, torch_dtype("bf16")) == want
         assert plsh.workspace_size(n, heads, s, torch_dtype("f32")) == 0
-    assert plsh.workspace_size(100, 2, 125, torch_dtype("bf16")) == 0
     nb = ctypes.c_int64(-1)
     L = plsh.lib()
     assert L.plsh_attention_workspace_size(0, 1, 1, plsh.PLSH_BF16, ctypes.byref(nb)) == plsh.PLSH_ERR_ARG
