@@ -26,6 +26,12 @@ turns a counter run with SQ_INSTS_VALU_MFMA_MOPS_BF16 and
 SQ_VALU_MFMA_BUSY_CYCLES into the bf16 matrix-core work per launch.  The
 counter counts units of 512 flops; the run is checked against the pairs the
 kernel issues by construction (P pairs of F flops each, from the tables).
+
+    python -m approximate_long_context_amd.rocprof_summary sweep \
+        --jsonl FILE --command "python bench.py --sweep" --out profiles/NAME.md
+
+turns the JSON lines of `bench.py --sweep` into a markdown table (and keeps
+the lines themselves below it).
 """
 
 from __future__ import annotations
@@ -108,7 +114,39 @@ def main(argv=None) -> None:
     m.add_argument("--command", required=True)
     m.add_argument("--out-md", required=True)
     m.add_argument("--out-json", required=True)
+    w = sub.add_parser("sweep")
+    w.add_argument("--jsonl", required=True)
+    w.add_argument("--command", required=True)
+    w.add_argument("--out", required=True)
     args = ap.parse_args(argv)
+
+    if args.cmd == "sweep":
+        recs = [json.loads(l) for l in open(args.jsonl) if l.startswith("{")]
+        out = ["# Every workload on one MI355X (`bench.py --sweep`)", "", "Command:", "", "```",
+               args.command, "```", "",
+               "| workload | s | call (ms) | kernel (ms) | warm median / min kernel (ms) | query-rows*samples/s "
+               "| HBM frac (kernel) | useful TFLOP/s (kernel) | % of attainable | rel. error vs exact "
+               "| backward from saved forward (ms) |",
+               "|---|---|---|---|---|---|---|---|---|---|---|"]
+        for r in recs:
+            rf = r.get("roofline") or {}
+            wm = r.get("warm") or {}
+            err = r.get("error_vs_exact_alibi")
+            bw = r.get("backward")
+            att = rf.get("attainable_useful_tflops")
+            frac_att = (100.0 * rf["useful_tflops_in_kernel"] / att) if att else float("nan")
+            out.append(f"| {r['workload']} | {r['s']} | {r['ms_per_call']:.4f} | {r['kernel_ms']:.4f} | "
+                       f"{wm.get('kernel_ms_median', float('nan')):.4f} / {wm.get('kernel_ms_min', float('nan')):.4f} | "
+                       f"{r['rows_samples_per_s']:.3g} | {r['hbm_frac_kernel']:.3f} | "
+                       f"{rf.get('useful_tflops_in_kernel', float('nan')):.0f} | {frac_att:.1f} | "
+                       f"{'n/a' if err is None else format(err['rel_fro'], '.3f')} | "
+                       f"{'n/a' if bw is None else format(bw['saved_forward_backward_ms'], '.3f')} |")
+        shas = sorted({r.get("kernel_sha", "?") for r in recs})
+        out += ["", f"Forward kernel source sha256[:16]: {', '.join(shas)}.", "", "The JSON lines:", "", "```"]
+        out += [json.dumps(r) for r in recs] + ["```", ""]
+        open(args.out, "w").write("\n".join(out))
+        print("\n".join(out[:20]))
+        return
 
     if args.cmd == "mfma":
         mops, nd = counter_per_dispatch(args.run, "SQ_INSTS_VALU_MFMA_MOPS_BF16", args.kernel)
