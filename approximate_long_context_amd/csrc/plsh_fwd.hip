@@ -59,12 +59,13 @@ struct FwdArgs {
   const uint8_t *ws;
   int32_t batch, n, heads, kv_heads, s, g32;
   int32_t nunits;
-  // unit u = a set of unit_hw[u] consecutive query heads from unit_head[u]
-  // (one GQA group); its workgroups are unit_start[u] .. unit_start[u+1]-1,
-  // batch * ceil(g32 / (4 / unit_hw[u])) of them; units heaviest first
+  // unit u = a set of hw consecutive query heads from head (one GQA group),
+  // unit_info[u] = head | log2(hw) << 8, hw in {1, 2, 4}; its workgroups
+  // are unit_start[u] .. unit_start[u+1]-1, batch * ceil(g32 / (4 / hw)) of
+  // them; units heaviest first (words, so that the kernel reads them with
+  // scalar loads)
   int32_t unit_start[kMaxUnits + 1];
-  uint8_t unit_head[kMaxUnits];
-  uint8_t unit_hw[kMaxUnits];
+  int32_t unit_info[kMaxUnits];
 };
 
 template <int D>
@@ -131,12 +132,14 @@ void attn_fwd_kernel(FwdArgs a) {
     start += cnt;
   }
   const int gidx = start + (tu - t0c) / 8;
-  const int hw = a.unit_hw[unit], gw = 4 / hw;
-  const int nblk = (a.g32 + gw - 1) / gw;
+  const int info = a.unit_info[unit];
+  const int lhw = info >> 8, lgw = 2 - lhw;  // log2 of heads and of row groups per workgroup
+  const int gw = 1 << lgw;
+  const int nblk = (a.g32 + gw - 1) >> lgw;
   const int b = gidx / nblk, blk = gidx - b * nblk;
-  const int h0 = a.unit_head[unit];
-  const int h = h0 + wave / gw;
-  const int grp = blk * gw + wave % gw;
+  const int h0 = info & 0xFF;
+  const int h = h0 + (wave >> lgw);
+  const int grp = (blk << lgw) + (wave & (gw - 1));
   const int r0 = 32 * grp;
   const bool active = grp < a.g32;
   const int kvh = h / (a.heads / a.kv_heads);
@@ -147,55 +150,36 @@ void attn_fwd_kernel(FwdArgs a) {
   const char *Kb = (const char *)(a.k + ((int64_t)b * a.kv_heads + kvh) * n * D);
   const char *Vb = (const char *)(a.v + ((int64_t)b * a.kv_heads + kvh) * n * D);
 
-  // ---- key ranges of the four waves' groups (one round trip), the union is
-  // the workgroup's stream; the lane's diagonal-tile counts
-  int U0 = INT32_MAX, U1 = INT32_MIN, U0w = 0, U1w = 0;
-  {
-    int4 hdr[kFwdWaves];
+  // ---- the record headers of the four waves' groups (scalar loads, issued
+  // before the copies below so that they may read through the scalar cache)
+  int4 hdr[kFwdWaves];
 #pragma unroll
-    for (int w = 0; w < kFwdWaves; ++w) {
-      const int g2 = min(blk * gw + w % gw, a.g32 - 1);
-      hdr[w] = *(const int4 *)(a.ws + ((size_t)(h0 + w / gw) * a.g32 + g2) * rb);
-    }
-#pragma unroll
-    for (int w = 0; w < kFwdWaves; ++w) {
-      if (blk * gw + w % gw < a.g32) {
-        U0 = min(U0, hdr[w].y);
-        U1 = max(U1, hdr[w].z);
-      }
-      if (w == wave) { U0w = hdr[w].y; U1w = hdr[w].z; }
-    }
+  for (int w = 0; w < kFwdWaves; ++w) {
+    const int g2 = min((blk << lgw) + (w & (gw - 1)), a.g32 - 1);
+    hdr[w] = *(const int4 *)(a.ws + ((size_t)(h0 + (w >> lgw)) * a.g32 + g2) * rb);
   }
+  // ---- then the loads that need only the wave's own record and rows: the
+  // lane's row of the diagonal table, the sorted edge lists (into the wave's
+  // LDS slice, 16 bytes = two edges per lane) and the 32 query rows (into
+  // ring slots 2, 3, free until the first stages have been read, whole rows
+  // per copy instruction, K-row swizzle); all land by the first stage's wait
   u32x4 dA = {0u, 0u, 0u, 0u}, dB = {0u, 0u, 0u, 0u};
   if (active) {
     const uint8_t *drow = rec + rec_diag_off(s) + 32 * t;
     dA = *(const u32x4 *)drow;
     dB = *(const u32x4 *)(drow + 16);
   }
-  const int nst = (U1 > U0) ? (U1 - U0) / kKeys : 0;
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
-  // the lane's words 2 i + hf of its row of the diagonal table
-  uint32_t dg[4] = {hf ? dA[1] : dA[0], hf ? dA[3] : dA[2], hf ? dB[1] : dB[0], hf ? dB[3] : dB[2]};
-  const int dlast = (int)(dB[3] >> 24);  // c(row, r0 + 31): the count after the diagonal tile
-
-  // ---- the wave's sorted edge lists into its LDS slice (16 bytes = two
-  // edges per lane), complete at the first stage's wait
   const int nch = ev_count(s) / 2;
   u32x2 *evl = (u32x2 *)(dyn + (size_t)wave * ev_wave_bytes(s, CAUSAL));
   u32x2 *evt = evl + ev_count(s);
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const uint32_t q_lds = lds_addr(&lds.kv[2][0][0]) + wave * 32 * D * 2;
   if (active) {
     for (int c0 = 0; c0 < nch; c0 += 64)
       if (c0 + lane < nch) dma16(rec + rec_evl_off() + 16 * (c0 + lane), lds_addr(evl + 2 * c0));
     if (!CAUSAL)
       for (int c0 = 0; c0 < nch; c0 += 64)
         if (c0 + lane < nch) dma16(rec + rec_evt_off(s) + 16 * (c0 + lane), lds_addr(evt + 2 * c0));
-  }
-
-  // ---- the wave's 32 query rows into ring slots 2, 3 (free until the first
-  // pair has read them), whole rows per copy instruction, K-row swizzle
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  const uint32_t q_lds = lds_addr(&lds.kv[2][0][0]) + wave * 32 * D * 2;
-  if (active) {
 #pragma unroll
     for (int c0 = 0; c0 < 32 * CPR; c0 += 64) {
       const int row = (c0 + lane) / CPR, ch = (c0 + lane) % CPR;
@@ -203,6 +187,21 @@ void attn_fwd_kernel(FwdArgs a) {
       dma16((const char *)Q + off, q_lds + 16 * c0);
     }
   }
+
+  // ---- key ranges of the four waves' groups (only the scalar header loads
+  // are waited for here), the union is the workgroup's stream
+  int U0 = INT32_MAX, U1 = INT32_MIN, U0w = 0, U1w = 0;
+  {
+#pragma unroll
+    for (int w = 0; w < kFwdWaves; ++w) {
+      if ((blk << lgw) + (w & (gw - 1)) < a.g32) {
+        U0 = min(U0, hdr[w].y);
+        U1 = max(U1, hdr[w].z);
+      }
+      if (w == wave) { U0w = hdr[w].y; U1w = hdr[w].z; }
+    }
+  }
+  const int nst = (U1 > U0) ? (U1 - U0) / kKeys : 0;
 
   // ---- K/V staging: a K tile is 32 whole rows (K-row swizzle), a V tile 32
   // keys x D as 64-byte pieces per 32 dims (vpiece128); each tile is 4 D
@@ -332,7 +331,9 @@ void attn_fwd_kernel(FwdArgs a) {
     float cf[16];
     int kind;  // 0: one count for the tile, 1: per-key counts
     if (j0 == r0) {
-      uint32_t d0 = dg[0], d1 = dg[1], d2 = dg[2], d3 = dg[3];
+      // the lane's words 2 i + hf of its row of the record's table (loaded
+      // in the prologue; landed by the first stage's wait)
+      uint32_t d0 = hf ? dA[1] : dA[0], d1 = hf ? dA[3] : dA[2], d2 = hf ? dB[1] : dB[0], d3 = hf ? dB[3] : dB[2];
       asm volatile("" : "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3));
       const uint32_t dd[4] = {d0, d1, d2, d3};
 #pragma unroll
@@ -341,7 +342,7 @@ void attn_fwd_kernel(FwdArgs a) {
       edges_in_tile(evl, lp, pl, jend, [](int, uint32_t) {});
       if (!CAUSAL) {
         edges_in_tile(evt, tp, pt, jend, [](int, uint32_t) {});
-        base = dlast;
+        base = (int)(dB[3] >> 24);  // c(row, r0 + 31): the count after the diagonal tile
       }
       kind = 1;
     } else if (pl < jend || (!CAUSAL && pt < jend)) {
@@ -556,8 +557,7 @@ plsh_status launch_fwd(const FwdCall &c, hipStream_t st, std::pair<hipEvent_t, h
   int64_t total = 0;
   for (size_t u = 0; u < units.size(); ++u) {
     a.unit_start[u] = (int32_t)total;
-    a.unit_head[u] = (uint8_t)units[u].head;
-    a.unit_hw[u] = (uint8_t)units[u].hw;
+    a.unit_info[u] = units[u].head | ((units[u].hw == 4 ? 2 : units[u].hw == 2 ? 1 : 0) << 8);
     const int gw = 4 / units[u].hw;
     total += (int64_t)c.batch * ((a.g32 + gw - 1) / gw);
     if (total >= ((int64_t)1 << 31)) return fail(PLSH_ERR_UNSUPPORTED, "%s: too many workgroups", who);
