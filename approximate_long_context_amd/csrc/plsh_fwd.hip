@@ -37,6 +37,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cmath>
 #include <numeric>
 #include <vector>
 
@@ -60,10 +62,12 @@ struct FwdArgs {
   int32_t batch, n, heads, kv_heads, s, g32;
   int32_t nunits;
   // unit u = a set of hw consecutive query heads from head (one GQA group),
-  // unit_info[u] = head | log2(hw) << 8, hw in {1, 2, 4}; its workgroups
-  // are unit_start[u] .. unit_start[u+1]-1, batch * ceil(g32 / (4 / hw)) of
-  // them; units heaviest first (words, so that the kernel reads them with
-  // scalar loads)
+  // unit_info[u] = head | log2(hw) << 8 | log2(sp) << 10, hw in {1, 2, 4},
+  // sp in {1, 2} waves per row group (sp = 2 only with hw = 1: the two
+  // waves of a group take alternate stages of its key range and merge their
+  // partial sums at the end); its workgroups are unit_start[u] ..
+  // unit_start[u+1]-1, batch * ceil(g32 / (4 / (hw sp))) of them; units
+  // heaviest first (words, so that the kernel reads them with scalar loads)
   int32_t unit_start[kMaxUnits + 1];
   int32_t unit_info[kMaxUnits];
 };
@@ -94,7 +98,9 @@ __device__ __forceinline__ uint32_t kpos(int key, int chunk) {
   return (uint32_t)(key * 2 * D + ((chunk ^ kswz<D>(key)) << 4));
 }
 
-template <int D, bool CAUSAL>
+// SPLIT: the launch has units with two waves per row group (the other
+// instantiation keeps that code out of the tile loop).
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kFwdWaves, 64 * kFwdWaves), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdArgs a) {
   using L = FwdLds<D>;
@@ -133,13 +139,17 @@ void attn_fwd_kernel(FwdArgs a) {
   }
   const int gidx = start + (tu - t0c) / 8;
   const int info = a.unit_info[unit];
-  const int lhw = info >> 8, lgw = 2 - lhw;  // log2 of heads and of row groups per workgroup
+  // wave bits, high to low: head in the set (lhw), row group (lgw), part (lsp)
+  const int lhw = (info >> 8) & 3, lsp = SPLIT ? (info >> 10) & 1 : 0, lgw = 2 - lhw - lsp;
   const int gw = 1 << lgw;
   const int nblk = (a.g32 + gw - 1) >> lgw;
   const int b = gidx / nblk, blk = gidx - b * nblk;
   const int h0 = info & 0xFF;
-  const int h = h0 + (wave >> lgw);
-  const int grp = (blk << lgw) + (wave & (gw - 1));
+  const bool split = lsp != 0;
+  const int part = wave & lsp;            // which alternate stages (split only)
+  const int wg_grp = (wave >> lsp) & (gw - 1);  // the wave's row group in the workgroup
+  const int h = h0 + (wave >> (lsp + lgw));
+  const int grp = (blk << lgw) + wg_grp;
   const int r0 = 32 * grp;
   const bool active = grp < a.g32;
   const int kvh = h / (a.heads / a.kv_heads);
@@ -155,8 +165,8 @@ void attn_fwd_kernel(FwdArgs a) {
   int4 hdr[kFwdWaves];
 #pragma unroll
   for (int w = 0; w < kFwdWaves; ++w) {
-    const int g2 = min((blk << lgw) + (w & (gw - 1)), a.g32 - 1);
-    hdr[w] = *(const int4 *)(a.ws + ((size_t)(h0 + (w >> lgw)) * a.g32 + g2) * rb);
+    const int g2 = min((blk << lgw) + ((w >> lsp) & (gw - 1)), a.g32 - 1);
+    hdr[w] = *(const int4 *)(a.ws + ((size_t)(h0 + (w >> (lsp + lgw))) * a.g32 + g2) * rb);
   }
   // ---- then the loads that need only the wave's own record and rows: the
   // lane's row of the diagonal table, the sorted edge lists (into the wave's
@@ -194,7 +204,7 @@ void attn_fwd_kernel(FwdArgs a) {
   {
 #pragma unroll
     for (int w = 0; w < kFwdWaves; ++w) {
-      if ((blk << lgw) + (w & (gw - 1)) < a.g32) {
+      if ((blk << lgw) + ((w >> lsp) & (gw - 1)) < a.g32) {
         U0 = min(U0, hdr[w].y);
         U1 = max(U1, hdr[w].z);
       }
@@ -443,6 +453,25 @@ void attn_fwd_kernel(FwdArgs a) {
     }
   };
 
+  // Split row groups: the edges of a stage the other wave of the group
+  // computes still move this wave's running count past it (the diagonal
+  // tile's table already counts every edge up to its end; after it, the
+  // count of the row's last key is the base, non-causal)
+  auto skip_tile = [&](int st) {
+    const int j0 = U0 + kKeys * st;
+    const int jend = j0 + kKeys;
+    if (j0 == r0) {
+      edges_in_tile(evl, lp, pl, jend, [](int, uint32_t) {});
+      if (!CAUSAL) {
+        edges_in_tile(evt, tp, pt, jend, [](int, uint32_t) {});
+        base = (int)(dB[3] >> 24);
+      }
+    } else {
+      edges_in_tile(evl, lp, pl, jend, [&](int, uint32_t W) { base += (int)((W >> t) & 1u); });
+      if (!CAUSAL) edges_in_tile(evt, tp, pt, jend, [&](int, uint32_t W) { base -= (int)((W >> t) & 1u); });
+    }
+  };
+
   // Two stages per barrier: the pair starting at stage st waits for stages
   // st, st + 1, refills the slots of stages st - 2, st - 1 (every wave is
   // past them) with st + 2, st + 3, and computes its two tiles.
@@ -468,13 +497,18 @@ void attn_fwd_kernel(FwdArgs a) {
     }
     if (st + 2 < nst) issue_stage(st + 2, (decltype(s0)::value + 2) % kFwdRing);
     if (st + 3 < nst) issue_stage(st + 3, (decltype(s1)::value + 2) % kFwdRing);
-    const bool ta = st >= sa && st < sb;
-    const bool tb = st + 1 < nst && st + 1 >= sa && st + 1 < sb;
+    // (split groups: part 0 computes stage st, part 1 stage st + 1, and each
+    // moves its count past the other's)
+    const bool ra = st >= sa && st < sb;
+    const bool rb = st + 1 < nst && st + 1 >= sa && st + 1 < sb;
+    const bool ta = ra && part == 0, tb = rb && (!split || part == 1);
     floatx16 SA, SB;
+    if (ra && part == 1) skip_tile(st);
     if (ta) {
       qk_tiles(s0, s0, false, SA, SB);
       finish_tile(st, s0, SA);
     }
+    if (rb && split && part == 0) skip_tile(st + 1);
     if (tb) {
       qk_tiles(s1, s1, false, SA, SB);
       finish_tile(st + 1, s1, SA);
@@ -485,17 +519,62 @@ void attn_fwd_kernel(FwdArgs a) {
     if (st0 + 2 < nst) pair(st0 + 2, Slot<2>{}, Slot<3>{});
   }
 
+  // ---- split row groups: the part-1 wave hands its partial sums (running
+  // max, row-sum share, O^T accumulators, lane by lane) to the part-0 wave
+  // through LDS, every ring slot being free once all waves have passed the
+  // barrier; the part-0 wave merges them into its own, each side scaled by
+  // 2^(m_p - max(m_0, m_1)), and writes the rows
+  if (split) {
+    PLSH_WAIT_VM_LGKM0(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    u32x4 *pacc = (u32x4 *)lds.kv[0][0] + wg_grp * (4 * NB * 64);  // [4 NB][64 lanes] 16-byte words
+    float *pml = (float *)&lds.step[0][0] + wg_grp * 128;            // [2][64 lanes]
+    if (part == 1 && active) {
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4)
+          pacc[(4 * db + r / 4) * 64 + lane] =
+              u32x4{__float_as_uint(oacc[db][r]), __float_as_uint(oacc[db][r + 1]), __float_as_uint(oacc[db][r + 2]),
+                    __float_as_uint(oacc[db][r + 3])};
+      pml[lane] = m2;
+      pml[64 + lane] = lsum;
+    }
+    PLSH_WAIT_VM_LGKM0(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (part == 1) return;
+    if (active) {
+      const float m1 = pml[lane], l1 = pml[64 + lane];
+      const float mm = fmaxf(m2, m1);
+      const float a0 = __builtin_amdgcn_exp2f(m2 - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+      lsum = lsum * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const u32x4 o1 = pacc[(4 * db + r / 4) * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[db][r + i] = oacc[db][r + i] * a0 + __uint_as_float(o1[i]) * a1;
+        }
+      m2 = mm;
+    }
+  }
+
   // ---- a8: O = acc / l, rounded to bf16, staged in the two ring slots the
-  // last pair does not use (every wave is past them) and stored whole rows
-  // per instruction
+  // last pair does not use (every wave is past them; split groups: slots 2,
+  // 3, past the merge's barrier) and stored whole rows per instruction
   if (!active) return;
   const float ltot = lsum + other_half_f(lsum, lane);
   const float inv = 1.0f / ltot;
   const int ns = 32 * a.g32;
   if (a.save_lse2 && hf == 0)
     a.save_lse2[((int64_t)b * a.heads + h) * ns + r0 + t] = r0 + t < n ? m2 + __log2f(ltot) : 0.f;
-  const int free_slot = (((nst - 1) >> 1) & 1) ? 0 : 2;
-  char *ob = (char *)lds.kv[free_slot][0] + wave * 32 * D * 2;
+  const int free_slot = split ? 2 : ((((nst - 1) >> 1) & 1) ? 0 : 2);
+  char *ob = (char *)lds.kv[free_slot][0] + (split ? wg_grp : wave) * 32 * D * 2;
 #pragma unroll
   for (int db = 0; db < NB; ++db)
 #pragma unroll
@@ -519,6 +598,66 @@ void attn_fwd_kernel(FwdArgs a) {
 }
 
 }  // namespace dev
+
+// Compute units of the current device (2 resident workgroups each), cached
+// per device; 256 if the query fails.
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+    (void)hipGetLastError();
+    v = 256;
+  }
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// Waves per row group for each unit (1, or 2 for single-head units whose
+// workgroups would otherwise set the kernel's length).  Work estimate per
+// 32-row group in 32-key stages: the union of a row's s blocks reaches
+// about 1.55 sigma ln s keys back (causal; twice that, both sides, when not),
+// fitted to sampled tables for sigma 2..256 and s 10..40.  A workgroup of
+// four groups computes about (stages + 3) tiles per wave; split into two
+// groups of two waves, each wave computes about half of its group's stages
+// plus a merge, with one tile per barrier instead of two.  Only when a
+// launch has fewer than two workgroups per resident slot (2 per CU) is the
+// tail not filled by later workgroups, so only then are heads split, and
+// only those whose workgroups exceed 1.5 times both the average load per
+// slot and the average workgroup's load: a split wave has one tile per
+// barrier to cover the next stages' copies, so splitting heads of equal
+// weight measured slower (sigma = 256 everywhere, n = 4096: 80 -> 92 us),
+// while splitting the few heaviest of unequal heads shortens the tail
+// (sigma = 2 .. 256, n = 4096: 59 -> 43 us).  The rule
+// counts one batch element, every head as its own unit, and never splits a
+// light head (sigma <= kSharedKvSigma): a batch and each of its slices, and
+// a GQA layout and the same heads with repeated K/V, take the same
+// decisions and so give the same bits.
+template <class HW, class KEY>
+static std::vector<int> split_units(const FwdCall &c, size_t nunits, HW hw_of, KEY sigma_of) {
+  std::vector<int> sp(nunits, 1);
+  const int g32 = (c.n + 31) / 32;
+  const double slots = 2.0 * device_cus();
+  const double lns = std::log((double)std::max(c.s, 2));
+  const double reach = c.causal ? 0.5 * c.n : (double)c.n;
+  auto load_of = [&](double sigma) {
+    const double keys = c.causal ? 48.0 + 1.55 * sigma * lns : 64.0 + 3.1 * sigma * lns;
+    return std::min(keys, reach) / 32.0 + 3.0;
+  };
+  const double nwg = (double)((g32 + 3) / 4);  // per head and batch element, four groups per workgroup
+  double load = 0.0;
+  for (int h = 0; h < c.heads; ++h) load += nwg * load_of(c.sigma[h]);
+  if (nwg * c.heads >= 2.0 * slots) return sp;
+  const double bar = 1.5 * std::max(load / slots, load / (nwg * c.heads));
+  for (size_t u = 0; u < nunits; ++u)
+    if (hw_of(u) == 1 && sigma_of(u) > kSharedKvSigma && load_of(sigma_of(u)) > bar) sp[u] = 2;
+  return sp;
+}
 
 plsh_status launch_fwd(const FwdCall &c, hipStream_t st, std::pair<hipEvent_t, hipEvent_t> *timer,
                        const char *who) {
@@ -553,12 +692,15 @@ plsh_status launch_fwd(const FwdCall &c, hipStream_t st, std::pair<hipEvent_t, h
     }
   }
   std::stable_sort(units.begin(), units.end(), [](const U &x, const U &y) { return x.key > y.key; });
+  const std::vector<int> sp = split_units(c, units.size(), [&](size_t u) { return units[u].hw; },
+                                          [&](size_t u) { return units[u].key; });
   a.nunits = (int32_t)units.size();
   int64_t total = 0;
   for (size_t u = 0; u < units.size(); ++u) {
     a.unit_start[u] = (int32_t)total;
-    a.unit_info[u] = units[u].head | ((units[u].hw == 4 ? 2 : units[u].hw == 2 ? 1 : 0) << 8);
-    const int gw = 4 / units[u].hw;
+    a.unit_info[u] =
+        units[u].head | ((units[u].hw == 4 ? 2 : units[u].hw == 2 ? 1 : 0) << 8) | ((sp[u] == 2 ? 1 : 0) << 10);
+    const int gw = 4 / (units[u].hw * sp[u]);
     total += (int64_t)c.batch * ((a.g32 + gw - 1) / gw);
     if (total >= ((int64_t)1 << 31)) return fail(PLSH_ERR_UNSUPPORTED, "%s: too many workgroups", who);
   }
@@ -570,12 +712,13 @@ plsh_status launch_fwd(const FwdCall &c, hipStream_t st, std::pair<hipEvent_t, h
     if (timer) hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)shm, st, timer->first, timer->second, 0u, a);
     else hipLaunchKernelGGL(kern, grid, block, shm, st, a);
   };
+  const bool any_split = std::find(sp.begin(), sp.end(), 2) != sp.end();
   if (c.d == 64) {
-    if (c.causal) go(dev::attn_fwd_kernel<64, true>);
-    else go(dev::attn_fwd_kernel<64, false>);
+    if (c.causal) any_split ? go(dev::attn_fwd_kernel<64, true, true>) : go(dev::attn_fwd_kernel<64, true, false>);
+    else any_split ? go(dev::attn_fwd_kernel<64, false, true>) : go(dev::attn_fwd_kernel<64, false, false>);
   } else {
-    if (c.causal) go(dev::attn_fwd_kernel<128, true>);
-    else go(dev::attn_fwd_kernel<128, false>);
+    if (c.causal) any_split ? go(dev::attn_fwd_kernel<128, true, true>) : go(dev::attn_fwd_kernel<128, true, false>);
+    else any_split ? go(dev::attn_fwd_kernel<128, false, true>) : go(dev::attn_fwd_kernel<128, false, false>);
   }
   return launch_check(who);
 }
