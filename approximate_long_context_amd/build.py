@@ -2,10 +2,11 @@
 
     python -m approximate_long_context_amd.build
 
-Device code is compiled without fast-math (the block predicate must be
-bit-exact with the host table) and without packed-fp32 instructions; the
-device sampler (plsh_sample.hip) also without contraction of multiply-adds
-(its draws must round exactly as the host sampler's).
+Device code is compiled without fast-math and without packed-fp32
+instructions; the pre-pass (plsh_prepass.hip: block intervals that must equal
+the host table's bit for bit) and the device sampler (plsh_sample.hip: draws
+that must round exactly as the host sampler's) also without contraction of
+multiply-adds.
 """
 
 from __future__ import annotations
@@ -44,14 +45,17 @@ def build(verbose: bool = False) -> str:
     _run(["g++", "-std=c++17", "-O2", "-fPIC", "-fvisibility=hidden", "-ffp-contract=off", "-Wall", "-c",
           os.path.join(CSRC, "plsh_host.cpp"), "-o", host_obj])
     _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "plsh_attention.hip"), "-o", dev_obj])
-    fwd_obj = os.path.join(objdir, "plsh_fwd.o")
-    _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "plsh_fwd.hip"), "-o", fwd_obj])
-    # the device sampler: no contraction, so its draws round as the host's
-    samp_obj = os.path.join(objdir, "plsh_sample.o")
-    _run([HIPCC, *COMMON, *DEVICE, "-ffp-contract=off", "-c", os.path.join(CSRC, "plsh_sample.hip"),
-          "-o", samp_obj])
+    objs = [host_obj, dev_obj]
+    # kernel translation units; the pre-pass (block intervals, which must equal
+    # the host table's) and the device sampler (draws that round as the
+    # host's) without contraction of multiply-adds
+    for name, extra in (("plsh_fwd", []), ("plsh_mfma16", []), ("plsh_exact", []),
+                        ("plsh_prepass", ["-ffp-contract=off"]), ("plsh_sample", ["-ffp-contract=off"])):
+        obj = os.path.join(objdir, name + ".o")
+        _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, name + ".hip"), "-o", obj])
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", host_obj, dev_obj, fwd_obj, samp_obj, "-o", tmp])
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
