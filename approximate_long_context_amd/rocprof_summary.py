@@ -32,6 +32,12 @@ kernel issues by construction (P pairs of F flops each, from the tables).
 
 turns the JSON lines of `bench.py --sweep` into a markdown table (and keeps
 the lines themselves below it).
+
+    python -m approximate_long_context_amd.rocprof_summary crossover \
+        --jsonl FILE --command "python bench.py --crossover" --out profiles/NAME.md
+
+does the same for the estimator-against-exact-ALiBi lines of `bench.py
+--crossover`.
 """
 
 from __future__ import annotations
@@ -118,7 +124,29 @@ def main(argv=None) -> None:
     w.add_argument("--jsonl", required=True)
     w.add_argument("--command", required=True)
     w.add_argument("--out", required=True)
+    x = sub.add_parser("crossover")
+    x.add_argument("--jsonl", required=True)
+    x.add_argument("--command", required=True)
+    x.add_argument("--out", required=True)
     args = ap.parse_args(argv)
+
+    if args.cmd == "crossover":
+        recs = [json.loads(l) for l in open(args.jsonl) if l.startswith("{")]
+        out = ["# Estimator against dense exact ALiBi over n (`bench.py --crossover`)", "",
+               "Mistral shape: B = 1, H = 32 / H_kv = 8, d = 128, causal, s = 20, sigma_h = 2^(h/4). "
+               "`estimator` is one `plsh_alibi_attention` call (pre-pass + kernel), tables resident; "
+               "`exact` is one `plsh_exact_alibi_attention` call; TFLOP/s counts the dense causal "
+               "work (4 d flops per visited pair) over the exact kernel's time.", "", "Command:", "", "```",
+               args.command, "```", "",
+               "| n | estimator call (ms) | estimator kernel (ms) | exact call (ms) | exact TFLOP/s | exact / estimator |",
+               "|---|---|---|---|---|---|"]
+        for r in recs:
+            out.append(f"| {r['n']} | {r['lsh_call_ms']:.3f} | {r['lsh_attention_kernel_ms']:.3f} | "
+                       f"{r['exact_ms']:.3f} | {r['exact_tflops']:.0f} | {r['exact_over_lsh']:.2f} |")
+        out += ["", "The JSON lines:", "", "```"] + [json.dumps(r) for r in recs] + ["```", ""]
+        open(args.out, "w").write("\n".join(out))
+        print("\n".join(out[:20]))
+        return
 
     if args.cmd == "sweep":
         recs = [json.loads(l) for l in open(args.jsonl) if l.startswith("{")]
