@@ -369,6 +369,29 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int ps
   u32x2 *evt = (u32x2 *)(rec + rec_evt_off(s));
   uint8_t *rec_c = (!CAUSAL && ws_causal) ? ws_causal + (size_t)item * rec_bytes(s) : nullptr;
   u32x2 *evl_c = rec_c ? (u32x2 *)(rec_c + rec_evl_off()) : nullptr;
+  // ranks of the edges (ties by sample index): with s <= 32, J = 64 / s lane
+  // groups split the comparisons of sample k (lane k + s j takes the samples
+  // k2 = j mod J) and add their partial ranks in LDS (the operand records of
+  // the mask step are free by now)
+  const int J = s <= 32 ? 64 / s : 1;
+  int *rk = (int *)w.lst;  // [2][s]: lead ranks, trail ranks
+  if (J > 1) {
+    for (int i = lane; i < 2 * s; i += 64) rk[i] = 0;
+    wave_sync();
+    const int k = lane % s, j = lane / s;
+    if (j < J) {
+      const int32_t lk = w.lead[k], tk = w.trail[k];
+      int rl = 0, rt = 0;
+      for (int k2 = j; k2 < s; k2 += J) {
+        const int32_t l2 = w.lead[k2], t2 = w.trail[k2];
+        rl += (l2 < lk) | ((l2 == lk) & (k2 < k));
+        rt += (t2 < tk) | ((t2 == tk) & (k2 < k));
+      }
+      atomicAdd(&rk[k], rl);
+      if (!CAUSAL) atomicAdd(&rk[s + k], rt);
+    }
+    wave_sync();
+  }
   int mn = INT32_MAX, mx = INT32_MIN;
   for (int k = lane; k < s; k += 64) {
     const int32_t lk = w.lead[k], tk = w.trail[k];
@@ -376,11 +399,16 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int ps
     mn = min(mn, lk);
     mx = max(mx, tk);
     int rl = 0, rt = 0;
+    if (J > 1) {
+      rl = rk[k];
+      if (!CAUSAL) rt = rk[s + k];
+    } else {
 #pragma unroll 4
-    for (int k2 = 0; k2 < s; ++k2) {
-      const int32_t l2 = w.lead[k2], t2 = w.trail[k2];
-      rl += (l2 < lk) | ((l2 == lk) & (k2 < k));
-      rt += (t2 < tk) | ((t2 == tk) & (k2 < k));
+      for (int k2 = 0; k2 < s; ++k2) {
+        const int32_t l2 = w.lead[k2], t2 = w.trail[k2];
+        rl += (l2 < lk) | ((l2 == lk) & (k2 < k));
+        rt += (t2 < tk) | ((t2 == tk) & (k2 < k));
+      }
     }
     const uint32_t ml = mk & ~1u;  // starts inside rows r0 + 1 .. r0 + 31
     const uint32_t wl = ml ? ((1u << __builtin_ctz(ml)) - 1u) : 0xFFFFFFFFu;
@@ -404,18 +432,19 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int ps
   // byte histograms; prefix sums give the counts
   const uint32_t low_t = bits_1_to(t), high_t = ~((2u << t) - 1u);
   uint32_t *hup = hist + 16 * t, *hdn = hup + 8;
-  for (int z = 0; z < nact; ++z) {
+  // (the two half-waves take alternate listed samples, every key of the row)
+  for (int z = hh; z < nact; z += 2) {
     const uint32_t mk = w.mask[w.act[z]];
     const uint32_t ml = mk & low_t;
     if (ml) {
       const int rel = 31 - __builtin_clz(ml);
-      if ((rel >> 4) == hh) atomicAdd(&hup[rel >> 2], 1u << (8 * (rel & 3)));
+      atomicAdd(&hup[rel >> 2], 1u << (8 * (rel & 3)));
     }
     if (!CAUSAL) {
       const uint32_t mh = mk & high_t;
       if (mh) {
         const int rel = __builtin_ctz(mh);
-        if ((rel >> 4) == hh) atomicAdd(&hdn[rel >> 2], 1u << (8 * (rel & 3)));
+        atomicAdd(&hdn[rel >> 2], 1u << (8 * (rel & 3)));
       }
     }
   }
