@@ -154,8 +154,8 @@ def main(argv=None) -> None:
                args.command, "```", "",
                "| workload | s | call (ms) | kernel (ms) | warm median / min kernel (ms) | query-rows*samples/s "
                "| HBM frac (kernel) | useful TFLOP/s (kernel) | % of attainable | rel. error vs exact "
-               "| backward from saved forward (ms) |",
-               "|---|---|---|---|---|---|---|---|---|---|---|"]
+               "| backward from saved forward (ms) | graph-replayed call (ms) |",
+               "|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for r in recs:
             rf = r.get("roofline") or {}
             wm = r.get("warm") or {}
@@ -168,7 +168,8 @@ def main(argv=None) -> None:
                        f"{r['rows_samples_per_s']:.3g} | {r['hbm_frac_kernel']:.3f} | "
                        f"{rf.get('useful_tflops_in_kernel', float('nan')):.0f} | {frac_att:.1f} | "
                        f"{'n/a' if err is None else format(err['rel_fro'], '.3f')} | "
-                       f"{'n/a' if bw is None else format(bw['saved_forward_backward_ms'], '.3f')} |")
+                       f"{'n/a' if bw is None else format(bw['saved_forward_backward_ms'], '.3f')} | "
+                       f"{'n/a' if r.get('graph_replay_ms_per_call') is None else format(r['graph_replay_ms_per_call'], '.4f')} |")
         shas = sorted({r.get("kernel_sha", "?") for r in recs})
         out += ["", f"Forward kernel source sha256[:16]: {', '.join(shas)}.", "", "The JSON lines:", "", "```"]
         out += [json.dumps(r) for r in recs] + ["```", ""]

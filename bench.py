@@ -83,11 +83,17 @@ def copy_calibration(mib: int) -> None:
 
 
 def error_stats(est: torch.Tensor, ref: torch.Tensor) -> dict:
-    """max |est - ref| and ||est - ref||_F / ||ref||_F over the whole output
-    (fp32 on the device)."""
-    d = est.float() - ref.float()
+    """max |est - ref|, ||est - ref||_F / ||ref||_F, and the per-row
+    infinity norm ||est_i - ref_i||_inf / ||ref_i||_inf (median and max over
+    rows), over the whole output (fp32 on the device)."""
+    e, r = est.float(), ref.float()
+    d = e - r
+    row_err = d.abs().amax(dim=-1)
+    row_ref = r.abs().amax(dim=-1).clamp_min(torch.finfo(torch.float32).tiny)
+    rel_rows = (row_err / row_ref).flatten()
     return {"rows": "all", "max_abs": float(d.abs().max()),
-            "rel_fro": float(d.norm() / ref.float().norm())}
+            "rel_fro": float(d.norm() / r.norm()),
+            "row_inf_rel_median": float(rel_rows.median()), "row_inf_rel_max": float(rel_rows.max())}
 
 
 def exact_reference(w: W.Workload, qd, kd, vd) -> torch.Tensor:
@@ -121,6 +127,34 @@ def time_calls(fn, reps: int, launches_per_call: int = 1):
     plsh.kernel_timer(False)
     assert launches == reps * launches_per_call, (launches, reps, launches_per_call)
     return e0.elapsed_time(e1) / reps, total / launches
+
+
+def graph_calls_ms(fn, reps: int) -> float:
+    """ms per call when one call, captured once in a HIP graph, is replayed
+    `reps` times back to back: the device's time per call without the host's
+    per-call work in the binding (fn must pass its output and workspace, so
+    the captured call neither allocates nor fills memory)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del g
+    return ms
 
 
 def crossover() -> None:
@@ -187,6 +221,10 @@ def sweep(settle_s: float) -> None:
                                                           out=out), reps)
         warm = per_call_stats(lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out),
                               reps)
+        wsd = torch.empty(max(1, plsh.workspace_size(w.n, w.heads, w.s, qd.dtype)), dtype=torch.uint8, device=dev)
+        graph_ms = graph_calls_ms(lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out,
+                                                         workspace=wsd), reps)
+        del wsd
         B, H, Hkv, n, d, s = w.batch, w.heads, w.kv_heads, w.n, w.d, w.s
         bytes_min = w.esz * B * n * d * (2 * H + 2 * Hkv)
         err = error_stats(out, exact_reference(w, qd, kd, vd)) if w.dtype == "bf16" else None
@@ -210,6 +248,7 @@ def sweep(settle_s: float) -> None:
                "s_walk_equivalent_tflops": 4.0 * d * B * pairs_alg / (ms / 1e3) / 1e12,
                "hbm_frac_kernel": bytes_min / (kernel_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
                "roofline": roofline_entry(w, pairs_distinct, kernel_ms, ms), "warm": warm,
+               "graph_replay_ms_per_call": graph_ms,
                "error_vs_exact_alibi": err, "backward": bwd, "kernel_sha": kernel_sha()}
         log(f"[sweep] {name}: {ms:.4f} ms/call, kernel {kernel_ms:.4f} ms, "
             f"{rec['rows_samples_per_s']:.3g} rows*samples/s, HBM frac {rec['hbm_frac_kernel']:.2f}, "
@@ -560,12 +599,19 @@ def main():
     # single synchronised calls: warm, and cold (a 1 GiB write before each)
     one = lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out)
     warm = cold = None
+    graph_ms = None
     if not args.no_percall:
         warm = per_call_stats(one, 50)
         flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
         cold = per_call_stats(one, 50, flush)
         del flush
         torch.cuda.empty_cache()
+        # the same call captured once in a HIP graph and replayed back to back
+        wsd = torch.empty(plsh.workspace_size(w.n, w.heads, w.s, qd.dtype), dtype=torch.uint8, device=dev)
+        graph_ms = graph_calls_ms(lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal,
+                                                         out=out, workspace=wsd), args.steps)
+        del wsd
+        log(f"[bench] graph-replayed calls: {graph_ms:.4f} ms per call")
     if warm:
         log(f"[bench] single calls, median/min: warm {warm['call_ms_median']:.4f}/{warm['call_ms_min']:.4f} ms "
             f"(kernel {warm['kernel_ms_median']:.4f}/{warm['kernel_ms_min']:.4f}), cold "
@@ -750,7 +796,7 @@ def main():
                          "pct_bf16_peak": 100.0 * mfma_flops / (kernel_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                          "source": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, profiles/mfma.json"}},
         "timing": {"steps": {"ms_per_step": ms, "kernel_ms": kernel_ms, "mean_over": args.steps},
-                   "warm": warm, "cold": cold},
+                   "warm": warm, "cold": cold, "graph_replay_ms_per_call": graph_ms},
         "other_sample_counts": companions,
         "cpu_baseline": cpu,
         "host_sample_ms": host_sample_ms,

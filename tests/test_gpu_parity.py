@@ -810,3 +810,49 @@ def test_binding_rejects_mismatched_buffers(dev):
     out = plsh.attention(q, k, v, w.sigma, w.s, td, causal=True)
     torch.cuda.synchronize()
     assert out.shape == q.shape
+
+
+# ---------------------------------------------------------- graph capture ---
+@pytest.mark.parametrize("entry", ["ws", "noalloc"])
+def test_graph_capture_replays_match_eager(dev, entry):
+    """A call through the caller-workspace or the allocation-free entry point
+    (no allocation, no memset on the stream) captured in a HIP graph: every
+    replay, with new inputs copied into the captured buffers and eager work in
+    between, gives the bits of an eager call on those inputs.  The captured
+    call is a heavy/light mix with GQA sharing and a split heavy head."""
+    w = small("graph", 1, 8, 2, 1500, 128, "bf16", True, [1.3, 2.0, 3.0, 4.0, 40.0, 90.0, 200.0, 600.0], 11)
+    t = plsh.sample_tables(6, w.n, w.sigma, w.s).to(dev)
+    q0, k0, v0 = (x.to(dev) for x in W.make_qkv(w, seed=1))
+    qs, ks, vs = q0.clone(), k0.clone(), v0.clone()
+    out = torch.empty_like(qs)
+    ws = torch.empty(plsh.workspace_size(w.n, w.heads, w.s, qs.dtype), dtype=torch.uint8, device=dev)
+
+    def call():
+        if entry == "ws":
+            plsh.attention(qs, ks, vs, w.sigma, w.s, t, causal=True, out=out, workspace=ws)
+        else:
+            plsh.attention_noalloc(qs, ks, vs, w.sigma, w.s, t, causal=True, out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("graph capture", entry)
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        q, k, v = (x.to(dev) for x in W.make_qkv(w, seed=10 + rep))
+        qs.copy_(q)
+        ks.copy_(k)
+        vs.copy_(v)
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = plsh.attention(q, k, v, w.sigma, w.s, t, causal=True)
+        torch.cuda.synchronize()
+        say("graph replay", entry, rep)
+        assert torch.equal(out, ref), (entry, rep)
