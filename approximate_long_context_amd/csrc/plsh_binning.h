@@ -39,13 +39,14 @@ PLSH_HD double bin_of(int32_t x, double delta, double u) {
 // 2^-54 together, which leaves a margin above 3.02 * 2^-53 |q| for
 // |q| >= 1/10; below that f = 0 and 0 <= D < 1 anyway.  q == 0 gives
 // |r - 1/2| == 1/2, |q| >= 2^49 a bound <= 0, inf and NaN a NaN: all rejected,
-// so the defining division decides (a fused multiply-add in the bound is
-// exact, the product being a power-of-two scaling).
+// so the defining division decides.  The bound is one fused multiply-add:
+// its product is a power-of-two scaling, exact, so it rounds once, as the
+// scaling followed by the subtraction would (one instruction fewer).
 PLSH_HD double bin_of_r(int32_t x, double delta, double u, double rinv) {
   const double a = (double)x + u;
   const double q = a * rinv;
   const double f = floor(q);
-  if (fabs((q - f) - 0.5) < 0.5 - fabs(q) * 0x1p-50) return f;
+  if (fabs((q - f) - 0.5) < fma(-fabs(q), 0x1p-50, 0.5)) return f;
   return floor(a / delta);
 }
 

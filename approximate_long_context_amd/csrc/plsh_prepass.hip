@@ -464,21 +464,20 @@ __global__ __launch_bounds__(256) void edges_kernel(const double *params, int ps
 #pragma unroll
     for (int i = 0; i < 4; ++i) c[i] -= hd[i] + (hh ? od : 0u) * 0x01010101u;
   }
-  const int last = min(r0 + 31, n - 1);
+  // keep the bytes of keys u <= lim (u < n; causal: u <= t): byte r of word
+  // i is key 16 hh + 4 i + r
+  auto keep = [&](int lim, int i) {
+    const int e = lim - 16 * hh - 4 * i;  // last kept byte of the word
+    return e >= 3 ? 0xFFFFFFFFu : (e < 0 ? 0u : (0xFFFFFFFFu >> (24 - 8 * e)));
+  };
+  const int lim_n = min(31, n - 1 - r0);
+  const int lim = CAUSAL ? min(t, lim_n) : lim_n;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int u = 16 * hh + 4 * i + r;
-      if ((CAUSAL && u > t) || r0 + u > last) c[i] &= ~(0xFFu << (8 * r));
-    }
+  for (int i = 0; i < 4; ++i) c[i] &= keep(lim, i);
   *(u32x4 *)(rec + rec_diag_off(s) + 32 * t + 16 * hh) = c;
   if (rec_c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * hh + 4 * i + r > t) c[i] &= ~(0xFFu << (8 * r));
+    for (int i = 0; i < 4; ++i) c[i] &= keep(min(t, lim_n), i);
     *(u32x4 *)(rec_c + rec_diag_off(s) + 32 * t + 16 * hh) = c;
   }
 }
