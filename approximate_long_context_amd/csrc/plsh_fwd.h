@@ -23,8 +23,15 @@ struct FwdCall {
 };
 
 // Workgroups of up to four query heads of one GQA group share their K/V
-// stages when every head of the set has sigma at or below this scale.
-constexpr double kSharedKvSigma = 16.0;
+// stages when every head of the set has sigma at or below this scale.  A
+// shared stream covers the union of the heads' key ranges for the same 32
+// rows; four consecutive row groups of one head add about three stages to
+// their range instead, which dominates short ranges and not long ones.
+// Measured on the 16k causal workload (32/8 heads, sigma 1.19 .. 256):
+// kernel 0.131 ms at 16, 0.127 at 64, 0.134 at 256; with every head at
+// sigma = 32, 0.137 ms at 16 and 0.116 at 64; with every head at 256,
+// 0.359 ms unshared and 0.401 shared.
+constexpr double kSharedKvSigma = 64.0;
 
 plsh_status launch_fwd(const FwdCall &c, hipStream_t st, std::pair<hipEvent_t, hipEvent_t> *timer,
                        const char *who);

@@ -57,7 +57,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # the measured forward kernel's source (its hash keys the committed counter runs)
 KERNEL_SRCS = [os.path.join(HERE, "approximate_long_context_amd", "csrc", f)
-               for f in ("plsh_fwd.hip", "plsh_device.h")]
+               for f in ("plsh_fwd.hip", "plsh_fwd.h", "plsh_device.h")]
 FLUSH_BYTES = 1 << 30          # > the 256 MB Infinity Cache and every L2
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 MFMA_FILE = os.path.join(HERE, "profiles", "mfma.json")
