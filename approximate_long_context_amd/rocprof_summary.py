@@ -136,13 +136,20 @@ def main(argv=None) -> None:
                "Mistral shape: B = 1, H = 32 / H_kv = 8, d = 128, causal, s = 20, sigma_h = 2^(h/4). "
                "`estimator` is one `plsh_alibi_attention` call (pre-pass + kernel), tables resident; "
                "`exact` is one `plsh_exact_alibi_attention` call; TFLOP/s counts the dense causal "
-               "work (4 d flops per visited pair) over the exact kernel's time.", "", "Command:", "", "```",
+               "work (4 d flops per visited pair) over the exact kernel's time. `torch SDPA flash` is "
+               "torch.nn.functional.scaled_dot_product_attention forced to its flash backend, causal, "
+               "without any bias: a lower bound on what dense exact attention costs on this stack.",
+               "", "Command:", "", "```",
                args.command, "```", "",
-               "| n | estimator call (ms) | estimator kernel (ms) | exact call (ms) | exact TFLOP/s | exact / estimator |",
-               "|---|---|---|---|---|---|"]
+               "| n | estimator call (ms) | estimator kernel (ms) | exact call (ms) | exact TFLOP/s | exact / estimator "
+               "| torch SDPA flash, no bias (ms) | its TFLOP/s |",
+               "|---|---|---|---|---|---|---|---|"]
         for r in recs:
+            fa = r.get("torch_sdpa_flash_no_bias_ms")
             out.append(f"| {r['n']} | {r['lsh_call_ms']:.3f} | {r['lsh_attention_kernel_ms']:.3f} | "
-                       f"{r['exact_ms']:.3f} | {r['exact_tflops']:.0f} | {r['exact_over_lsh']:.2f} |")
+                       f"{r['exact_ms']:.3f} | {r['exact_tflops']:.0f} | {r['exact_over_lsh']:.2f} | "
+                       f"{'n/a' if fa is None else format(fa, '.3f')} | "
+                       f"{'n/a' if fa is None else format(r['torch_sdpa_flash_tflops'], '.0f')} |")
         out += ["", "The JSON lines:", "", "```"] + [json.dumps(r) for r in recs] + ["```", ""]
         open(args.out, "w").write("\n".join(out))
         print("\n".join(out[:20]))

@@ -108,6 +108,32 @@ def dense_flops(w: W.Workload) -> float:
     return 4.0 * w.d * w.batch * w.heads * pairs
 
 
+def sdpa_flash_ms(qd, kd, vd, causal: bool, reps: int):
+    """torch's scaled_dot_product_attention restricted to its flash backend
+    (no bias: a lower bound on what dense exact attention can cost on this
+    stack), GQA by enable_gqa; ms per call, or the reason it is unavailable.
+    The backend is forced so that no other path (the math path's batched
+    products in particular) runs instead."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            fn = lambda: F.scaled_dot_product_attention(qd, kd, vd, is_causal=causal,
+                                                        enable_gqa=qd.shape[1] != kd.shape[1])
+            fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps, None
+    except RuntimeError as ex:
+        return None, str(ex)[:200]
+
+
 def time_calls(fn, reps: int, launches_per_call: int = 1):
     """(ms per call by events around the calls, ms per attention kernel by the
     library's kernel timer)."""
@@ -179,10 +205,13 @@ def crossover() -> None:
             lambda: plsh.attention(qd, kd, vd, w.sigma, w.s, dt, causal=w.causal, out=out), reps_lsh)
         ex_ms, ex_kernel_ms = time_calls(
             lambda: plsh.exact_alibi_attention(qd, kd, vd, w.sigma, causal=w.causal, out=out), reps_exact)
+        fa_ms, _ = sdpa_flash_ms(qd, kd, vd, w.causal, reps_exact)
         rec = {"crossover": True, "workload": w.name, "n": n, "lsh_call_ms": lsh_ms,
                "lsh_attention_kernel_ms": lsh_kernel_ms, "exact_ms": ex_ms,
                "exact_tflops": dense_flops(w) / (ex_kernel_ms / 1e3) / 1e12,
-               "exact_over_lsh": ex_ms / lsh_ms}
+               "exact_over_lsh": ex_ms / lsh_ms,
+               "torch_sdpa_flash_no_bias_ms": fa_ms,
+               "torch_sdpa_flash_tflops": None if fa_ms is None else dense_flops(w) / (fa_ms / 1e3) / 1e12}
         log(f"[crossover] n={n}: estimator {lsh_ms:.3f} ms, exact {ex_ms:.3f} ms "
             f"({rec['exact_tflops']:.0f} TFLOP/s), ratio {rec['exact_over_lsh']:.2f}")
         print(json.dumps(rec), flush=True)
@@ -654,12 +683,18 @@ def main():
         ex_ms, ex_kernel_ms = time_calls(
             lambda: plsh.exact_alibi_attention(qd, kd, vd, w.sigma, causal=w.causal, out=ex_out), 3)
         ex_tflops = dense_flops(w) / (ex_kernel_ms / 1e3) / 1e12
+        fa_ms, fa_why = sdpa_flash_ms(qd, kd, vd, w.causal, 3)
         exact_rec = {"kernel": "exact_mfma_kernel", "ms": ex_ms, "kernel_ms": ex_kernel_ms,
                      "dense_tflop": dense_flops(w) / 1e12, "tflops": ex_tflops,
                      "pct_bf16_peak": 100.0 * ex_tflops / PEAK_BF16_TFLOPS,
-                     "exact_over_lsh_call": ex_ms / ms}
+                     "exact_over_lsh_call": ex_ms / ms,
+                     "torch_sdpa_flash_no_bias": None if fa_ms is None else {
+                         "ms": fa_ms, "tflops": dense_flops(w) / (fa_ms / 1e3) / 1e12,
+                         "over_lsh_call": fa_ms / ms, "over_exact_alibi": fa_ms / ex_ms},
+                     "torch_sdpa_flash_unavailable": fa_why}
         log(f"[bench] exact ALiBi kernel {ex_ms:.3f} ms ({ex_tflops:.0f} TFLOP/s), "
-            f"{ex_ms / ms:.1f}x the estimator's call")
+            f"{ex_ms / ms:.1f}x the estimator's call; torch SDPA flash (no bias) "
+            f"{'unavailable' if fa_ms is None else format(fa_ms, '.3f') + ' ms'}")
         del ex_out
 
     # the "fixed blocks" baseline (one deterministic hash per head, pitch
