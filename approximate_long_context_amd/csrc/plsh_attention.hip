@@ -224,7 +224,7 @@ plsh_status free_records(void *ws, hipStream_t st, const char *who, plsh_status 
 // caller's workspace when one is given, else to one from the stream-ordered
 // allocator.
 plsh_status launch_mfma(const dev::AttnArgs &a, const double *sigma, int d, int causal, hipStream_t st,
-                        const char *who, void *caller_ws = nullptr) {
+                        const char *who, void *caller_ws = nullptr, bool records_ready = false) {
   auto forward = [&](const void *ws) {
     FwdCall c;
     c.q = a.q;
@@ -249,7 +249,7 @@ plsh_status launch_mfma(const dev::AttnArgs &a, const double *sigma, int d, int 
     return a.o32 ? launch_attn(a, d, causal, st, who, 0, ws) : forward(ws);
   };
   if (caller_ws) {
-    plsh_status rc = launch_edges(a, causal != 0, st, who, caller_ws);
+    plsh_status rc = records_ready ? PLSH_OK : launch_edges(a, causal != 0, st, who, caller_ws);
     return rc == PLSH_OK ? attend(caller_ws) : rc;
   }
   void *ws = nullptr;
@@ -351,6 +351,62 @@ extern "C" plsh_status plsh_alibi_attention_ws(const void *q, const void *k, con
   fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
   if (mfma) return launch_mfma(a, sigma, d, causal != 0, (hipStream_t)stream, who, workspace);
   return launch_valu(a, d, dtype, causal != 0, (hipStream_t)stream, who);
+}
+
+// The pre-pass alone, into a caller's workspace (see include/plsh.h).
+extern "C" plsh_status plsh_alibi_records(const plsh_tables *boundaries, int32_t causal, void *workspace,
+                                          int64_t workspace_bytes, plsh_stream_t stream) {
+  static const char *who = "plsh_alibi_records";
+  clear_error();
+  if (!boundaries || !boundaries->params || !workspace) return fail(PLSH_ERR_ARG, "%s: null pointer argument", who);
+  const int32_t n = boundaries->n, heads = boundaries->heads, s = boundaries->s;
+  if (n < 1 || heads < 1 || s < 1) return fail(PLSH_ERR_TABLE, "%s: need n, heads, s >= 1", who);
+  if (s > dev::kMaxFwdSamples) return fail(PLSH_ERR_UNSUPPORTED, "%s: s = %d exceeds %d", who, s, dev::kMaxFwdSamples);
+  if (heads > dev::kMaxHeadsArg)
+    return fail(PLSH_ERR_UNSUPPORTED, "%s: heads = %d exceeds %d", who, heads, dev::kMaxHeadsArg);
+  if ((uintptr_t)workspace & 15u) return fail(PLSH_ERR_ARG, "%s: workspace must be 16-byte aligned", who);
+  const size_t need = records_bytes(n, heads, s);
+  if (workspace_bytes < 0 || (size_t)workspace_bytes < need)
+    return fail(PLSH_ERR_CAPACITY, "%s: workspace of %lld bytes, the records need %zu", who,
+                (long long)workspace_bytes, need);
+  plsh_status st = have_device(who);
+  if (st != PLSH_OK) return st;
+  dev::AttnArgs a{};
+  a.params = boundaries->params;
+  a.n = n;
+  a.heads = heads;
+  a.s = s;
+  a.pstride = s;
+  return launch_edges(a, causal != 0, (hipStream_t)stream, who, workspace);
+}
+
+// The attention kernel alone over records already in the workspace (see
+// include/plsh.h).
+extern "C" plsh_status plsh_alibi_attention_from_records(const void *q, const void *k, const void *v, void *out,
+                                                         int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                                         int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                                         const plsh_tables *boundaries, int32_t causal,
+                                                         const void *workspace, int64_t workspace_bytes,
+                                                         plsh_stream_t stream) {
+  static const char *who = "plsh_alibi_attention_from_records";
+  clear_error();
+  plsh_status st = check_common(q, k, v, out, batch, n, heads, kv_heads, d, dtype, sigma, s, boundaries, who);
+  if (st != PLSH_OK) return st;
+  if (dtype != PLSH_BF16 || s > dev::kMaxFwdSamples)
+    return fail(PLSH_ERR_UNSUPPORTED, "%s: bf16 with s <= %d only", who, dev::kMaxFwdSamples);
+  const size_t need = records_bytes(n, heads, s);
+  if (!workspace) return fail(PLSH_ERR_ARG, "%s: null workspace", who);
+  if ((uintptr_t)workspace & 15u) return fail(PLSH_ERR_ARG, "%s: workspace must be 16-byte aligned", who);
+  if (workspace_bytes < 0 || (size_t)workspace_bytes < need)
+    return fail(PLSH_ERR_CAPACITY, "%s: workspace of %lld bytes, the records need %zu", who,
+                (long long)workspace_bytes, need);
+  // (the kernel only reads the records, so only out must not overlap them)
+  if (overlaps(workspace, need, out, (size_t)batch * heads * n * d * 2))
+    return fail(PLSH_ERR_ARG, "%s: workspace overlaps out", who);
+  if ((st = have_device(who)) != PLSH_OK) return st;
+  dev::AttnArgs a;
+  fill_args(a, q, k, v, out, batch, n, heads, kv_heads, sigma, s, boundaries);
+  return launch_mfma(a, sigma, d, causal != 0, (hipStream_t)stream, who, const_cast<void *>(workspace), true);
 }
 
 // plsh_alibi_attention with its records in the library's static scratch: no

@@ -211,6 +211,10 @@ void attn_fwd_kernel(FwdArgs a) {
       if (w == wave) { U0w = hdr[w].y; U1w = hdr[w].z; }
     }
   }
+  // (a record always holds 0 <= U0 < U1 <= 32 g32; the clamp keeps every
+  // address inside the tensors even for a workspace that holds no records)
+  U0 = min(max(U0, 0), 32 * a.g32);
+  U1 = min(U1, 32 * a.g32);
   const int nst = (U1 > U0) ? (U1 - U0) / kKeys : 0;
 
   // ---- K/V staging: a K tile is 32 whole rows (K-row swizzle), a V tile 32
@@ -313,7 +317,9 @@ void attn_fwd_kernel(FwdArgs a) {
   // Visits, in order, the edges of a sorted list at positions < jend from
   // index ptr (position pp) and advances both: lane l reads edge ptr + l, so up
   // to 64 edges are found with one LDS read and a ballot (the list ends in 16
-  // sentinels at INT32_MAX; reads stay inside it).
+  // sentinels at INT32_MAX, so ptr stops at the first of them).  Reads are
+  // clamped to the list, and a full ballot at or past its last entry ends the
+  // walk, so even a list that is not sorted stays inside itself and ends.
   const int ev_last = s + kSentinels - 1;
   auto edges_in_tile = [&](const u32x2 *ev, int &ptr, int &pp, int jend, auto &&visit) {
     while (pp < jend) {
@@ -322,7 +328,7 @@ void attn_fwd_kernel(FwdArgs a) {
       for (int i = 0; i < k; ++i)
         visit((int32_t)__builtin_amdgcn_readlane(e[0], i), __builtin_amdgcn_readlane(e[1], i));
       ptr += k;
-      pp = k < 64 ? (int32_t)__builtin_amdgcn_readlane(e[0], k) : pos_at(ev, ptr);
+      pp = k < 64 ? (int32_t)__builtin_amdgcn_readlane(e[0], k) : (ptr >= ev_last ? INT32_MAX : pos_at(ev, ptr));
     }
   };
 
@@ -359,9 +365,13 @@ void attn_fwd_kernel(FwdArgs a) {
       const uint32_t b4 = (uint32_t)base * 0x01010101u;
       uint32_t cw[4] = {b4, b4, b4, b4};
       const uint32_t *srow = &lds.step[0][4 * hf];
+      // (an edge visited here lies in the tile, pos - j0 in [0, 32), for any
+      // list the pre-pass wrote; for any other the read stays an LDS read,
+      // which the hardware range-checks against the workgroup's allocation)
+      auto step_at = [&](int pos) { return *(const u32x4 *)(srow + 8 * (pos - j0)); };
       edges_in_tile(evl, lp, pl, jend, [&](int pos, uint32_t W) {
         const uint32_t w = (W >> t) & 1u;
-        const u32x4 sr = *(const u32x4 *)(srow + 8 * (pos - j0));
+        const u32x4 sr = step_at(pos);
 #pragma unroll
         for (int i = 0; i < 4; ++i) cw[i] += w * sr[i];
         base += (int)w;
@@ -369,7 +379,7 @@ void attn_fwd_kernel(FwdArgs a) {
       if (!CAUSAL)
         edges_in_tile(evt, tp, pt, jend, [&](int pos, uint32_t W) {
           const uint32_t w = (W >> t) & 1u;
-          const u32x4 sr = *(const u32x4 *)(srow + 8 * (pos - j0));
+          const u32x4 sr = step_at(pos);
 #pragma unroll
           for (int i = 0; i < 4; ++i) cw[i] -= w * sr[i];
           base -= (int)w;

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "PLSH_OK", 1: "PLSH_ERR_ARG", 2: "PLSH_ERR_TABLE", 3: "PLSH_E
 
 EXPORTED = ["plsh_sample_tables", "plsh_build_tables", "plsh_validate_tables", "plsh_count_work",
             "plsh_alibi_attention", "plsh_alibi_attention_ws", "plsh_attention_workspace_size",
-            "plsh_alibi_attention_noalloc",
+            "plsh_alibi_attention_noalloc", "plsh_alibi_records", "plsh_alibi_attention_from_records",
             "plsh_debug_block_intervals",
             "plsh_debug_attention_reference", "plsh_alibi_attention_unfused", "plsh_alibi_attention_walk",
             "plsh_alibi_attention_backward", "plsh_alibi_attention_backward_saved",
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.plsh_alibi_attention_walk.argtypes = attn
         L.plsh_alibi_attention_noalloc.argtypes = attn
         L.plsh_alibi_attention_ws.argtypes = attn[:-1] + [vp, i64, vp]
+        L.plsh_alibi_attention_from_records.argtypes = attn[:-1] + [vp, i64, vp]
+        L.plsh_alibi_records.argtypes = [TP, i32, vp, i64, vp]
         L.plsh_attention_workspace_size.argtypes = [i32, i32, i32, ctypes.c_int, ctypes.POINTER(i64)]
         L.plsh_alibi_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                     ctypes.c_int, vp, i32, TP, i32, vp]
@@ -318,6 +320,42 @@ def attention(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,
         raise PlshError(PLSH_ERR_ARG, "workspace must be a contiguous uint8 tensor on q's device")
     ws = (workspace.data_ptr(), workspace.numel())
     return _attention(lib().plsh_alibi_attention_ws, q, k, v, sigma, s, tables, causal, out, stream, ws)
+
+
+def _require_workspace(workspace, device: torch.device) -> None:
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or \
+            not workspace.is_contiguous() or workspace.device != device:
+        raise PlshError(PLSH_ERR_ARG, f"workspace must be a contiguous uint8 tensor on {device}")
+
+
+def build_records(tables: DeviceTables, causal: bool, workspace: torch.Tensor,
+                  stream: Optional[int] = None) -> torch.Tensor:
+    """plsh_alibi_records: the block-edge records of `tables` (the pre-pass
+    alone) into `workspace` (a device uint8 tensor of at least
+    workspace_size(n, heads, s, torch.bfloat16) bytes), for
+    attention_from_records with the same tables and causal flag."""
+    if not isinstance(tables, DeviceTables):
+        raise PlshError(PLSH_ERR_ARG, "tables must be a DeviceTables (Tables.to(device))")
+    dev = tables.params.device
+    _require_device_tables(tables, dev)
+    _require_workspace(workspace, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = tables.c_struct()
+    _check(lib().plsh_alibi_records(ctypes.byref(st), int(bool(causal)), workspace.data_ptr(),
+                                    workspace.numel(), stream))
+    return workspace
+
+
+def attention_from_records(q, k, v, sigma, s, tables: DeviceTables, workspace: torch.Tensor,
+                           causal: bool = False, out: Optional[torch.Tensor] = None,
+                           stream: Optional[int] = None) -> torch.Tensor:
+    """plsh_alibi_attention_from_records: the attention kernel alone, over
+    the records build_records wrote to `workspace` for the same tables and
+    causal flag (bitwise the output of attention())."""
+    _require_workspace(workspace, q.device)
+    ws = (workspace.data_ptr(), workspace.numel())
+    return _attention(lib().plsh_alibi_attention_from_records, q, k, v, sigma, s, tables, causal, out, stream, ws)
 
 
 def attention_noalloc(q, k, v, sigma, s, tables: DeviceTables, causal: bool = False,

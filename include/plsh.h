@@ -235,6 +235,49 @@ PLSH_API plsh_status plsh_alibi_attention_ws(const void *q, const void *k, const
                                     int64_t workspace_bytes, plsh_stream_t stream);
 
 /*
+ * plsh_alibi_records -- the pre-pass alone: the block-edge records of every
+ * (head, 32-row group) of a table, into a caller-owned DEVICE workspace, for
+ * plsh_alibi_attention_from_records.  The records are the per-row block
+ * intervals of Methodology §1 (the blocks of each row in every sample, with
+ * the multiplicities of the diagonal tile); they depend only on the table
+ * (n, heads, s, the (delta, u) rows) and on causal, not on q, k or v, so a
+ * caller whose hashes stay fixed across calls (inference with fixed tables)
+ * builds them once.
+ *   boundaries       HOST struct, params DEVICE (as for plsh_alibi_attention)
+ *   causal           0 or 1, as the attention calls that will read them
+ *   workspace        DEVICE, 16-byte aligned, at least
+ *                    plsh_attention_workspace_size(n, heads, s, PLSH_BF16)
+ *                    bytes; overwritten
+ *   workspace_bytes  its size in bytes
+ * Errors: PLSH_ERR_ARG (null pointer, misaligned workspace), PLSH_ERR_TABLE
+ * (n, heads or s < 1), PLSH_ERR_UNSUPPORTED (s above 255, heads above 128),
+ * PLSH_ERR_CAPACITY (workspace too small), PLSH_ERR_HIP.
+ */
+PLSH_API plsh_status plsh_alibi_records(const plsh_tables *boundaries, int32_t causal, void *workspace,
+                               int64_t workspace_bytes, plsh_stream_t stream);
+
+/*
+ * plsh_alibi_attention_from_records -- plsh_alibi_attention_ws without its
+ * pre-pass: the attention kernel alone, over records that plsh_alibi_records
+ * wrote to `workspace` for the same boundaries and causal flag (then the
+ * output is bitwise that of plsh_alibi_attention_ws).  Methodology §3
+ * (Theorem 2.2), as for plsh_alibi_attention; every argument is as for
+ * plsh_alibi_attention_ws.  bf16 with s <= 255 only (the VALU path of fp32
+ * has no records).  Records of another table or shape give a wrong estimate
+ * but no global access outside q, k, v, out and the workspace, and the call
+ * still ends: the kernel clamps every key range it reads from them and
+ * bounds every walk over their edge lists.
+ * Errors: those of plsh_alibi_attention_ws, plus PLSH_ERR_UNSUPPORTED for
+ * fp32.
+ */
+PLSH_API plsh_status plsh_alibi_attention_from_records(const void *q, const void *k, const void *v, void *out,
+                                              int32_t batch, int32_t n, int32_t heads, int32_t kv_heads,
+                                              int32_t d, plsh_dtype dtype, const double *sigma, int32_t s,
+                                              const plsh_tables *boundaries, int32_t causal,
+                                              const void *workspace, int64_t workspace_bytes,
+                                              plsh_stream_t stream);
+
+/*
  * plsh_alibi_attention_noalloc -- plsh_alibi_attention (same estimator, same
  * kernels, bitwise the same output) for callers that cannot allocate device
  * memory during the call: code under HIP graph capture, tight serving loops,

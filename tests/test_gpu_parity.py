@@ -856,3 +856,30 @@ def test_graph_capture_replays_match_eager(dev, entry):
         torch.cuda.synchronize()
         say("graph replay", entry, rep)
         assert torch.equal(out, ref), (entry, rep)
+
+
+# ------------------------------------------------- records built once -----
+@pytest.mark.parametrize("wname,causal", [("mistral-7b-n16384-s20", True), ("slopes-n4096", False),
+                                           ("graph-small", True)])
+def test_records_reused_across_calls_bitwise(dev, wname, causal):
+    """plsh_alibi_records once, then plsh_alibi_attention_from_records on
+    three different inputs: each output has the bits of the full call
+    (pre-pass + kernel) on the same inputs (the records depend only on the
+    table and the causal flag).  The small case splits its heaviest heads'
+    row groups; the n = 4096 one as well (non-causal)."""
+    import dataclasses
+    if wname == "graph-small":
+        w = small("rec-small", 1, 8, 2, 1500, 128, "bf16", causal,
+                  [1.3, 2.0, 3.0, 4.0, 40.0, 90.0, 200.0, 600.0], 11)
+    else:
+        w = dataclasses.replace(W.get(wname), causal=causal)
+    t = plsh.sample_tables(w.hash_seed, w.n, w.sigma, w.s).to(dev)
+    ws = torch.empty(plsh.workspace_size(w.n, w.heads, w.s, torch.bfloat16), dtype=torch.uint8, device=dev)
+    plsh.build_records(t, causal, ws)
+    for seed in (1, 2, 3):
+        q, k, v = (x.to(dev) for x in W.make_qkv(w, seed=seed))
+        say(w.name, "records reused", "seed", seed)
+        a = plsh.attention_from_records(q, k, v, w.sigma, w.s, t, ws, causal=causal)
+        b = plsh.attention(q, k, v, w.sigma, w.s, t, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (w.name, seed)

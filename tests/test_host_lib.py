@@ -289,6 +289,50 @@ def test_noalloc_argument_errors_before_any_device_work():
         assert call()[0] == plsh.PLSH_ERR_HIP
 
 
+def test_records_entry_points_argument_errors_before_any_device_work():
+    """plsh_alibi_records and plsh_alibi_attention_from_records refuse, before
+    any device work: null tables or workspace, a misaligned workspace, one
+    smaller than the records (PLSH_ERR_CAPACITY), s above 255, fp32 on the
+    records path (PLSH_ERR_UNSUPPORTED), a workspace overlapping out; without
+    a device the checked calls report PLSH_ERR_HIP."""
+    import torch
+    L, a, keep = _attn_args()
+    need = plsh.workspace_size(64, 4, 3, torch.bfloat16)
+    ws = 0x8000000
+
+    def rec(tables=a["tables"], w=ws, nbytes=need):
+        st = L.plsh_alibi_records(tables, 1, w, nbytes, None)
+        return st, L.plsh_last_error().decode()
+
+    def fwd(w=ws, nbytes=need, **over):
+        b = dict(a, **over)
+        st = L.plsh_alibi_attention_from_records(b["q"], b["k"], b["v"], b["out"], b["batch"], b["n"], b["heads"],
+                                                 b["kv_heads"], b["d"], b["dtype"], b["sigma"], b["s"],
+                                                 b["tables"], b["causal"], w, nbytes, None)
+        return st, L.plsh_last_error().decode()
+
+    assert rec(tables=None)[0] == plsh.PLSH_ERR_ARG
+    assert rec(w=None)[0] == plsh.PLSH_ERR_ARG
+    assert rec(w=ws + 8)[0] == plsh.PLSH_ERR_ARG
+    st, msg = rec(nbytes=need - 16)
+    assert st == plsh.PLSH_ERR_CAPACITY and "records need" in msg
+    params = np.zeros((4 * 300, 2))
+    big_s = plsh._Tables(64, 4, 300, params.ctypes.data, None, None)
+    assert rec(tables=ctypes.byref(big_s))[0] == plsh.PLSH_ERR_UNSUPPORTED
+    zero_n = plsh._Tables(0, 4, 3, params.ctypes.data, None, None)
+    assert rec(tables=ctypes.byref(zero_n))[0] == plsh.PLSH_ERR_TABLE
+
+    assert fwd(q=None)[0] == plsh.PLSH_ERR_ARG
+    assert fwd(w=None)[0] == plsh.PLSH_ERR_ARG
+    assert fwd(w=ws + 8)[0] == plsh.PLSH_ERR_ARG
+    assert fwd(nbytes=need - 16)[0] == plsh.PLSH_ERR_CAPACITY
+    assert fwd(dtype=plsh.PLSH_F32)[0] == plsh.PLSH_ERR_UNSUPPORTED
+    assert fwd(w=a["out"])[0] == plsh.PLSH_ERR_ARG  # the records would overlap out
+    if not torch.cuda.is_available():
+        assert rec()[0] == plsh.PLSH_ERR_HIP
+        assert fwd()[0] == plsh.PLSH_ERR_HIP
+
+
 def test_lse_and_saved_backward_argument_errors():
     """plsh_alibi_attention_lse and plsh_alibi_attention_backward_saved check
     their extra operands before any device work: null or misaligned lse2 /
