@@ -50,8 +50,20 @@ namespace plsh {
 namespace dev {
 
 constexpr int kFwdWaves = 4;   // waves per workgroup, one 32-row group each
-constexpr int kFwdRing = 4;    // K/V ring stages (the tile loop is written for 4)
+// K/V ring stages: 4 (two stages per barrier) for D = 64 and for launches
+// with split row groups; 3 (one stage per barrier) for D = 128 otherwise,
+// which keeps a workgroup within a third of the compute unit's LDS
+template <int D, bool SPLIT>
+constexpr int kFwdRing = (D == 128 && !SPLIT) ? 3 : 4;
 constexpr int kKeys = 32;      // keys per stage
+// Waves per SIMD the register allocation is held to: D = 64 fits four
+// (116 registers; four workgroups of 34 KB of LDS per compute unit); D = 128
+// three with the three-stage ring (168 registers, 50 KB), two with the
+// four-stage one (188 registers, 66.5 KB).  Against two at D = 64: the
+// n = 16384 Mistral-shaped layer at d = 64 takes 0.060 instead of 0.086 ms
+// (three: 0.066).
+template <int D, bool SPLIT>
+constexpr int kFwdWavesPerEu = D == 64 ? 4 : (kFwdRing<D, SPLIT> == 3 ? 3 : 2);
 constexpr int kMaxUnits = 128;
 
 struct FwdArgs {
@@ -72,9 +84,9 @@ struct FwdArgs {
   int32_t unit_info[kMaxUnits];
 };
 
-template <int D>
+template <int D, int RING>
 struct FwdLds {
-  alignas(16) uint16_t kv[kFwdRing][2][kKeys * D];
+  alignas(16) uint16_t kv[RING][2][kKeys * D];
   // step[u][4 hf + i]: word 2 i + hf of the byte counters of a tile (keys
   // 4 w .. 4 w + 3 in word w) with 1 in every key at or after offset u
   alignas(16) uint32_t step[kKeys][8];
@@ -101,9 +113,11 @@ __device__ __forceinline__ uint32_t kpos(int key, int chunk) {
 // SPLIT: the launch has units with two waves per row group (the other
 // instantiation keeps that code out of the tile loop).
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kFwdWaves, 64 * kFwdWaves), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kFwdWaves, 64 * kFwdWaves),
+                          amdgpu_waves_per_eu(kFwdWavesPerEu<D, SPLIT>, kFwdWavesPerEu<D, SPLIT>)))
 void attn_fwd_kernel(FwdArgs a) {
-  using L = FwdLds<D>;
+  constexpr int RING = kFwdRing<D, SPLIT>;
+  using L = FwdLds<D, RING>;
   __shared__ __attribute__((aligned(16))) L lds;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int s = a.s, n = a.n;
@@ -170,14 +184,27 @@ void attn_fwd_kernel(FwdArgs a) {
   }
   // ---- then the loads that need only the wave's own record and rows: the
   // lane's row of the diagonal table, the sorted edge lists (into the wave's
-  // LDS slice, 16 bytes = two edges per lane) and the 32 query rows (into
-  // ring slots 2, 3, free until the first stages have been read, whole rows
-  // per copy instruction, K-row swizzle); all land by the first stage's wait
-  u32x4 dA = {0u, 0u, 0u, 0u}, dB = {0u, 0u, 0u, 0u};
+  // LDS slice, 16 bytes = two edges per lane) and the 32 query rows; all
+  // land by the first stage's wait.  The query rows go straight to the
+  // lane's Q fragments (B operand: query t, dims 16 c + 8 hf .. + 7) with the
+  // three-stage ring, whose slots are all taken by K/V from the start, and
+  // else through ring slots 2, 3 (free until the first stages have been
+  // read; whole rows per copy instruction, K-row swizzle).
+  constexpr int NC = D / 16;  // QK^T products per stage
+  bf16x8 qf[NC];
+  if (RING == 3 && active) {
+    const uint16_t *qrow = Q + (int64_t)min(r0 + t, n - 1) * D + 8 * hf;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[c] = *(const bf16x8 *)(qrow + 16 * c);
+  }
+  // (of the row's eight table words, the lane's are 2 i + hf, i = 0..3;
+  // non-causal, the last byte too: the count after the diagonal tile)
+  uint32_t dw[4] = {0u, 0u, 0u, 0u}, dlast = 0u;
   if (active) {
-    const uint8_t *drow = rec + rec_diag_off(s) + 32 * t;
-    dA = *(const u32x4 *)drow;
-    dB = *(const u32x4 *)(drow + 16);
+    const uint32_t *drow = (const uint32_t *)(rec + rec_diag_off(s) + 32 * t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dw[i] = drow[2 * i + hf];
+    if (!CAUSAL) dlast = drow[7] >> 24;
   }
   const int nch = ev_count(s) / 2;
   u32x2 *evl = (u32x2 *)(dyn + (size_t)wave * ev_wave_bytes(s, CAUSAL));
@@ -190,11 +217,13 @@ void attn_fwd_kernel(FwdArgs a) {
     if (!CAUSAL)
       for (int c0 = 0; c0 < nch; c0 += 64)
         if (c0 + lane < nch) dma16(rec + rec_evt_off(s) + 16 * (c0 + lane), lds_addr(evt + 2 * c0));
+    if (RING == 4) {
 #pragma unroll
-    for (int c0 = 0; c0 < 32 * CPR; c0 += 64) {
-      const int row = (c0 + lane) / CPR, ch = (c0 + lane) % CPR;
-      const int64_t off = (int64_t)min(r0 + row, n - 1) * (2 * D) + 16 * (ch ^ kswz<D>(row));
-      dma16((const char *)Q + off, q_lds + 16 * c0);
+      for (int c0 = 0; c0 < 32 * CPR; c0 += 64) {
+        const int row = (c0 + lane) / CPR, ch = (c0 + lane) % CPR;
+        const int64_t off = (int64_t)min(r0 + row, n - 1) * (2 * D) + 16 * (ch ^ kswz<D>(row));
+        dma16((const char *)Q + off, q_lds + 16 * c0);
+      }
     }
   }
 
@@ -249,7 +278,6 @@ void attn_fwd_kernel(FwdArgs a) {
   if (nst > 1) issue_stage(1, 1);
 
   // ---- running state of the lane's row
-  constexpr int NC = D / 16;  // QK^T products per stage
   constexpr int NB = D / 32;  // 32-dim blocks of O^T
   floatx16 oacc[NB];
 #pragma unroll
@@ -261,7 +289,6 @@ void attn_fwd_kernel(FwdArgs a) {
   int pl = 0, pt = 0;    // their positions (wave-uniform)
   int lg_base = -1;      // the count whose log2 is lg
   float lg = 0.f;
-  bf16x8 qf[NC];
   auto pos_at = [&](const u32x2 *ev, int i) { return (int32_t)__builtin_amdgcn_readfirstlane(ev[i][0]); };
 
   // K operand of product c: key t, chunk 2 c + hf
@@ -281,36 +308,23 @@ void attn_fwd_kernel(FwdArgs a) {
   const int sa = active ? (U0w - U0) / kKeys : 0;
   const int sb = active ? (U1w - U0) / kKeys : 0;
 
-  // a5: S^T = K Q^T for the stages in ring slots Q0 (and Q1): every K
-  // fragment read is issued first, then the products; with two tiles their
-  // two accumulation chains alternate, so no product waits for the previous
-  // one of its own chain
-  auto qk_tiles = [&](auto s0, auto s1, bool two, floatx16 &SA, floatx16 &SB) {
+  // a5: S^T = K Q^T for the stage in ring slot Q0: the K fragment reads of
+  // a group are issued first, then its products (one group; two with the
+  // three-stage ring, whose register budget holds half the fragments)
+  auto qk_tile = [&](auto s0, floatx16 &SA) {
     const char *ka = (const char *)lds.kv[decltype(s0)::value][0];
-    const char *kb = (const char *)lds.kv[decltype(s1)::value][0];
-    u32x4 kra[NC], krb[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) kra[c] = *(const u32x4 *)(ka + kofs[c]);
-    if (two) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) krb[c] = *(const u32x4 *)(kb + kofs[c]);
-    }
+    constexpr int KG = RING == 3 ? NC / 2 : NC;  // fragments per group
     SA = floatx16{};
-    SB = floatx16{};
-    if (two) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        SA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kra[c]), qf[c], SA, 0, 0, 0);
-        SB = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, krb[c]), qf[c], SB, 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NC, 0);  // every K read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NC, 0);  // then the products
-    } else {
+    for (int g0 = 0; g0 < NC; g0 += KG) {
+      u32x4 kra[KG];
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        SA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kra[c]), qf[c], SA, 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, NC, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NC, 0);
+      for (int c = 0; c < KG; ++c) kra[c] = *(const u32x4 *)(ka + kofs[g0 + c]);
+#pragma unroll
+      for (int c = 0; c < KG; ++c)
+        SA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kra[c]), qf[g0 + c], SA, 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, KG, 0);  // the group's K reads
+      __builtin_amdgcn_sched_group_barrier(0x008, KG, 0);  // then its products
     }
   };
 
@@ -349,7 +363,7 @@ void attn_fwd_kernel(FwdArgs a) {
     if (j0 == r0) {
       // the lane's words 2 i + hf of its row of the record's table (loaded
       // in the prologue; landed by the first stage's wait)
-      uint32_t d0 = hf ? dA[1] : dA[0], d1 = hf ? dA[3] : dA[2], d2 = hf ? dB[1] : dB[0], d3 = hf ? dB[3] : dB[2];
+      uint32_t d0 = dw[0], d1 = dw[1], d2 = dw[2], d3 = dw[3];
       asm volatile("" : "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3));
       const uint32_t dd[4] = {d0, d1, d2, d3};
 #pragma unroll
@@ -358,7 +372,7 @@ void attn_fwd_kernel(FwdArgs a) {
       edges_in_tile(evl, lp, pl, jend, [](int, uint32_t) {});
       if (!CAUSAL) {
         edges_in_tile(evt, tp, pt, jend, [](int, uint32_t) {});
-        base = (int)(dB[3] >> 24);  // c(row, r0 + 31): the count after the diagonal tile
+        base = (int)dlast;  // c(row, r0 + 31): the count after the diagonal tile
       }
       kind = 1;
     } else if (pl < jend || (!CAUSAL && pt < jend)) {
@@ -474,7 +488,7 @@ void attn_fwd_kernel(FwdArgs a) {
       edges_in_tile(evl, lp, pl, jend, [](int, uint32_t) {});
       if (!CAUSAL) {
         edges_in_tile(evt, tp, pt, jend, [](int, uint32_t) {});
-        base = (int)(dB[3] >> 24);
+        base = (int)dlast;
       }
     } else {
       edges_in_tile(evl, lp, pl, jend, [&](int, uint32_t W) { base += (int)((W >> t) & 1u); });
@@ -505,28 +519,68 @@ void attn_fwd_kernel(FwdArgs a) {
         if (!CAUSAL) pt = pos_at(evt, 0);
       }
     }
-    if (st + 2 < nst) issue_stage(st + 2, (decltype(s0)::value + 2) % kFwdRing);
-    if (st + 3 < nst) issue_stage(st + 3, (decltype(s1)::value + 2) % kFwdRing);
+    if (st + 2 < nst) issue_stage(st + 2, (decltype(s0)::value + 2) % RING);
+    if (st + 3 < nst) issue_stage(st + 3, (decltype(s1)::value + 2) % RING);
     // (split groups: part 0 computes stage st, part 1 stage st + 1, and each
     // moves its count past the other's)
     const bool ra = st >= sa && st < sb;
     const bool rb = st + 1 < nst && st + 1 >= sa && st + 1 < sb;
     const bool ta = ra && part == 0, tb = rb && (!split || part == 1);
-    floatx16 SA, SB;
+    floatx16 SA;
     if (ra && part == 1) skip_tile(st);
     if (ta) {
-      qk_tiles(s0, s0, false, SA, SB);
+      qk_tile(s0, SA);
       finish_tile(st, s0, SA);
     }
     if (rb && split && part == 0) skip_tile(st + 1);
     if (tb) {
-      qk_tiles(s1, s1, false, SA, SB);
+      qk_tile(s1, SA);
       finish_tile(st + 1, s1, SA);
     }
   };
-  for (int st0 = 0; st0 < nst; st0 += kFwdRing) {
-    pair(st0, Slot<0>{}, Slot<1>{});
-    if (st0 + 2 < nst) pair(st0 + 2, Slot<2>{}, Slot<3>{});
+  // One stage per barrier (three-stage ring): stage st waits for its own
+  // copies only (those of st + 1, issued after them, may still be in
+  // flight: copies complete in issue order), refills the slot of stage
+  // st - 1 (every wave is past it) with st + 2, and computes its tile.
+  auto single = [&](int st, auto s0) {
+    if (st + 1 < nst) PLSH_WAIT_VM_LGKM0(2 * NCW);
+    else PLSH_WAIT_VM_LGKM0(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st == 0 && active) {  // the edge lists landed before stage 0
+      pl = pos_at(evl, 0);
+      if (!CAUSAL) pt = pos_at(evt, 0);
+    }
+    if (st + 2 < nst) issue_stage(st + 2, (decltype(s0)::value + 2) % RING);
+    if (st >= sa && st < sb) {
+      floatx16 SA;
+      qk_tile(s0, SA);
+      finish_tile(st, s0, SA);
+    }
+  };
+  if constexpr (RING == 3) {
+    // the first stage's wait, and with it the Q fragments and the table
+    // words, ahead of the loop: the compiler, which does not see the
+    // copies, then counts those loads as done inside it (else it waits on
+    // them at every tile, and with them on the later stages' copies)
+    if (nst > 1) PLSH_WAIT_VM_LGKM0(2 * NCW);
+    else PLSH_WAIT_VM_LGKM0(0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qf[c]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(dw[i]));
+    asm volatile("" : "+v"(dlast));
+    for (int st0 = 0; st0 < nst; st0 += 3) {
+      single(st0, Slot<0>{});
+      if (st0 + 1 < nst) single(st0 + 1, Slot<1>{});
+      if (st0 + 2 < nst) single(st0 + 2, Slot<2>{});
+    }
+  } else {
+    for (int st0 = 0; st0 < nst; st0 += 4) {
+      pair(st0, Slot<0>{}, Slot<1>{});
+      if (st0 + 2 < nst) pair(st0 + 2, Slot<2>{}, Slot<3>{});
+    }
   }
 
   // ---- split row groups: the part-1 wave hands its partial sums (running
@@ -574,17 +628,25 @@ void attn_fwd_kernel(FwdArgs a) {
     }
   }
 
-  // ---- a8: O = acc / l, rounded to bf16, staged in the two ring slots the
-  // last pair does not use (every wave is past them; split groups: slots 2,
-  // 3, past the merge's barrier) and stored whole rows per instruction
+  // ---- a8: O = acc / l, rounded to bf16, staged in two ring slots no wave
+  // still reads (four stages: the two the last pair does not use; three: those
+  // of the last stage's two predecessors, every wave being past both; split
+  // groups: slots 2, 3, past the merge's barrier) and stored whole rows per
+  // instruction
   if (!active) return;
   const float ltot = lsum + other_half_f(lsum, lane);
   const float inv = 1.0f / ltot;
   const int ns = 32 * a.g32;
   if (a.save_lse2 && hf == 0)
     a.save_lse2[((int64_t)b * a.heads + h) * ns + r0 + t] = r0 + t < n ? m2 + __log2f(ltot) : 0.f;
-  const int free_slot = split ? 2 : ((((nst - 1) >> 1) & 1) ? 0 : 2);
-  char *ob = (char *)lds.kv[free_slot][0] + (split ? wg_grp : wave) * 32 * D * 2;
+  char *ob;
+  if constexpr (RING == 3) {
+    const int last = nst > 0 ? (nst - 1) % 3 : 2;
+    ob = (char *)lds.kv[(last + 1 + (wave >> 1)) % 3][0] + (wave & 1) * 32 * D * 2;
+  } else {
+    const int free_slot = split ? 2 : ((((nst - 1) >> 1) & 1) ? 0 : 2);
+    ob = (char *)lds.kv[free_slot][0] + (split ? wg_grp : wave) * 32 * D * 2;
+  }
 #pragma unroll
   for (int db = 0; db < NB; ++db)
 #pragma unroll
