@@ -113,6 +113,32 @@ __device__ __forceinline__ void dma16(const void *gsrc, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// Buffer resource (gfx9 descriptor) for `bytes` bytes from `base`: raw
+// addressing, no stride; reads at offsets past the end return zeros.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+  r[3] = 0x00020000;  // 32-bit data format, the untyped loads ignore it
+  return r;
+}
+
+// The same copy as dma16 through a buffer resource: lane l's 16 bytes at
+// offset voff (lane) + soff (wave-uniform) of the resource land at
+// lds_base + 16 l; offsets past the resource's end give zeros.  Only the
+// scalar offset changes between the stages of a ring, so a stage's copies
+// take no vector address arithmetic.
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(m0)
+               : "memory", "m0");
+}
+
 // s_waitcnt with vmcnt <= v and lgkmcnt == 0 (gfx9 encoding)
 #define PLSH_WAIT_VM_LGKM0(v) __builtin_amdgcn_s_waitcnt(((v) & 15) | (((v) >> 4) << 14) | (7 << 4))
 

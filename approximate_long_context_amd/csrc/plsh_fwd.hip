@@ -248,30 +248,29 @@ void attn_fwd_kernel(FwdArgs a) {
 
   // ---- K/V staging: a K tile is 32 whole rows (K-row swizzle), a V tile 32
   // keys x D as 64-byte pieces per 32 dims (vpiece128); each tile is 4 D
-  // 16-byte chunks, wave w copies chunks [w D, (w + 1) D).  Keys past the
-  // end read row n - 1, whose products get c = 0.
+  // 16-byte chunks, wave w copies chunks [w D, (w + 1) D).  The copies go
+  // through buffer resources over the head's K and V rows: the lane's offset
+  // inside a tile is fixed, the tile's start is a scalar offset, and keys
+  // past the end read as zeros, whose products get c = 0.
   constexpr int NCW = D / 64;  // copy instructions per wave, tile and stage
   const uint32_t kv_lds = lds_addr(&lds.kv[0][0][0]);
-  int ck_key[NCW], ck_off[NCW], cv_key[NCW], cv_off[NCW];
+  const i32x4 krs = buffer_rsrc(Kb, (uint32_t)n * (2 * D)), vrs = buffer_rsrc(Vb, (uint32_t)n * (2 * D));
+  uint32_t ck_off[NCW], cv_off[NCW];
 #pragma unroll
   for (int j = 0; j < NCW; ++j) {
     const int ci = wave * D + 64 * j + lane;  // the lane's chunk position in the tile
-    ck_key[j] = ci / CPR;
-    ck_off[j] = 16 * ((ci % CPR) ^ kswz<D>(ci / CPR));
+    ck_off[j] = (uint32_t)((ci / CPR) * (2 * D) + 16 * ((ci % CPR) ^ kswz<D>(ci / CPR)));
     const int P = 16 * ci;
     const int vkey = (P >> 6) & 31;
-    cv_key[j] = vkey;
-    cv_off[j] = 16 * (4 * (P >> 11) + (((P >> 4) & 3) ^ (((vkey >> 2) & 1) << 1)));
+    cv_off[j] = (uint32_t)(vkey * (2 * D) + 16 * (4 * (P >> 11) + (((P >> 4) & 3) ^ (((vkey >> 2) & 1) << 1))));
   }
   auto issue_stage = [&](int st, int q) {  // q = st % kFwdRing
-    const int j0 = U0 + kKeys * st;
+    const uint32_t soff = (uint32_t)(U0 + kKeys * st) * (2 * D);
 #pragma unroll
     for (int j = 0; j < NCW; ++j) {
-      const int64_t krow = (int64_t)min(j0 + ck_key[j], n - 1) * (2 * D);
-      const int64_t vrow = (int64_t)min(j0 + cv_key[j], n - 1) * (2 * D);
       const uint32_t dst = kv_lds + (uint32_t)(2 * q) * (kKeys * D * 2) + 16 * (wave * D + 64 * j);
-      dma16(Kb + krow + ck_off[j], dst);
-      dma16(Vb + vrow + cv_off[j], dst + kKeys * D * 2);
+      dma16_buf(krs, ck_off[j], soff, dst);
+      dma16_buf(vrs, cv_off[j], soff, dst + kKeys * D * 2);
     }
   };
   if (nst > 0) issue_stage(0, 0);
@@ -733,6 +732,11 @@ static std::vector<int> split_units(const FwdCall &c, size_t nunits, HW hw_of, K
 
 plsh_status launch_fwd(const FwdCall &c, hipStream_t st, std::pair<hipEvent_t, hipEvent_t> *timer,
                        const char *who) {
+  // (a head's K or V rows, up to the last tile's end, are addressed through
+  // 32-bit buffer offsets)
+  if (((int64_t)c.n + 31) * 2 * c.d >= ((int64_t)1 << 32))
+    return fail(PLSH_ERR_UNSUPPORTED, "%s: n = %d exceeds %lld at d = %d", who, c.n,
+                (long long)(((int64_t)1 << 32) / (2 * c.d) - 32), c.d);
   if (c.heads > dev::kMaxUnits) return fail(PLSH_ERR_UNSUPPORTED, "%s: heads = %d exceeds %d", who, c.heads, dev::kMaxUnits);
   dev::FwdArgs a;
   a.q = (const uint16_t *)c.q;
