@@ -346,7 +346,8 @@ void attn_fwd_kernel(FwdArgs a) {
   };
 
   // a4, a6, a7 for the stage in ring slot Q, whose logits are in sacc
-  auto finish_tile = [&](int st, auto slotc, const floatx16 &sacc) {
+  auto finish_tile = [&](int st, auto slotc, const floatx16 &sacc_in) {
+    floatx16 sacc = sacc_in;
     const char *vt = (const char *)lds.kv[decltype(slotc)::value][1];
     const int j0 = U0 + kKeys * st;
     const int jend = j0 + kKeys;
@@ -367,6 +368,13 @@ void attn_fwd_kernel(FwdArgs a) {
       const uint32_t dd[4] = {d0, d1, d2, d3};
 #pragma unroll
       for (int r = 0; r < 16; ++r) cf[r] = (float)((dd[r >> 2] >> (8 * (r & 3))) & 0xFFu);
+      // keys of the tile outside the row's blocks (causal: the keys after
+      // the row) leave the running max and the weights: their logits, which
+      // may be far above the row's own, would otherwise raise the max until
+      // the row's weights underflow.  The row's own key always counts s, so
+      // the max stays finite.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = cf[r] > 0.f ? sacc[r] : -INFINITY;
       // the table already counts every edge up to the tile's end
       edges_in_tile(evl, lp, pl, jend, [](int, uint32_t) {});
       if (!CAUSAL) {

@@ -355,6 +355,33 @@ def test_g7_huge_sigma_is_softmax_attention(dev, causal):
     check_bf16(out.cpu().double().numpy(), ref.double().numpy(), what="G7")
 
 
+@pytest.mark.parametrize("sigma", [2.0, 64.0])
+def test_causal_later_keys_do_not_take_the_rows_max(dev, sigma):
+    """Logits that rise by 100 per key position (q_i . k_j = 100 j): in the
+    diagonal tile the keys after row i would raise a running max taken over
+    the whole 32-key tile about 144 binary orders above the row's own logits,
+    so that its weights underflow and the row turns to 0/0.  Causal, the
+    estimate is then about v_i.  GPU output finite and within the bf16 bar of
+    the oracle."""
+    n, d = 96, 128
+    w = small("ramp", 1, 2, 1, n, d, "bf16", True, [sigma, sigma], 4)
+    e0 = torch.zeros(d)
+    e0[0] = 1.0
+    j = torch.arange(n, dtype=torch.float32)
+    q = (10.0 * e0).expand(1, 2, n, d).contiguous().to(torch.bfloat16)
+    k = (10.0 * j[:, None] * e0[None, :]).expand(1, 1, n, d).contiguous().to(torch.bfloat16)
+    v = torch.randn((1, 1, n, d), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    t = plsh.sample_tables(3, n, w.sigma, w.s)
+    out = plsh.attention(q.to(dev), k.to(dev), v.to(dev), w.sigma, w.s, t.to(dev), causal=True)
+    torch.cuda.synchronize()
+    o = W.to_f64(out)
+    assert np.isfinite(o).all()
+    off, st = orc.tables_from_params(n, t.params)
+    tabs = orc.starts_per_head(off, st, w.heads, w.s)
+    ref = orc.lsh_estimate(W.to_f64(q), W.to_f64(k), W.to_f64(v), tabs, True)
+    check_bf16(o, ref, what=f"ramp sigma={sigma}")
+
+
 def test_error_after_bad_call_leaves_no_work(dev):
     w = small("err", 1, 2, 1, 64, 64, "bf16", True, [2.0, 3.0], 3)
     q, k, v = W.make_qkv(w)
