@@ -61,6 +61,10 @@ plsh_status check_common(const void *q, const void *k, const void *v, void *out,
   if ((int64_t)batch * heads * n * d >= ((int64_t)1 << 31) ||
       (int64_t)batch * kv_heads * n * d >= ((int64_t)1 << 31))
     return fail(PLSH_ERR_UNSUPPORTED, "%s: tensor has >= 2^31 elements", who);
+  // (the bf16 kernels address a head's K or V rows, up to the last 32-row
+  // tile's end, through 32-bit buffer offsets)
+  if (dtype == PLSH_BF16 && ((int64_t)n + 31) * d * 2 >= ((int64_t)1 << 32))
+    return fail(PLSH_ERR_UNSUPPORTED, "%s: n = %d too long for d = %d in bf16", who, n, d);
   if (!bt->params) return fail(PLSH_ERR_ARG, "%s: boundaries->params is null", who);
   if (bt->n != n || bt->heads != heads || bt->s != s)
     return fail(PLSH_ERR_TABLE, "%s: boundaries (n=%d, heads=%d, s=%d) do not match the call (n=%d, heads=%d, s=%d)",
@@ -277,6 +281,10 @@ plsh_status check_exact(const void *q, const void *k, const void *v, void *out, 
   if ((int64_t)batch * heads * n * d >= ((int64_t)1 << 31) ||
       (int64_t)batch * kv_heads * n * d >= ((int64_t)1 << 31))
     return fail(PLSH_ERR_UNSUPPORTED, "%s: tensor has >= 2^31 elements", who);
+  // (the bf16 kernels address a head's K or V rows, up to the last 32-row
+  // tile's end, through 32-bit buffer offsets)
+  if (dtype == PLSH_BF16 && ((int64_t)n + 31) * d * 2 >= ((int64_t)1 << 32))
+    return fail(PLSH_ERR_UNSUPPORTED, "%s: n = %d too long for d = %d in bf16", who, n, d);
   if ((int64_t)((n + 127) / 128) * batch * heads >= ((int64_t)1 << 31))
     return fail(PLSH_ERR_UNSUPPORTED, "%s: too many row tiles", who);
   const size_t qbytes = (size_t)batch * heads * n * d * 2;

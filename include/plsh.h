@@ -187,8 +187,8 @@ PLSH_API plsh_status plsh_count_work(const plsh_tables *host_tables, int32_t cau
  * Errors: PLSH_ERR_ARG (null pointer, n < 1, batch < 1, heads or kv_heads < 1,
  * heads % kv_heads != 0, s < 1, sigma not finite or <= 0, aliasing),
  * PLSH_ERR_TABLE (boundaries mismatch), PLSH_ERR_UNSUPPORTED (d not 64/128,
- * batch*heads*n*d >= 2^31, s > 255), PLSH_ERR_HIP (launch error, workspace
- * allocation failure).  Execution
+ * batch*heads*n*d >= 2^31, bf16 with (n + 31)*d*2 >= 2^32, s > 255),
+ * PLSH_ERR_HIP (launch error, workspace allocation failure).  Execution
  * faults surface at the caller's next synchronisation.
  */
 PLSH_API plsh_status plsh_alibi_attention(const void *q, const void *k, const void *v, void *out,

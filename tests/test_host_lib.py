@@ -181,6 +181,17 @@ def test_attention_argument_errors(over, status):
     assert msg
 
 
+def test_attention_rejects_n_beyond_32bit_row_offsets():
+    """bf16 reaches a head's K/V rows through 32-bit byte offsets up to the
+    end of the last 32-row tile; an n within 31 rows of that limit is refused
+    before any device work, although the tensor is under 2^31 elements."""
+    n = (1 << 24) - 1  # n * 128 < 2^31, (n + 31) * 128 * 2 > 2^32
+    st, msg = _call(n=n, heads=1, kv_heads=1, d=128)
+    assert st == plsh.PLSH_ERR_UNSUPPORTED and "too long" in msg, msg
+    st, msg = _call(n=n, heads=1, kv_heads=1, d=128, dtype=plsh.PLSH_F32)
+    assert st != plsh.PLSH_ERR_UNSUPPORTED, msg
+
+
 def test_attention_table_mismatch():
     L, a, keep = _attn_args()
     sig, params, _ = keep
