@@ -126,13 +126,18 @@ void exact_fwd_kernel(ExactArgs a) {
   }
 
   // ---- K/V stages [0, nst): keys [0, U1) for the workgroup; this wave
-  // computes stages [0, sb).  A K tile is 32 whole rows (K-row swizzle), a V
+  // computes stages [sa, sb).  A K tile is 32 whole rows (K-row swizzle), a V
   // tile 32 keys x D as 64-byte pieces per 32 dims (vpiece128); wave w copies
   // the tile's 16-byte chunks [w D, (w + 1) D).  Keys past the end read as
   // zeros through the buffer resource and are masked.
   const int U1 = CAUSAL ? min(n, g * 128 + 128) : n;
   const int nst = (U1 + kExKeys - 1) / kExKeys;
-  const int sb = !active ? 0 : CAUSAL ? r0 / kExKeys + 1 : nst;
+  // causal: stage st holds key tile nst - 1 - st (from the diagonal down to
+  // key 0), so each row meets its largest biases first and the running max
+  // rarely rises later; a wave's tiles are stages [sa, nst)
+  auto key_tile = [&](int st) { return CAUSAL ? nst - 1 - st : st; };
+  const int sa = !active ? nst : CAUSAL ? nst - 1 - r0 / kExKeys : 0;
+  const int sb = !active ? 0 : nst;
   constexpr int CPR = D / 8;   // 16-byte chunks per row
   constexpr int NCW = D / 64;  // copy instructions per wave, tile and stage
   const uint32_t kv_lds = lds_addr(&kv[0][0][0]);
@@ -147,7 +152,7 @@ void exact_fwd_kernel(ExactArgs a) {
     cv_off[j] = (uint32_t)(vkey * (2 * D) + 16 * (4 * (P >> 11) + (((P >> 4) & 3) ^ (((vkey >> 2) & 1) << 1))));
   }
   auto issue_stage = [&](int st, int q) {  // q = st % kExRing
-    const uint32_t soff = (uint32_t)(kExKeys * st) * (2 * D);
+    const uint32_t soff = (uint32_t)(kExKeys * key_tile(st)) * (2 * D);
 #pragma unroll
     for (int j = 0; j < NCW; ++j) {
       const uint32_t dst = kv_lds + (uint32_t)(2 * q) * (kExKeys * D * 2) + 16 * (wave * D + 64 * j);
@@ -229,15 +234,14 @@ void exact_fwd_kernel(ExactArgs a) {
   // softmax and PV of stage st (ring slot slotc), logits in SA
   auto finish_tile = [&](int st, auto slotc, const floatx16 &SA) {
     const char *vt = (const char *)kv[decltype(slotc)::value][1];
-    const int j0 = kExKeys * st;
+    const int j0 = kExKeys * key_tile(st);
     const bool plain = j0 < r0 && j0 + kExKeys <= n;
     // the tile's logits in log2 units are fma(x, sc, off)
-    float x[16], sc, off;
+    floatx16 x = SA;
+    float sc, off;
     const float tb = slope2 * (float)(j0 - r0);
     if (__builtin_amdgcn_readfirstlane(plain)) {
       // keys left of the wave's rows: log2(e) SA + slope2 (j0 - r0)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = SA[r];
       sc = kLog2e;
       off = tb;
     } else {
@@ -251,14 +255,14 @@ void exact_fwd_kernel(ExactArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const bool left = (dmask >> r) & 1u;
-          x[r] = fmaf(SA[r], kLog2e, left ? tb : CAUSAL ? -INFINITY : right(r));
+          x[r] = fmaf(x[r], kLog2e, left ? tb : CAUSAL ? -INFINITY : right(r));
         }
       } else if (CAUSAL || j0 < r0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = fmaf(SA[r], kLog2e, tb);
+        for (int r = 0; r < 16; ++r) x[r] = fmaf(x[r], kLog2e, tb);
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = fmaf(SA[r], kLog2e, right(r));
+        for (int r = 0; r < 16; ++r) x[r] = fmaf(x[r], kLog2e, right(r));
       }
       if (!CAUSAL && j0 + kExKeys > n) {
         const int lim = n - j0 - 4 * hf;  // c_r >= lim: the key is past the end
@@ -320,7 +324,7 @@ void exact_fwd_kernel(ExactArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (st + 2 < nst) issue_stage(st + 2, (decltype(s0)::value + 2) % kExRing);
-    if (st < sb) {
+    if (st >= sa && st < sb) {
       floatx16 SA;
       qk_tile(s0, SA);
       finish_tile(st, s0, SA);
