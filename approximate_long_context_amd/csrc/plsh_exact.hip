@@ -132,10 +132,13 @@ void exact_fwd_kernel(ExactArgs a) {
   // zeros through the buffer resource and are masked.
   const int U1 = CAUSAL ? min(n, g * 128 + 128) : n;
   const int nst = (U1 + kExKeys - 1) / kExKeys;
-  // causal: stage st holds key tile nst - 1 - st (from the diagonal down to
-  // key 0), so each row meets its largest biases first and the running max
-  // rarely rises later; a wave's tiles are stages [sa, nst)
-  auto key_tile = [&](int st) { return CAUSAL ? nst - 1 - st : st; };
+  // The bias is largest at a row's own key, so the stream starts at the
+  // workgroup's last diagonal tile dt and runs down to key 0 (causal: the
+  // whole stream; a wave's tiles are stages [sa, nst)), then, without the
+  // causal mask, on from dt + 1 to the end: each row meets its largest
+  // biases within its first stages and the running max rarely rises later.
+  const int dt = min(g * 4 + 3, nst - 1);
+  auto key_tile = [&](int st) { return st <= dt ? dt - st : st; };
   const int sa = !active ? nst : CAUSAL ? nst - 1 - r0 / kExKeys : 0;
   const int sb = !active ? 0 : nst;
   constexpr int CPR = D / 8;   // 16-byte chunks per row
