@@ -99,7 +99,6 @@ void fill_args(dev::AttnArgs &a, const void *q, const void *k, const void *v, vo
   a.dout = nullptr;
   a.lse2 = nullptr;
   a.dvec = nullptr;
-  a.stat_lse2 = nullptr;
   a.stat_dvec = nullptr;
   a.save_lse2 = nullptr;
   a.saved_out = nullptr;
@@ -157,6 +156,45 @@ plsh_status scratch_ptr(const char *who, void **out) {
   return PLSH_OK;
 }
 
+// Workspaces of the allocating entry points come, stream-ordered, from a
+// memory pool of the library's own on each device.  The pool keeps up to
+// kPoolKeepBytes of released memory for later calls; the device's default
+// pool returns it to the driver at every synchronisation, so that each call
+// mapped its workspace afresh (the backward from a saved forward, 16k
+// Mistral-shaped layer, synchronised per call: 0.74 ms, 0.56 ms from a pool
+// that keeps its memory).
+constexpr uint64_t kPoolKeepBytes = (uint64_t)1 << 30;
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kMaxScratchDevices] = {};
+
+hipError_t pool_alloc(void **p, size_t bytes, hipStream_t st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipMallocAsync(p, bytes, st);
+  hipMemPool_t pool = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    if (!g_pool[dev]) {
+      hipMemPoolProps props = {};
+      props.allocType = hipMemAllocationTypePinned;
+      props.handleTypes = hipMemHandleTypeNone;
+      props.location.type = hipMemLocationTypeDevice;
+      props.location.id = dev;
+      hipMemPool_t created = nullptr;
+      if ((e = hipMemPoolCreate(&created, &props)) != hipSuccess) return e;
+      uint64_t keep = kPoolKeepBytes;
+      if ((e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
+        (void)hipMemPoolDestroy(created);
+        return e;
+      }
+      g_pool[dev] = created;
+    }
+    pool = g_pool[dev];
+  }
+  return hipMallocFromPoolAsync(p, bytes, pool, st);
+}
+
 // the event pair for the next timed launch, or nullptr when timing is off
 
 }  // namespace
@@ -180,12 +218,12 @@ namespace {
 // bytes of the block-edge records of every (head, 32-row group)
 size_t records_bytes(int n, int heads, int s) { return (size_t)heads * ((n + 31) / 32) * dev::rec_bytes(s); }
 
-// The records into a workspace from the stream-ordered allocator (released by
+// The records into a workspace from the library's pool (released by
 // free_records).
 plsh_status build_records(const dev::AttnArgs &a, bool causal, hipStream_t st, const char *who, void **ws) {
   const size_t ws_bytes = records_bytes(a.n, a.heads, a.s);
   *ws = nullptr;
-  hipError_t e = hipMallocAsync(ws, ws_bytes, st);
+  hipError_t e = pool_alloc(ws, ws_bytes, st);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     *ws = nullptr;
@@ -196,13 +234,13 @@ plsh_status build_records(const dev::AttnArgs &a, bool causal, hipStream_t st, c
 }
 
 // Causal and non-causal records in one pre-pass (the causal backward's two
-// record sets), each in its own workspace from the stream-ordered allocator.
+// record sets), each in its own workspace from the library's pool.
 plsh_status build_record_pair(const dev::AttnArgs &a, hipStream_t st, const char *who, void **ws_causal,
                               void **ws_nc) {
   const size_t ws_bytes = records_bytes(a.n, a.heads, a.s);
   *ws_causal = *ws_nc = nullptr;
   for (void **p : {ws_causal, ws_nc}) {
-    const hipError_t e = hipMallocAsync(p, ws_bytes, st);
+    const hipError_t e = pool_alloc(p, ws_bytes, st);
     if (e != hipSuccess) {
       (void)hipGetLastError();
       *p = nullptr;
@@ -511,7 +549,7 @@ extern "C" plsh_status plsh_alibi_attention_unfused(const void *q, const void *k
   const int64_t rows = (int64_t)batch * heads * n;
   const size_t bytes = (size_t)s * rows * ((size_t)d + 1) * sizeof(float);
   void *ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, hs);
+  hipError_t e = pool_alloc(&ws, bytes, hs);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(PLSH_ERR_HIP, "%s: partials allocation of %zu bytes failed: %s", who, bytes, hipGetErrorString(e));
@@ -567,10 +605,10 @@ extern "C" plsh_status plsh_alibi_attention_walk(const void *q, const void *k, c
   return free_records(rec, hs, who, rc);
 }
 
-// Gradients of the estimate for fixed tables (see include/plsh.h).
-// The backward of the estimate for fixed tables.  With saved_out and
-// saved_lse2 (the output and row statistics of plsh_alibi_attention_lse) the
-// statistics pass is replaced by D = dO . O from the saved output.
+// The backward of the estimate for fixed tables (see include/plsh.h).  With
+// saved_out and saved_lse2 (the output and row normalisers of
+// plsh_alibi_attention_lse) no forward runs; without them the call first
+// runs that forward into a buffer of its own.
 static plsh_status backward_common(const char *who, const void *q, const void *k, const void *v,
                                    const void *dout, void *dq, void *dk, void *dv, int32_t batch, int32_t n,
                                    int32_t heads, int32_t kv_heads, int32_t d, plsh_dtype dtype,
@@ -606,40 +644,46 @@ static plsh_status backward_common(const char *who, const void *q, const void *k
   if ((st = have_device(who)) != PLSH_OK) return st;
   hipStream_t hs = (hipStream_t)stream;
   const int64_t prows = (int64_t)batch * heads * ns;
-  const size_t bytes = (saved ? 1 : 2) * (size_t)prows * sizeof(float);
+  // the recomputing backward first runs the forward that writes each row's
+  // normaliser, into an output of its own, and then proceeds as from that
+  // saved forward: [O (bf16, as q)][lse2][D]; from a saved forward only [D]
+  const size_t obytes = saved ? 0 : ((size_t)batch * heads * n * d * 2 + 255) & ~(size_t)255;
+  const size_t bytes = obytes + (saved ? 1 : 2) * (size_t)prows * sizeof(float);
   void *stats = nullptr;
-  hipError_t e = hipMallocAsync(&stats, bytes, hs);
+  hipError_t e = pool_alloc(&stats, bytes, hs);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(PLSH_ERR_HIP, "%s: statistics allocation of %zu bytes failed: %s", who, bytes, hipGetErrorString(e));
   }
-  const float *lse2 = saved ? saved_lse2 : (const float *)stats;
-  float *dvec = saved ? (float *)stats : (float *)stats + prows;
+  float *tail = (float *)((char *)stats + obytes);
+  const void *out_used = saved ? saved_out : stats;
+  const float *lse2 = saved ? saved_lse2 : tail;
+  float *dvec = saved ? tail : tail + prows;
   dev::AttnArgs a;
   fill_args(a, q, k, v, dq, batch, n, heads, kv_heads, sigma, s, boundaries);
   a.dout = dout;
   plsh_status rc = PLSH_OK;
-  // the records of the estimator serve its statistics pass and dQ; dK/dV
-  // takes non-causal ones (the same records when the call is not causal;
-  // a causal call gets both sets from one pre-pass)
+  // the records of the estimator serve its forward and dQ; dK/dV takes
+  // non-causal ones (the same records when the call is not causal; a causal
+  // call gets both sets from one pre-pass)
   void *rec = nullptr, *rec_nc = nullptr;
   if (rc == PLSH_OK) {
     if (causal) rc = build_record_pair(a, hs, who, &rec, &rec_nc);
     else rc = build_records(a, false, hs, who, &rec);
   }
   if (rc == PLSH_OK && !saved) {
-    // statistics: each row's normaliser and D = dO . O
-    a.stat_lse2 = (float *)stats;
-    a.stat_dvec = dvec;
-    rc = launch_attn(a, d, causal != 0, hs, who, 0, rec);
+    // the forward with each row's normaliser (the forward kernel over the
+    // records just built)
+    dev::AttnArgs f = a;
+    f.out = stats;
+    f.save_lse2 = tail;
+    rc = launch_mfma(f, sigma, d, causal != 0, hs, who, rec, true);
   }
   if (rc == PLSH_OK) {
-    // dQ; from a saved forward it also forms D = dO . O into dvec
-    a.stat_lse2 = nullptr;
-    a.stat_dvec = saved ? dvec : nullptr;
-    a.saved_out = saved ? saved_out : nullptr;
+    // dQ; it also forms D = dO . O from the forward's output into dvec
+    a.stat_dvec = dvec;
+    a.saved_out = out_used;
     a.lse2 = lse2;
-    a.dvec = saved ? nullptr : dvec;
     rc = launch_attn(a, d, causal != 0, hs, who, 1, rec);
     a.stat_dvec = nullptr;
     a.saved_out = nullptr;

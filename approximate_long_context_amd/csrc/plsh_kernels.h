@@ -33,20 +33,18 @@ struct AttnArgs {
   // backward: the upstream gradient dO ([batch, heads, n, d], the dtype of
   // q), each row's normaliser in log2 units lse2 = log2 sum_j c_ij 2^(q_i.k_j
   // log2 e), and D_i = dO_i . O_i, both [batch, heads, ns] with ns = n rounded
-  // up to a multiple of 32 (rows n .. ns - 1 hold 0).  When stat_lse2 is set
-  // the MFMA kernel writes these two arrays (stat_lse2, stat_dvec) instead of
-  // out; the dQ and dK/dV kernels read them (lse2, dvec).
+  // up to a multiple of 32 (rows n .. ns - 1 hold 0); the dQ and dK/dV
+  // kernels read them (lse2, dvec).
   const void *dout;
   const float *lse2;
   const float *dvec;
-  float *stat_lse2;
   float *stat_dvec;
-  // when set, the MFMA kernel writes lse2 ([batch, heads, ns], rows n .. ns - 1
-  // hold 0) beside out: the statistic a later backward reads
+  // when set, the forward kernel writes lse2 ([batch, heads, ns], rows
+  // n .. ns - 1 hold 0) beside out: the statistic a later backward reads
   float *save_lse2;
-  // backward from a saved forward: the dQ kernel forms D = dO . O from this
-  // output ([batch, heads, n, d], bf16) itself and writes it to stat_dvec
-  // (rows n .. ns - 1: 0) for the dK/dV kernel, instead of reading dvec
+  // the dQ kernel forms D = dO . O from this forward output ([batch, heads,
+  // n, d], bf16) itself and writes it to stat_dvec (rows n .. ns - 1: 0) for
+  // the dK/dV kernel
   const void *saved_out;
   int32_t order[kMaxHeadsArg];  // head processed in slot i, heaviest sigma first
 };

@@ -1,6 +1,6 @@
 // plsh_mfma16.hip -- the kernels with 16-row waves (gfx950): the estimator
 // as the unfused form's fp32 partials and as the per-sample walk, the
-// backward's statistics pass, dQ and dK/dV, and the log-sum-exp combine.
+// backward's dQ and dK/dV, and the log-sum-exp combine.
 //
 // "Positional LSH: Binary Block Matrix Approximation for Attention with Linear
 // Biases", Methodology §3 (Theorem 2.2): the ratio-of-sums estimator
@@ -471,38 +471,10 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
   // The wave's 16 x D output block is staged in LDS (in the two ring slots
   // the last pair does not use: every wave is past them), then written whole
   // rows per instruction.
-  const int ns = (n + 31) & ~31;
-  const int64_t srow = ((int64_t)b * a.heads + h) * ns + r0 + qc;
-  if (!active) {
-    if (a.stat_lse2 && r0 < ns && gq == 0) a.stat_lse2[srow] = a.stat_dvec[srow] = 0.f;
-    if (a.save_lse2 && r0 < ns && gq == 0) a.save_lse2[srow] = 0.f;
-    return;
-  }
+  if (!active) return;
   float ltot = lsum + xor16_f(lsum);
   ltot += other_half_f(ltot, lane);
   const float inv = 1.0f / ltot;
-  if (a.stat_lse2) {
-    // backward statistics of the row: lse2 and D = dO . O (O in fp32, before
-    // its rounding); the lane holds dims 16 db + 4 gq .. + 3
-    const int io = r0 + qc;
-    const uint16_t *dOr = (const uint16_t *)a.dout + (((int64_t)b * a.heads + h) * n + min(io, n - 1)) * D + 4 * gq;
-    float acc = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const u32x2 raw = *(const u32x2 *)(dOr + 16 * db);
-      acc = fmaf(__uint_as_float(raw[0] << 16), oacc[db][0], acc);
-      acc = fmaf(__uint_as_float(raw[0] & 0xFFFF0000u), oacc[db][1], acc);
-      acc = fmaf(__uint_as_float(raw[1] << 16), oacc[db][2], acc);
-      acc = fmaf(__uint_as_float(raw[1] & 0xFFFF0000u), oacc[db][3], acc);
-    }
-    acc += xor16_f(acc);
-    acc += other_half_f(acc, lane);
-    if (gq == 0) {
-      a.stat_lse2[srow] = io < n ? m2 + __log2f(ltot) : 0.f;
-      a.stat_dvec[srow] = io < n ? acc * inv : 0.f;
-    }
-    return;
-  }
   if (a.o32) {
     // fp32 partials for a log-sum-exp combine: O (normalised) and lse, in
     // natural-log units (the running max m2 is in log2 units)
@@ -516,7 +488,6 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
     }
     return;
   }
-  if (a.save_lse2 && gq == 0) a.save_lse2[srow] = r0 + qc < n ? m2 + __log2f(ltot) : 0.f;
   const int free_slot = (((nst - 1) >> 1) & 1) ? 0 : 2;
   char *ob = (char *)lds.kv[free_slot][0] + wave * 32 * D;
 #pragma unroll
@@ -540,7 +511,7 @@ void attn_mfma_kernel(AttnArgs a, const uint8_t *ws) {
 // Backward, dQ (gradients of the estimate for fixed tables; the pages train
 // with the method, Experimental Validation).  The forward's structure -- the
 // same records, multiplicities, ring and Q staging -- with the normaliser
-// known (lse2 from a statistics pass) instead of an online softmax:
+// known (lse2 from the forward) instead of an online softmax:
 //   P_ij = c_ij 2^(q_i.k_j log2 e - lse2_i),  dP^T = V dO^T (MFMA),
 //   dS = P o (dP - D_i),  dQ_i = sum_j dS_ij k_j  (dQ^T += K^T dS^T, MFMA,
 //   the K tile read through the transposing LDS reads).
@@ -630,7 +601,7 @@ void attn_dq_kernel(AttnArgs a, const uint8_t *ws) {
   // stage st covers keys [U0 + 32 st, U0 + 32 st + 32)
   const int nst = (U1 > U0) ? (U1 - U0) / kTileKeys : 0;
   // the dO fragment (B operand of dP^T = V dO^T, laid out as the Q
-  // fragment), the row's normaliser and D = dO . O
+  // fragment), the row's normaliser and D = dO . O from the forward's output
   const uint16_t *dOp = (const uint16_t *)a.dout + ((int64_t)b * a.heads + h) * n * D;
   bf16x8 dof[NC];
   float lse2r = 0.f, dvr = 0.f;
@@ -644,32 +615,27 @@ void attn_dq_kernel(AttnArgs a, const uint8_t *ws) {
     }
     const int ns = (n + 31) & ~31;
     const int64_t row = ((int64_t)b * a.heads + h) * ns + i;  // rows padded to 32
+    if (active && i < n) lse2r = a.lse2[row];
+    // D_i = dO_i . O_i in the dO fragment's layout: the lane's 8 NC dims,
+    // then the sum over the row's four lanes; written for the dK/dV kernel
+    const uint16_t *Op = (const uint16_t *)a.saved_out + ((int64_t)b * a.heads + h) * n * D;
+    float acc = 0.f;
     if (active && i < n) {
-      lse2r = a.lse2[row];
-      if (!a.saved_out) dvr = a.dvec[row];
-    }
-    if (a.saved_out) {
-      // D_i = dO_i . O_i from the saved output, in the dO fragment's layout:
-      // the lane's 8 NC dims, then the sum over the row's four lanes
-      const uint16_t *Op = (const uint16_t *)a.saved_out + ((int64_t)b * a.heads + h) * n * D;
-      float acc = 0.f;
-      if (active && i < n) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const u32x4 o = *(const u32x4 *)(Op + (int64_t)i * D + 32 * c + 8 * gq);
-          const u32x4 g = __builtin_bit_cast(u32x4, dof[c]);
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 o = *(const u32x4 *)(Op + (int64_t)i * D + 32 * c + 8 * gq);
+        const u32x4 g = __builtin_bit_cast(u32x4, dof[c]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc = fmaf(__uint_as_float(o[e] << 16), __uint_as_float(g[e] << 16), acc);
-            acc = fmaf(__uint_as_float(o[e] & 0xFFFF0000u), __uint_as_float(g[e] & 0xFFFF0000u), acc);
-          }
+        for (int e = 0; e < 4; ++e) {
+          acc = fmaf(__uint_as_float(o[e] << 16), __uint_as_float(g[e] << 16), acc);
+          acc = fmaf(__uint_as_float(o[e] & 0xFFFF0000u), __uint_as_float(g[e] & 0xFFFF0000u), acc);
         }
       }
-      acc += xor16_f(acc);
-      acc += other_half_f(acc, lane);
-      dvr = acc;
-      if (gq == 0 && i < ns) a.stat_dvec[row] = i < n ? acc : 0.f;
     }
+    acc += xor16_f(acc);
+    acc += other_half_f(acc, lane);
+    dvr = acc;
+    if (gq == 0 && i < ns) a.stat_dvec[row] = i < n ? acc : 0.f;
   }
   // Everything loaded so far is needed before the first tile.  Waiting here,
   // before the first K/V copies are issued, measured faster than letting the

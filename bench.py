@@ -753,9 +753,10 @@ def main():
             f"{walk_rec['s_walk_tflops_in_kernel']:.0f} TFLOP/s of s-walk work), max |diff| from fused {wk_diff:.3e}")
         del wk_out
 
-    # the backward for fixed tables (a statistics pass of the estimator, the
-    # dQ kernel, the dK/dV kernel): its call time; and the backward from a
-    # saved forward, with the relative difference of the two gradients
+    # the backward for fixed tables (the estimator's forward with each row's
+    # normaliser, the dQ kernel, the dK/dV kernel): its call time; and the
+    # backward from a saved forward, with the relative difference of the two
+    # gradients (zero: the first runs the second after its own forward)
     bwd_rec = None
     if not args.no_comparators:
         g = torch.Generator().manual_seed(3)
@@ -774,8 +775,8 @@ def main():
                    "useful_pct_bf16_peak": 100.0 * bw_tflops / PEAK_BF16_TFLOPS}
         log(f"[bench] backward: {bw_ms:.3f} ms ({bw_ms / ms:.1f}x the forward call, {bw_tflops:.0f} useful "
             f"TFLOP/s)")
-        # the same backward from a saved forward (output and row statistics of
-        # plsh_alibi_attention_lse): D = dO.O replaces the statistics pass
+        # the same backward from a saved forward (output and row normalisers of
+        # plsh_alibi_attention_lse): no forward inside the call
         def bwd_saved():
             res["g"] = plsh.attention_backward(qd, kd, vd, dod, w.sigma, w.s, dt, causal=w.causal,
                                                out=o_s, lse2=l_s)

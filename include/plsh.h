@@ -31,13 +31,18 @@
  *     until then).
  *   - Device memory: plsh_alibi_attention on the bf16 path takes a workspace
  *     of heads * ceil(n/32) * (1040 + 16 * E) bytes, E = s + 16 rounded up to
- *     even, from the stream-ordered allocator (hipMallocAsync on `stream`) and
- *     releases it on the same stream (hipFreeAsync) within the call;
+ *     even, stream-ordered on `stream` (hipMallocFromPoolAsync) and releases
+ *     it on the same stream (hipFreeAsync) within the call;
  *     plsh_alibi_attention_ws takes the same workspace from the caller
  *     instead.  The ablation and backward entry points allocate their own
- *     workspaces the same way; the others allocate no device memory.
- *   - The library keeps no state besides a thread-local error string and the
- *     thread-local kernel timer below.
+ *     workspaces the same way; the others allocate no device memory.  These
+ *     workspaces come from a memory pool of the library's own on each device
+ *     (created on first use, kept until the process ends), which holds up to
+ *     1 GiB of released memory for later calls instead of returning it to
+ *     the driver at each synchronisation.
+ *   - The library keeps no state besides a thread-local error string, the
+ *     thread-local kernel timer below, those pools and the static scratch of
+ *     plsh_alibi_attention_noalloc.
  */
 #ifndef PLSH_H
 #define PLSH_H
@@ -369,7 +374,7 @@ PLSH_API plsh_status plsh_debug_attention_reference(const void *q, const void *k
  * Kernels: the block-edge pre-pass over heads*s single-sample record sets,
  * then the MFMA attention kernel looping over the samples.
  * Device memory: heads*s*ceil(n/32)*1328 bytes of records from the
- * stream-ordered allocator on `stream`, released within the call.
+ * library's pool (stream-ordered on `stream`), released within the call.
  * Errors: as plsh_alibi_attention, and PLSH_ERR_UNSUPPORTED for fp32 or when
  * heads*s*ceil(n/32) exceeds 2^31.
  */
@@ -392,17 +397,22 @@ PLSH_API plsh_status plsh_alibi_attention_walk(const void *q, const void *k, con
  *   dk, dv      DEVICE [batch, kv_heads, n, d] outputs
  *   the other arguments as for plsh_alibi_attention; bf16, s <= 124.
  * Launches: the block-edge pre-pass (for causal calls one pass that writes
- * both the causal records and the non-causal ones the dK/dV kernel takes); a
- * pass of the estimator that writes, in place of O, each row's normaliser
- * and D_i = dO_i.O_i (O in fp32); the dQ kernel (rows as in the estimator,
- * same records); the dK/dV kernel (key positions in place of rows, using
- * c_ij = c_ji; one workgroup per 128 key positions of a KV head, looping
- * over that head's query heads).  dq, dk, dv are written whole (no
+ * both the causal records and the non-causal ones the dK/dV kernel takes);
+ * the estimator's forward kernel over those records, writing O (bf16, into
+ * a buffer of the call's own) and each row's normaliser, as
+ * plsh_alibi_attention_lse does; then as plsh_alibi_attention_backward_saved
+ * from that output: the dQ kernel (rows as in the estimator, same records),
+ * which also forms D_i = dO_i.O_i, and the dK/dV kernel (key positions in
+ * place of rows, using c_ij = c_ji; one workgroup per 128 key positions of a
+ * KV head, looping over that head's query heads).  The gradients are
+ * therefore bitwise those of plsh_alibi_attention_lse followed by
+ * plsh_alibi_attention_backward_saved.  dq, dk, dv are written whole (no
  * accumulation into them).
- * Device memory: 8 * batch*heads*ceil32(n) bytes of statistics from the
- * stream-ordered allocator on `stream`, released within the call, plus the
- * pre-pass workspaces.  dout, dk, dv 16-byte
- * aligned; dq, dk, dv must not overlap q, k, v, dout or each other.
+ * Device memory: batch*heads*n*d*2 bytes (rounded up to 256) of forward
+ * output and 8 * batch*heads*ceil32(n) bytes of statistics from the
+ * library's pool (stream-ordered on `stream`), released within the call,
+ * plus the pre-pass workspaces.  dout, dk, dv 16-byte aligned; dq, dk, dv
+ * must not overlap q, k, v, dout or each other.
  * Errors: as plsh_alibi_attention (null dout, dq, dk or dv, misalignment and
  * aliasing: PLSH_ERR_ARG), and PLSH_ERR_UNSUPPORTED for fp32 or s > 124.
  */
@@ -440,18 +450,17 @@ PLSH_API plsh_status plsh_alibi_attention_lse(const void *q, const void *k, cons
  * plsh_alibi_attention_backward_saved -- plsh_alibi_attention_backward from a
  * saved forward: `out` and `lse2` as written by plsh_alibi_attention_lse for
  * the same q, k, v, tables and causal flag (Experimental Validation: training
- * with the method).  There is no statistics pass: the dQ kernel forms
- * D_i = dO_i . out_i (fp32 sums of the bf16 products) from the saved output
- * and writes it for the dK/dV kernel; the other launches are
- * plsh_alibi_attention_backward's.  Because D is taken from the bf16 output
- * rather than the fp32 estimate, the gradients differ from
- * plsh_alibi_attention_backward's by the output's rounding (relative 2^-8
- * per element at most).
+ * with the method).  No forward runs: the dQ kernel forms D_i = dO_i . out_i
+ * (fp32 sums of the bf16 products) from the saved output and writes it for
+ * the dK/dV kernel; the other launches are plsh_alibi_attention_backward's.
+ * D is taken from the bf16 output, not from the fp32 estimate: the
+ * gradients differ from those with the exact D by the output's rounding
+ * (relative 2^-8 per element at most).
  *   out    DEVICE [batch, heads, n, d] bf16, 16-byte aligned
  *   lse2   DEVICE float [batch][heads][ceil32(n)], 16-byte aligned
  *   the other arguments as for plsh_alibi_attention_backward.
- * Device memory: 4 * batch*heads*ceil32(n) bytes for D from the
- * stream-ordered allocator on `stream`, released within the call, plus the
+ * Device memory: 4 * batch*heads*ceil32(n) bytes for D from the library's
+ * pool (stream-ordered on `stream`), released within the call, plus the
  * pre-pass workspaces.  dq, dk, dv must not overlap any input (out and lse2
  * included).
  * Errors: as plsh_alibi_attention_backward, plus PLSH_ERR_ARG for a null or
@@ -475,8 +484,8 @@ PLSH_API plsh_status plsh_alibi_attention_backward_saved(const void *q, const vo
  * combine out_i = sum_k e^{lse_k} O_k / sum_k e^{lse_k}.  An ablation of the
  * sample fusion of plsh_alibi_attention (same arguments, same result up to
  * rounding); bf16 only.  Device memory: s * batch * heads * n * (d + 1) * 4
- * bytes of partials from the stream-ordered allocator on `stream`, released
- * within the call, plus each pass's pre-pass workspace.
+ * bytes of partials from the library's pool (stream-ordered on `stream`),
+ * released within the call, plus each pass's pre-pass workspace.
  * Errors: as plsh_alibi_attention, and PLSH_ERR_UNSUPPORTED for fp32.
  */
 PLSH_API plsh_status plsh_alibi_attention_unfused(const void *q, const void *k, const void *v, void *out,
