@@ -163,36 +163,39 @@ plsh_status scratch_ptr(const char *who, void **out) {
 // mapped its workspace afresh (the backward from a saved forward, 16k
 // Mistral-shaped layer, synchronised per call: 0.74 ms, 0.56 ms from a pool
 // that keeps its memory).
+// (a device whose pool cannot be made keeps the default pool)
 constexpr uint64_t kPoolKeepBytes = (uint64_t)1 << 30;
 std::mutex g_pool_mu;
 hipMemPool_t g_pool[kMaxScratchDevices] = {};
+bool g_pool_tried[kMaxScratchDevices] = {};
 
 hipError_t pool_alloc(void **p, size_t bytes, hipStream_t st) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxScratchDevices) return hipMallocAsync(p, bytes, st);
   hipMemPool_t pool = nullptr;
-  {
+  if (dev >= 0 && dev < kMaxScratchDevices) {
     std::lock_guard<std::mutex> lock(g_pool_mu);
-    if (!g_pool[dev]) {
+    if (!g_pool_tried[dev]) {
+      g_pool_tried[dev] = true;
       hipMemPoolProps props = {};
       props.allocType = hipMemAllocationTypePinned;
       props.handleTypes = hipMemHandleTypeNone;
       props.location.type = hipMemLocationTypeDevice;
       props.location.id = dev;
       hipMemPool_t created = nullptr;
-      if ((e = hipMemPoolCreate(&created, &props)) != hipSuccess) return e;
-      uint64_t keep = kPoolKeepBytes;
-      if ((e = hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
-        (void)hipMemPoolDestroy(created);
-        return e;
+      if (hipMemPoolCreate(&created, &props) == hipSuccess) {
+        uint64_t keep = kPoolKeepBytes;
+        if (hipMemPoolSetAttribute(created, hipMemPoolAttrReleaseThreshold, &keep) == hipSuccess)
+          g_pool[dev] = created;
+        else
+          (void)hipMemPoolDestroy(created);
       }
-      g_pool[dev] = created;
+      (void)hipGetLastError();
     }
     pool = g_pool[dev];
   }
-  return hipMallocFromPoolAsync(p, bytes, pool, st);
+  return pool ? hipMallocFromPoolAsync(p, bytes, pool, st) : hipMallocAsync(p, bytes, st);
 }
 
 // the event pair for the next timed launch, or nullptr when timing is off
